@@ -1,0 +1,311 @@
+"""Benchmark of the FP8 W8A8 linear hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|mlp_down|mlp_down_tensor|large|tiny]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+dynamic activation quantization followed by the block-scaled GEMM (weights
+are quantized once, offline, before timing).  The default workload is the
+decode shape: N = 11008, K = 4096, and one step runs the three decode batch
+sizes M = 1, 4 and 16 back to back.  Each GEMM of a decode step reads a
+different copy of the weight codes (8 copies, 360 MB, more than the 256 MB
+Infinity Cache) so the weight really comes from HBM.
+
+Timing: W warm-up steps, then exactly K steps replayed from HIP graphs (one
+graph per step pattern), bracketed by torch.cuda.synchronize() on both sides
+(one process, one GPU: no barrier needed).  The dominant kernel's average
+launch duration is measured with HIP events around each launch on the
+launch stream, in a pass whose launches are queued behind a GPU-side delay
+so no host gap falls between an event and its kernel.
+
+Prints ONE JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+N_WCOPIES = 8
+
+
+def quant_bytes(M, K):
+    """Algorithmic bytes of the activation quantizer: bf16 in, codes + scales out."""
+    return 2 * M * K + M * K + 4 * M * (K // 128)
+
+
+def gemm_bytes(M, N, K, per_tensor=False):
+    """Each operand once: A codes + scales, W codes + scales, bf16 out."""
+    sa = 4 if per_tensor else 4 * M * (K // 128)
+    sw = 4 if per_tensor else 4 * (N // 128) * (K // 128)
+    return M * K + sa + N * K + sw + 2 * M * N
+
+
+def gemm_flops(M, N, K):
+    return 2 * M * N * K
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "prefill", "mlp_down", "mlp_down_tensor", "large", "tiny"])
+    p.add_argument("--cpu-baseline-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle baseline sample (0 disables it)")
+    return p.parse_args()
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+class Workload:
+    """Device buffers and the launch list of one step."""
+
+    def __init__(self, name):
+        import torch
+        import fp8_w8a8_block_amd as fp8
+        from workloads import synth
+        self.fp8 = fp8
+        self.name = name
+        base = "mlp_down" if name == "mlp_down_tensor" else name
+        self.mode = "tensor" if name == "mlp_down_tensor" else "block"
+        c = synth.CONFIGS[base]
+        self.cfg = c
+        self.N, self.K = c["N"], c["K"]
+        self.Ms = list(c["decode_m"]) if base == "decode" else [c["M"]]
+        ch = synth.outlier_channels(c["cfg"], self.K, c["n_outliers"])
+        self.A_bits = [synth.make_activation(c["cfg"], M, self.K, c["a_kind"], c["a_std"], ch,
+                                             c["outlier_mult"]) for M in self.Ms]
+        W_bits = synth.make_weight(c["cfg"], self.N, self.K, c["w_std"])
+        self.W_bits = W_bits
+        wd = dev_bf16(W_bits)
+        wq, ws = fp8.quant_weight_block(wd, self.mode)
+        torch.cuda.synchronize()
+        del wd
+        ncopy = N_WCOPIES if base == "decode" else 1
+        self.wq = [wq] + [wq.clone() for _ in range(ncopy - 1)]
+        self.ws = ws
+        self.x = [dev_bf16(b) for b in self.A_bits]
+        self.aq = [torch.empty((M, self.K), dtype=torch.uint8, device="cuda") for M in self.Ms]
+        if self.mode == "block":
+            self.as_ = [torch.empty((M, self.K // 128), dtype=torch.float32, device="cuda")
+                        for M in self.Ms]
+        else:
+            self.as_ = [torch.empty((1,), dtype=torch.float32, device="cuda") for _ in self.Ms]
+        nws = fp8.workspace_bytes(0, max(self.Ms), 0, self.K, self.mode)
+        self.ws_buf = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda") if nws else None
+        self.out = [torch.empty((M, self.N), dtype=torch.bfloat16, device="cuda") for M in self.Ms]
+        self.ncopy = ncopy
+        self.launches_per_step = len(self.Ms)
+
+    def copy_index(self, step, j):
+        return (step * self.launches_per_step + j) % self.ncopy
+
+    def n_patterns(self):
+        # step patterns repeat when the weight-copy rotation does
+        from math import gcd
+        return self.ncopy // gcd(self.ncopy, self.launches_per_step)
+
+    def step(self, s, on_gemm=None):
+        fp8 = self.fp8
+        for j, M in enumerate(self.Ms):
+            fp8.quant_act(self.x[j], self.mode, workspace=self.ws_buf, q=self.aq[j],
+                          scales=self.as_[j])
+            ev = on_gemm() if on_gemm else None
+            if ev:
+                ev[0].record()
+            fp8.block_gemm(self.aq[j], self.as_[j], self.wq[self.copy_index(s, j)], self.ws,
+                           self.mode, out=self.out[j])
+            if ev:
+                ev[1].record()
+
+    def bytes_per_step(self):
+        pt = self.mode == "tensor"
+        q = sum(quant_bytes(M, self.K) + (2 * M * self.K if pt else 0) for M in self.Ms)
+        g = sum(gemm_bytes(M, self.N, self.K, pt) for M in self.Ms)
+        return q + g, q, g
+
+    def flops_per_step(self):
+        return sum(gemm_flops(M, self.N, self.K) for M in self.Ms)
+
+
+def time_gemm_launches(wl, n_steps):
+    """Average duration of the GEMM launches, from HIP event pairs on the launch
+    stream; the launches are queued behind a GPU-side delay first."""
+    import torch
+    pairs = []
+
+    def mk():
+        p = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        pairs.append(p)
+        return p
+
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(5e7))          # a bounded GPU-side delay while the host queues work
+    for s in range(n_steps):
+        wl.step(s, on_gemm=mk)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in pairs])
+    return float(ms.mean()), float(np.median(ms)), len(ms)
+
+
+def cpu_baseline(wl, target_s):
+    """Oracle timed on the host on a bounded sample of the same step."""
+    from oracle import gemm, quant
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = os.cpu_count() or 1
+    if wl.mode == "block":
+        # weight quantization is offline: done once, outside the timed sample
+        if len(wl.Ms) > 1:
+            rows = wl.N
+        else:
+            rows = 128 * max(1, min(wl.N // 128, 4))
+        rwq, rws = quant.quant_weight_block_ref(wl.W_bits[:rows])
+    else:
+        rows = 128 * max(1, min(wl.N // 128, 4))
+        amax_w = quant.tensor_amax_ref(wl.W_bits)
+        rwq, rws = quant.quant_tensor_with_amax_ref(wl.W_bits[:rows], amax_w)
+    a_rows = [min(M, 256) for M in wl.Ms]
+    nbytes = 0
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for j, M in enumerate(wl.Ms):
+            ab = wl.A_bits[j][:a_rows[j]]
+            if wl.mode == "block":
+                aq, as_ = quant.quant_act_ref(ab)
+                gemm.gemm_block_ref(aq, as_, rwq, rws)
+                nbytes += quant_bytes(a_rows[j], wl.K) + gemm_bytes(a_rows[j], rows, wl.K)
+            else:
+                aq, as_ = quant.quant_tensor_ref(ab)
+                gemm.gemm_tensor_ref(aq, as_, rwq, rws)
+                nbytes += quant_bytes(a_rows[j], wl.K) + gemm_bytes(a_rows[j], rows, wl.K, True)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    flops = sum(gemm_flops(r, rows, wl.K) for r in a_rows) * reps
+    sample = (f"oracle quant_act + fp64 GEMM, rows M={a_rows} of A against {rows} of {wl.N} "
+              f"weight rows, K={wl.K}, repeated {reps}x; weight quantized beforehand")
+    if len(wl.Ms) > 1:
+        return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": sample, "seconds": round(el, 2)}
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(el, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels are "
+              "single-GPU and no multi-GPU path is built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = Workload(args.workload)
+    decode = len(wl.Ms) > 1
+
+    # warm-up (eager), then capture one HIP graph per step pattern
+    for s in range(args.warmup):
+        wl.step(s)
+    torch.cuda.synchronize()
+    graphs = []
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for p in range(wl.n_patterns()):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                wl.step(p)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(stream)
+    for p in range(len(graphs)):       # graph warm-up replays
+        graphs[p].replay()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        graphs[s % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec = t1 - t0
+    ms_per_step = sec / K * 1e3
+
+    total_b, q_b, g_b = wl.bytes_per_step()
+    flops = wl.flops_per_step()
+
+    g_ms_mean, g_ms_med, n_l = time_gemm_launches(wl, min(K, 64))
+    gemm_bytes_per_launch = g_b / wl.launches_per_step
+    flops_per_launch = flops / wl.launches_per_step
+
+    if decode:
+        metric_value = total_b / (sec / K) / 1e9
+        unit = "GB/s"
+        roof = {"bound": "hbm", "achieved": gemm_bytes_per_launch / (g_ms_mean * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        metric_value = flops / (sec / K) / 1e12
+        unit = "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": flops_per_launch / (g_ms_mean * 1e-3) / 1e12,
+                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "gemm_decode_kernel" if decode else "gemm_tile_kernel"
+    roof["avg_launch_us"] = g_ms_mean * 1e3
+    roof["median_launch_us"] = g_ms_med * 1e3
+    roof["launches_timed"] = n_l
+    roof["algorithmic_bytes_per_launch" if decode else "flop_per_launch"] = (
+        gemm_bytes_per_launch if decode else flops_per_launch)
+
+    cpu = None
+    if args.cpu_baseline_seconds > 0:
+        cpu = cpu_baseline(wl, args.cpu_baseline_seconds)
+
+    c = wl.cfg
+    config = {"workload": args.workload, "M": wl.Ms if decode else wl.Ms[0], "N": wl.N, "K": wl.K,
+              "scales": "per-tensor" if wl.mode == "tensor" else "A 1x128, W 128x128",
+              "step": "quant_act + block_gemm" + (" for each M" if decode else ""),
+              "weight_copies": wl.ncopy}
+    line = {
+        "metric": ("FP8 block-scaled GEMM TFLOPS (prefill) & GB/s (decode) as % of MI355X "
+                   "roofline"),
+        "value": metric_value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp8e4m3 -> fp32 accumulate -> bf16",
+        "data": "synthetic (seeded numpy, shapes and distributions of the workload)",
+        "config": config,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "step_bytes": {"total": total_b, "quant_act": q_b, "gemm": g_b},
+        "step_flop": flops,
+        "tflops_per_step": flops / (sec / K) / 1e12,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

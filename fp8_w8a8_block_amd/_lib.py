@@ -1,0 +1,185 @@
+"""ctypes binding of libfp8w8a8.so: argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; this module
+turns torch tensors into device pointers, leading dimensions and the current
+HIP stream, and turns nonzero status codes into ValueError (the same
+convention as the eager configuration errors of "[vLLM] FP8", block
+quantization).  There is no fallback: if the library is missing, importing
+the binding raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8w8a8.so")
+
+FP8_OK = 0
+SCALE_BLOCK = 0
+SCALE_TENSOR = 1
+OP_QUANT_ACT = 0
+OP_QUANT_WEIGHT = 1
+OP_GEMM = 2
+
+_MODES = {"block": SCALE_BLOCK, "tensor": SCALE_TENSOR}
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "fp8_status_str": (ctypes.c_char_p, [_int]),
+    "fp8_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _int]),
+    "fp8_quant_act": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _vp, _sz, _vp]),
+    "fp8_quant_weight_block": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _int,
+                                      _int, _vp, _sz, _vp]),
+    "fp8_block_gemm": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
+                              _i64, _int, _vp, _sz, _vp]),
+    "fp8_validate_quant_act": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _vp,
+                                      _sz]),
+    "fp8_validate_quant_weight_block": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _int,
+                                               _int, _int, _vp, _sz]),
+    "fp8_validate_block_gemm": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                       _i64, _i64, _i64, _int]),
+    "fp8_e4m3_encode_f32": (_int, [_vp, _i64, _vp, _vp]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded shared library (ctypes.CDLL) with argument types set."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m fp8_w8a8_block_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_str(code):
+    return lib().fp8_status_str(int(code)).decode()
+
+
+def _check(code):
+    if code != FP8_OK:
+        raise ValueError(f"fp8w8a8 status {code}: {status_str(code)}")
+
+
+def _mode(scale_mode):
+    if isinstance(scale_mode, str):
+        if scale_mode not in _MODES:
+            raise ValueError(f"unknown scale mode {scale_mode!r}")
+        return _MODES[scale_mode]
+    return int(scale_mode)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _rows(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D row-major tensor with unit column stride")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def workspace_bytes(op, M, N, K, scale_mode):
+    return int(lib().fp8_workspace_bytes(int(op), int(M), int(N), int(K), _mode(scale_mode)))
+
+
+def quant_act(x, scale_mode="block", workspace=None, q=None, scales=None):
+    """Dynamic activation quantization of bf16 x [M, K] -> (codes uint8 [M, K], scales fp32).
+
+    Block mode gives scales [M, K/128]; tensor mode a 1-element tensor.
+    """
+    mode = _mode(scale_mode)
+    M, K, ld_x = _rows(x, torch.bfloat16, "x")
+    with torch.cuda.device(x.device):
+        if q is None:
+            q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        if scales is None:
+            shape = (M, K // 128) if mode == SCALE_BLOCK else (1,)
+            scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+        ld_s = scales.stride(0) if scales.dim() == 2 else 1
+        nws = workspace_bytes(OP_QUANT_ACT, M, 0, K, mode)
+        if nws and workspace is None:
+            workspace = torch.empty(nws, dtype=torch.uint8, device=x.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        _check(lib().fp8_quant_act(x.data_ptr(), M, K, ld_x, q.data_ptr(), q.stride(0),
+                                   scales.data_ptr(), ld_s, mode, ws_ptr, ws_len, _stream(x)))
+    return q, scales
+
+
+def quant_weight_block(w, scale_mode="block", block_n=128, block_k=128, workspace=None):
+    """Weight quantization of bf16 w [N, K] -> (codes uint8 [N, K], scales fp32 [N/128, K/128])."""
+    mode = _mode(scale_mode)
+    N, K, ld_w = _rows(w, torch.bfloat16, "w")
+    with torch.cuda.device(w.device):
+        q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+        if mode == SCALE_BLOCK:
+            scales = torch.empty((max(N // 128, 0), K // 128), dtype=torch.float32, device=w.device)
+            ld_s = scales.stride(0)
+        else:
+            scales = torch.empty((1,), dtype=torch.float32, device=w.device)
+            ld_s = 1
+        nws = workspace_bytes(OP_QUANT_WEIGHT, N, 0, K, mode)
+        if nws and workspace is None:
+            workspace = torch.empty(nws, dtype=torch.uint8, device=w.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_len = workspace.numel() if workspace is not None else 0
+        _check(lib().fp8_quant_weight_block(w.data_ptr(), N, K, ld_w, q.data_ptr(), q.stride(0),
+                                            scales.data_ptr(), ld_s, int(block_n), int(block_k),
+                                            mode, ws_ptr, ws_len, _stream(w)))
+    return q, scales
+
+
+def block_gemm(a_q, a_s, w_q, w_s, scale_mode="block", out=None):
+    """out[M, N] bf16 = A . W^T from FP8 codes and their scales."""
+    mode = _mode(scale_mode)
+    M, K, ld_a = _rows(a_q, torch.uint8, "a_q")
+    N, K2, ld_w = _rows(w_q, torch.uint8, "w_q")
+    if K2 != K:
+        raise ValueError(f"K mismatch: a_q has {K}, w_q has {K2}")
+    for t, nm in ((a_s, "a_s"), (w_s, "w_s")):
+        if t.dtype != torch.float32 or not t.is_cuda:
+            raise TypeError(f"{nm} must be a float32 device tensor")
+    ld_as = a_s.stride(0) if a_s.dim() == 2 else 1
+    ld_ws = w_s.stride(0) if w_s.dim() == 2 else 1
+    with torch.cuda.device(a_q.device):
+        if out is None:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+        _check(lib().fp8_block_gemm(a_q.data_ptr(), ld_a, a_s.data_ptr(), ld_as, w_q.data_ptr(),
+                                    ld_w, w_s.data_ptr(), ld_ws, out.data_ptr(), out.stride(0),
+                                    M, N, K, mode, None, 0, _stream(a_q)))
+    return out
+
+
+def linear(x, w_q, w_s, scale_mode="block"):
+    """One W8A8 linear call: dynamic activation quantization, then the GEMM."""
+    a_q, a_s = quant_act(x, scale_mode)
+    return block_gemm(a_q, a_s, w_q, w_s, scale_mode)
+
+
+def encode_f32(x):
+    """E4M3 codes of fp32 values with the device encoder (saturating, RNE)."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 device tensor")
+    with torch.cuda.device(x.device):
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        _check(lib().fp8_e4m3_encode_f32(x.data_ptr(), x.numel(), codes.data_ptr(), _stream(x)))
+    return codes

@@ -1,0 +1,213 @@
+// C ABI of the FP8 W8A8 library: argument validation, device check, and
+// dispatch to the launchers.  Validation mirrors the eager configuration
+// checks of "[vLLM] FP8", block quantization (block mode needs pre-quantized
+// weights, a two-dimensional block size, and a dynamic activation scheme),
+// turned into status codes returned before anything is enqueued.
+#include <atomic>
+#include <cstring>
+
+#include "fp8w8a8.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;        // any single extent
+constexpr int64_t kMaxElems = (int64_t)1 << 40;      // rows * cols of one tensor
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Byte range [lo, hi) of a row-major matrix.
+struct Range {
+  uintptr_t lo, hi;
+};
+Range range_of(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+  uintptr_t lo = (uintptr_t)p;
+  if (rows <= 0 || cols <= 0) return {lo, lo};
+  uintptr_t hi = lo + (uintptr_t)(((rows - 1) * ld + cols) * elem);
+  return {lo, hi};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool shape_ok_kn(int64_t K) { return K > 0 && K % 128 == 0 && K < kMaxDim; }
+
+fp8_status validate_quant(const uint16_t* x, int64_t R, int64_t K, int64_t ld_x,
+                          const uint8_t* q, int64_t ld_q, const float* scales, int64_t ld_s,
+                          int scale_mode, const void* ws, size_t ws_bytes, bool rows_blocked) {
+  if (scale_mode != FP8_SCALE_BLOCK && scale_mode != FP8_SCALE_TENSOR) return FP8_ERR_SCHEME;
+  if (R < 0 || R >= kMaxDim || !shape_ok_kn(K)) return FP8_ERR_SHAPE;
+  if (rows_blocked && scale_mode == FP8_SCALE_BLOCK && R % 128 != 0) return FP8_ERR_SHAPE;
+  if (R > 0 && R * K > kMaxElems) return FP8_ERR_SHAPE;
+  if (R == 0) return FP8_OK;
+  if (!x || !q || !scales) return FP8_ERR_NULL;
+  const int64_t groups = K / 128;
+  if (ld_x < K || ld_q < K) return FP8_ERR_STRIDE;
+  if (scale_mode == FP8_SCALE_BLOCK && ld_s < groups) return FP8_ERR_STRIDE;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4)) return FP8_ERR_ALIGN;
+  if (ld_x % 8 != 0 || ld_q % 16 != 0) return FP8_ERR_ALIGN;
+  const int64_t srows = scale_mode == FP8_SCALE_BLOCK ? (rows_blocked ? R / 128 : R) : 1;
+  const int64_t scols = scale_mode == FP8_SCALE_BLOCK ? groups : 1;
+  const int64_t sld = scale_mode == FP8_SCALE_BLOCK ? ld_s : 1;
+  Range rx = range_of(x, R, K, ld_x, 2), rq = range_of(q, R, K, ld_q, 1);
+  Range rs = range_of(scales, srows, scols, sld, 4);
+  if (overlap(rx, rq) || overlap(rx, rs) || overlap(rq, rs)) return FP8_ERR_ALIAS;
+  if (scale_mode == FP8_SCALE_TENSOR) {
+    const size_t need = (size_t)fp8k::kTensorPartials * sizeof(uint32_t);
+    if (!ws || ws_bytes < need || !aligned(ws, 4)) return FP8_ERR_WORKSPACE;
+    Range rw = {(uintptr_t)ws, (uintptr_t)ws + need};
+    if (overlap(rw, rx) || overlap(rw, rq) || overlap(rw, rs)) return FP8_ERR_ALIAS;
+  }
+  return FP8_OK;
+}
+
+fp8_status validate_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, int64_t ld_as,
+                         const uint8_t* w_q, int64_t ld_w, const float* w_s, int64_t ld_ws,
+                         const uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
+                         int scale_mode) {
+  if (scale_mode != FP8_SCALE_BLOCK && scale_mode != FP8_SCALE_TENSOR) return FP8_ERR_SCHEME;
+  if (M < 0 || M >= kMaxDim || !shape_ok_kn(K) || !shape_ok_kn(N)) return FP8_ERR_SHAPE;
+  if (M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems) return FP8_ERR_SHAPE;
+  if (M == 0) return FP8_OK;
+  if (!a_q || !a_s || !w_q || !w_s || !out) return FP8_ERR_NULL;
+  const int64_t KB = K / 128;
+  if (ld_a < K || ld_w < K || ld_out < N) return FP8_ERR_STRIDE;
+  if (scale_mode == FP8_SCALE_BLOCK && (ld_as < KB || ld_ws < KB)) return FP8_ERR_STRIDE;
+  if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(out, 16)) return FP8_ERR_ALIGN;
+  if (!aligned(a_s, 4) || !aligned(w_s, 4)) return FP8_ERR_ALIGN;
+  if (ld_a % 16 != 0 || ld_w % 16 != 0 || ld_out % 8 != 0) return FP8_ERR_ALIGN;
+  Range ro = range_of(out, M, N, ld_out, 2);
+  Range ra = range_of(a_q, M, K, ld_a, 1), rw = range_of(w_q, N, K, ld_w, 1);
+  Range ras = scale_mode == FP8_SCALE_BLOCK ? range_of(a_s, M, KB, ld_as, 4) : range_of(a_s, 1, 1, 1, 4);
+  Range rws = scale_mode == FP8_SCALE_BLOCK ? range_of(w_s, N / 128, KB, ld_ws, 4)
+                                            : range_of(w_s, 1, 1, 1, 4);
+  if (overlap(ro, ra) || overlap(ro, rw) || overlap(ro, ras) || overlap(ro, rws)) return FP8_ERR_ALIAS;
+  return FP8_OK;
+}
+
+// Per-device cache of "is this a gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+fp8_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8_ERR_DEVICE;
+  int state = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8_ERR_DEVICE;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? FP8_OK : FP8_ERR_DEVICE;
+}
+
+fp8_status launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_status_str(fp8_status s) {
+  switch (s) {
+    case FP8_OK: return "ok";
+    case FP8_ERR_NULL: return "a required pointer is NULL";
+    case FP8_ERR_SHAPE: return "bad shape: K and N must be positive multiples of 128, M >= 0";
+    case FP8_ERR_STRIDE: return "leading dimension smaller than the row length";
+    case FP8_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case FP8_ERR_BLOCK: return "the weight block size must have two dimensions, 128 x 128";
+    case FP8_ERR_SCHEME: return "unsupported scale mode: block mode supports only dynamic activation scales";
+    case FP8_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP8_ERR_DEVICE: return "no gfx950 device is current";
+    case FP8_ERR_LAUNCH: return "kernel launch failed";
+    case FP8_ERR_ALIAS: return "an output overlaps another tensor";
+  }
+  return "unknown status";
+}
+
+size_t fp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int scale_mode) {
+  (void)M; (void)N; (void)K;
+  if ((op == FP8_OP_QUANT_ACT || op == FP8_OP_QUANT_WEIGHT) && scale_mode == FP8_SCALE_TENSOR)
+    return (size_t)fp8k::kTensorPartials * sizeof(uint32_t);
+  return 0;
+}
+
+fp8_status fp8_validate_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                  const uint8_t* q, int64_t ld_q, const float* scales,
+                                  int64_t ld_s, int scale_mode, const void* workspace,
+                                  size_t ws_bytes) {
+  return validate_quant(x, M, K, ld_x, q, ld_q, scales, ld_s, scale_mode, workspace, ws_bytes,
+                        false);
+}
+
+fp8_status fp8_validate_quant_weight_block(const uint16_t* w, int64_t N, int64_t K,
+                                           int64_t ld_w, const uint8_t* q, int64_t ld_q,
+                                           const float* scales, int64_t ld_s, int block_n,
+                                           int block_k, int scale_mode,
+                                           const void* workspace, size_t ws_bytes) {
+  if (scale_mode == FP8_SCALE_BLOCK && (block_n != 128 || block_k != 128)) return FP8_ERR_BLOCK;
+  return validate_quant(w, N, K, ld_w, q, ld_q, scales, ld_s, scale_mode, workspace, ws_bytes,
+                        true);
+}
+
+fp8_status fp8_validate_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s,
+                                   int64_t ld_as, const uint8_t* w_q, int64_t ld_w,
+                                   const float* w_s, int64_t ld_ws, const uint16_t* out,
+                                   int64_t ld_out, int64_t M, int64_t N, int64_t K,
+                                   int scale_mode) {
+  return validate_gemm(a_q, ld_a, a_s, ld_as, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N, K,
+                       scale_mode);
+}
+
+fp8_status fp8_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* q,
+                         int64_t ld_q, float* scales, int64_t ld_s, int scale_mode,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  fp8_status st = validate_quant(x, M, K, ld_x, q, ld_q, scales, ld_s, scale_mode, workspace,
+                                 ws_bytes, false);
+  if (st != FP8_OK || M == 0) return st;
+  if ((st = check_device()) != FP8_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (scale_mode == FP8_SCALE_BLOCK)
+    return launched(fp8k::launch_quant_act_block(x, M, K, ld_x, q, ld_q, scales, ld_s, s));
+  return launched(fp8k::launch_quant_tensor(x, M, K, ld_x, q, ld_q, scales,
+                                            (uint32_t*)workspace, s));
+}
+
+fp8_status fp8_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
+                                  uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s,
+                                  int block_n, int block_k, int scale_mode, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  fp8_status st = fp8_validate_quant_weight_block(w, N, K, ld_w, q, ld_q, scales, ld_s, block_n,
+                                                  block_k, scale_mode, workspace, ws_bytes);
+  if (st != FP8_OK || N == 0) return st;
+  if ((st = check_device()) != FP8_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (scale_mode == FP8_SCALE_BLOCK)
+    return launched(fp8k::launch_quant_weight_block(w, N, K, ld_w, q, ld_q, scales, ld_s, s));
+  return launched(fp8k::launch_quant_tensor(w, N, K, ld_w, q, ld_q, scales,
+                                            (uint32_t*)workspace, s));
+}
+
+fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, int64_t ld_as,
+                          const uint8_t* w_q, int64_t ld_w, const float* w_s, int64_t ld_ws,
+                          uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
+                          int scale_mode, void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace; (void)ws_bytes;
+  fp8_status st = validate_gemm(a_q, ld_a, a_s, ld_as, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N,
+                                K, scale_mode);
+  if (st != FP8_OK || M == 0) return st;
+  if ((st = check_device()) != FP8_OK) return st;
+  return launched(fp8k::launch_gemm(a_q, ld_a, a_s, ld_as, w_q, ld_w, w_s, ld_ws, out, ld_out, M,
+                                    N, K, scale_mode == FP8_SCALE_TENSOR, (hipStream_t)stream));
+}
+
+fp8_status fp8_e4m3_encode_f32(const float* x, int64_t n, uint8_t* codes, void* stream) {
+  if (n < 0 || n > kMaxElems) return FP8_ERR_SHAPE;
+  if (n == 0) return FP8_OK;
+  if (!x || !codes) return FP8_ERR_NULL;
+  if (!aligned(x, 4)) return FP8_ERR_ALIGN;
+  if (overlap(range_of(x, 1, n, n, 4), range_of(codes, 1, n, n, 1))) return FP8_ERR_ALIAS;
+  fp8_status st = check_device();
+  if (st != FP8_OK) return st;
+  return launched(fp8k::launch_encode_f32(x, n, codes, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// Internal launchers behind the C ABI.  Arguments are already validated by
+// the ABI layer (abi.hip); each launcher only enqueues kernels on `st` and
+// returns hipGetLastError() of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8k {
+
+// workspace of the per-tensor quantizer: one partial amax per workgroup of
+// the first pass
+constexpr int kTensorPartials = 1024;
+
+hipError_t launch_quant_act_block(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                  uint8_t* q, int64_t ld_q, float* s, int64_t ld_s,
+                                  hipStream_t st);
+hipError_t launch_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
+                                     uint8_t* q, int64_t ld_q, float* s, int64_t ld_s,
+                                     hipStream_t st);
+hipError_t launch_quant_tensor(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
+                               uint8_t* q, int64_t ld_q, float* s, uint32_t* partials,
+                               hipStream_t st);
+hipError_t launch_encode_f32(const float* x, int64_t n, uint8_t* codes, hipStream_t st);
+
+// out = A . W^T, block scales (per_tensor = false) or one scale each.
+hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
+                       const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
+                       uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
+                       bool per_tensor, hipStream_t st);
+
+}  // namespace fp8k

@@ -1,0 +1,231 @@
+// Dynamic FP8 quantizers for gfx950: 1x128 activation groups, 128x128
+// weight blocks, whole-tensor scales, and the bare element encoder.
+//
+// Rule per group G ("[vLLM] FP8", block quantization and scaling strategies;
+// "FP8 Quantization", D.2 for run-time activation scales):
+//   amax = max |x| over G,  s = fp32(amax) / 448,  code = E4M3(x / s)
+// with the quotient correctly rounded in fp32 and the encoding rounded to
+// nearest even, saturating (format: "[vLLM] FP8" format table).
+//
+// The path is HBM-bound: 2 bytes read and 1 + 4/128 bytes written per
+// element.  Loads are 16 bytes per lane, 16 lanes per 128-group, so a wave
+// reads four consecutive 256-byte groups; the group max is a 16-lane DPP
+// reduction with no LDS traffic.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8k {
+
+namespace {
+
+// Quantize the 8 bf16 values a lane holds (uint4) with the group divisor;
+// returns the 8 codes as a uint2.
+__device__ __forceinline__ uint2 quant8(const uint4 v, const GroupDivisor& d) {
+  uint32_t c0 = e4m3_pack4_mag(quotient_abs(bf16_lo(v.x), d), quotient_abs(bf16_hi(v.x), d),
+                               quotient_abs(bf16_lo(v.y), d), quotient_abs(bf16_hi(v.y), d));
+  uint32_t c1 = e4m3_pack4_mag(quotient_abs(bf16_lo(v.z), d), quotient_abs(bf16_hi(v.z), d),
+                               quotient_abs(bf16_lo(v.w), d), quotient_abs(bf16_hi(v.w), d));
+  c0 |= bf16x4_signs(v.x, v.y);
+  c1 |= bf16x4_signs(v.z, v.w);
+  return make_uint2(c0, c1);
+}
+
+__device__ __forceinline__ uint32_t absmax8_bits(const uint4 v) {
+  uint32_t a = bf16x2_absmax_bits(v.x);
+  uint32_t b = bf16x2_absmax_bits(v.y);
+  uint32_t c = bf16x2_absmax_bits(v.z);
+  uint32_t e = bf16x2_absmax_bits(v.w);
+  a = a > b ? a : b;
+  c = c > e ? c : e;
+  return a > c ? a : c;
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 activation groups.  Block = 256 threads = 16 groups per slot; each
+// thread handles GPT groups (GPT loads in flight).  The grid is one run of
+// blocks per row: blockIdx.x = row * blocks_per_row + block_in_row.
+template <int GPT>
+__global__ __launch_bounds__(256) void quant_act_block_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
+    float* __restrict__ s, int64_t ld_s, uint32_t groups_per_row, uint32_t blocks_per_row) {
+  const uint32_t row = blockIdx.x / blocks_per_row;
+  const uint32_t blk = blockIdx.x - row * blocks_per_row;
+  const uint32_t lane16 = threadIdx.x & 15u;
+  const uint32_t slot = threadIdx.x >> 4;
+  const uint16_t* xrow = x + (int64_t)row * ld_x;
+  uint8_t* qrow = q + (int64_t)row * ld_q;
+
+  uint4 v[GPT];
+  bool ok[GPT];
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    uint32_t g = (blk * GPT + j) * 16u + slot;
+    ok[j] = g < groups_per_row;
+    v[j] = ok[j] ? *reinterpret_cast<const uint4*>(xrow + (int64_t)g * kGroup + lane16 * 8u)
+                 : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    uint32_t g = (blk * GPT + j) * 16u + slot;
+    uint32_t amax = row16_max(absmax8_bits(v[j]));
+    GroupDivisor d = make_divisor(__uint_as_float(amax));
+    uint2 c = quant8(v[j], d);
+    if (ok[j]) {
+      *reinterpret_cast<uint2*>(qrow + (int64_t)g * kGroup + lane16 * 8u) = c;
+      if (lane16 == 0) s[(int64_t)row * ld_s + g] = d.s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 weight blocks: one 256-thread workgroup per block.  Thread t owns
+// the 16-byte column chunk t % 16 of rows t/16 + 16 i, i = 0..7 (64 values
+// held in registers between the max and the encode).
+__global__ __launch_bounds__(256) void quant_weight_block_kernel(
+    const uint16_t* __restrict__ w, int64_t ld_w, uint8_t* __restrict__ q, int64_t ld_q,
+    float* __restrict__ s, int64_t ld_s, uint32_t kblocks) {
+  __shared__ uint32_t wave_amax[4];
+  const uint32_t nb = blockIdx.x / kblocks;
+  const uint32_t kb = blockIdx.x - nb * kblocks;
+  const uint32_t chunk = threadIdx.x & 15u;
+  const uint32_t r0 = threadIdx.x >> 4;
+  const uint16_t* base = w + (int64_t)nb * kGroup * ld_w + (int64_t)kb * kGroup + chunk * 8u;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = *reinterpret_cast<const uint4*>(base + (int64_t)(r0 + 16 * i) * ld_w);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t t = absmax8_bits(v[i]);
+    m = m > t ? m : t;
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63u) == 0) wave_amax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t a = wave_amax[0] > wave_amax[1] ? wave_amax[0] : wave_amax[1];
+  uint32_t b = wave_amax[2] > wave_amax[3] ? wave_amax[2] : wave_amax[3];
+  m = a > b ? a : b;
+  GroupDivisor d = make_divisor(__uint_as_float(m));
+  uint8_t* qbase = q + (int64_t)nb * kGroup * ld_q + (int64_t)kb * kGroup + chunk * 8u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint2*>(qbase + (int64_t)(r0 + 16 * i) * ld_q) = quant8(v[i], d);
+  if (threadIdx.x == 0) s[(int64_t)nb * ld_s + kb] = d.s;
+}
+
+// ---------------------------------------------------------------------------
+// Whole-tensor scale, two passes.  The tensor is [R, C] with C % 128 == 0,
+// walked as 16-byte chunks (8 values); chunk i is row i / (C/8).
+// Pass 1: each workgroup writes the max over its grid-stride share.
+__global__ __launch_bounds__(256) void absmax_partial_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, uint32_t chunks_per_row, uint64_t nchunks,
+    uint32_t* __restrict__ partials) {
+  __shared__ uint32_t wave_amax[4];
+  uint32_t m = 0;
+  for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < nchunks;
+       i += (uint64_t)gridDim.x * 256u) {
+    uint64_t row = i / chunks_per_row;
+    uint64_t c = i - row * chunks_per_row;
+    uint4 v = *reinterpret_cast<const uint4*>(x + row * ld_x + c * 8u);
+    uint32_t t = absmax8_bits(v);
+    m = m > t ? m : t;
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63u) == 0) wave_amax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = wave_amax[0] > wave_amax[1] ? wave_amax[0] : wave_amax[1];
+    uint32_t b = wave_amax[2] > wave_amax[3] ? wave_amax[2] : wave_amax[3];
+    partials[blockIdx.x] = a > b ? a : b;
+  }
+}
+
+// Pass 2: every workgroup folds the partials into the tensor amax, then
+// encodes its grid-stride share; workgroup 0 writes the scale.
+__global__ __launch_bounds__(256) void quant_tensor_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
+    float* __restrict__ s, uint32_t chunks_per_row, uint64_t nchunks,
+    const uint32_t* __restrict__ partials, uint32_t npartials) {
+  __shared__ uint32_t wave_amax[4];
+  uint32_t m = 0;
+  for (uint32_t i = threadIdx.x; i < npartials; i += 256u) {
+    uint32_t t = partials[i];
+    m = m > t ? m : t;
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63u) == 0) wave_amax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t a = wave_amax[0] > wave_amax[1] ? wave_amax[0] : wave_amax[1];
+  uint32_t b = wave_amax[2] > wave_amax[3] ? wave_amax[2] : wave_amax[3];
+  m = a > b ? a : b;
+  GroupDivisor d = make_divisor(__uint_as_float(m));
+  if (blockIdx.x == 0 && threadIdx.x == 0) s[0] = d.s;
+  for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < nchunks;
+       i += (uint64_t)gridDim.x * 256u) {
+    uint64_t row = i / chunks_per_row;
+    uint64_t c = i - row * chunks_per_row;
+    uint4 v = *reinterpret_cast<const uint4*>(x + row * ld_x + c * 8u);
+    *reinterpret_cast<uint2*>(q + row * ld_q + c * 8u) = quant8(v, d);
+  }
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void encode_f32_kernel(const float* __restrict__ x, uint64_t n,
+                                                         uint8_t* __restrict__ codes) {
+  uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  if (i < n) codes[i] = e4m3_encode_one(x[i]);
+}
+
+}  // namespace
+
+hipError_t launch_quant_act_block(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                  uint8_t* q, int64_t ld_q, float* s, int64_t ld_s,
+                                  hipStream_t st) {
+  constexpr int GPT = 2;
+  const uint32_t groups = (uint32_t)(K / kGroup);
+  const uint32_t per_block = 16u * GPT;
+  const uint32_t bpr = (groups + per_block - 1) / per_block;
+  const uint64_t grid = (uint64_t)bpr * (uint64_t)M;
+  hipLaunchKernelGGL(quant_act_block_kernel<GPT>, dim3((uint32_t)grid), dim3(256), 0, st, x,
+                     ld_x, q, ld_q, s, ld_s, groups, bpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
+                                     uint8_t* q, int64_t ld_q, float* s, int64_t ld_s,
+                                     hipStream_t st) {
+  const uint32_t kb = (uint32_t)(K / kGroup);
+  const uint64_t grid = (uint64_t)(N / kGroup) * kb;
+  hipLaunchKernelGGL(quant_weight_block_kernel, dim3((uint32_t)grid), dim3(256), 0, st, w, ld_w,
+                     q, ld_q, s, ld_s, kb);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tensor(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
+                               uint8_t* q, int64_t ld_q, float* s, uint32_t* partials,
+                               hipStream_t st) {
+  const uint32_t cpr = (uint32_t)(C / 8);
+  const uint64_t nchunks = (uint64_t)R * cpr;
+  uint64_t want = (nchunks + 255) / 256;
+  const uint32_t p1 = (uint32_t)(want < (uint64_t)kTensorPartials ? want : kTensorPartials);
+  hipLaunchKernelGGL(absmax_partial_kernel, dim3(p1), dim3(256), 0, st, x, ld_x, cpr, nchunks,
+                     partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // second pass: enough workgroups to cover the chip several times over
+  uint64_t want2 = (nchunks + 255) / 256;
+  const uint32_t p2 = (uint32_t)(want2 < 8192 ? want2 : 8192);
+  hipLaunchKernelGGL(quant_tensor_kernel, dim3(p2), dim3(256), 0, st, x, ld_x, q, ld_q, s, cpr,
+                     nchunks, partials, p1);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_f32(const float* x, int64_t n, uint8_t* codes, hipStream_t st) {
+  const uint64_t grid = ((uint64_t)n + 255) / 256;
+  hipLaunchKernelGGL(encode_f32_kernel, dim3((uint32_t)grid), dim3(256), 0, st, x, (uint64_t)n,
+                     codes);
+  return hipGetLastError();
+}
+
+}  // namespace fp8k

@@ -1,0 +1,169 @@
+/*
+ * fp8w8a8.h -- C ABI of the FP8 W8A8 block-scaled linear layer for gfx950.
+ *
+ * What the library computes (the passages each call follows are named on
+ * the call):
+ *   1. dynamic activation quantization: per token, per 128-element group,
+ *      scale = amax / 448, codes = E4M3(x / scale) rounded to nearest even
+ *      and saturating;
+ *   2. 128x128 block quantization of the weight (the same rule per block);
+ *   3. the block-scaled FP8 x FP8 GEMM out = A . W^T with fp32 accumulation,
+ *      the two scales applied once per 128-wide K block, bf16 output.
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronizes; it enqueues kernels on
+ *     `stream` (a hipStream_t; NULL is the default stream) and returns.
+ *   - bf16 tensors are raw uint16 bit patterns, FP8 tensors raw uint8 OCP
+ *     E4M3 codes (bias 7, max 448, NaN = S.1111.111, no infinity), scales
+ *     fp32.  Matrices are row-major with an explicit leading dimension in
+ *     elements (ld >= row length).
+ *   - Argument errors are detected on the host and returned before anything
+ *     is enqueued; a failed launch returns FP8_ERR_LAUNCH.  On error no
+ *     output is written.
+ *   - Inputs and outputs must not overlap (FP8_ERR_ALIAS).
+ *   - M = 0 is a valid empty call (nothing is enqueued).  K and N must be
+ *     positive multiples of 128.
+ *   - Alignment: base pointers of bf16 and FP8 tensors 16-byte aligned,
+ *     scale pointers 4-byte aligned; ld of bf16 tensors a multiple of 8,
+ *     of FP8 tensors a multiple of 16 (FP8_ERR_ALIGN).
+ *   - Calls are thread-safe; the only global state is a per-device cache of
+ *     the architecture check.  Calls on one stream are ordered; calls on
+ *     different streams that write the same buffers race (caller's duty).
+ *   - Inputs are assumed finite (no NaN/Inf in bf16 inputs).
+ *
+ * Page references: "[vLLM] FP8" = blog.secrett2633.cloud/opensource/vllm/fp8;
+ * "FP8 Quantization" = zzong2006.github.io fp8-quantization;
+ * "FP8 and FP4: Throughput Needs Scaling" = llm-engineer.pages.dev card.
+ */
+#ifndef FP8W8A8_H
+#define FP8W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8_OK = 0,
+  FP8_ERR_NULL = 1,       /* a required pointer is NULL */
+  FP8_ERR_SHAPE = 2,      /* K or N not a positive multiple of 128, M < 0, or too large */
+  FP8_ERR_STRIDE = 3,     /* a leading dimension is smaller than the row length */
+  FP8_ERR_ALIGN = 4,      /* pointer or leading-dimension alignment */
+  FP8_ERR_BLOCK = 5,      /* weight block size other than 128 x 128 */
+  FP8_ERR_SCHEME = 6,     /* unsupported scale mode / scheme combination */
+  FP8_ERR_WORKSPACE = 7,  /* workspace missing or smaller than fp8_workspace_bytes() */
+  FP8_ERR_DEVICE = 8,     /* current device is not gfx950, or no device */
+  FP8_ERR_LAUNCH = 9,     /* the kernel launch failed */
+  FP8_ERR_ALIAS = 10      /* an output overlaps an input or another output */
+} fp8_status;
+
+/* Scale modes.
+ * FP8_SCALE_BLOCK : activations 1x128 per row, weights 128x128 blocks
+ *                   (the dynamic 128-group and static 128-block schemes of
+ *                   "[vLLM] FP8", scaling strategies).
+ * FP8_SCALE_TENSOR: one scale for the whole tensor, computed dynamically from
+ *                   the tensor's amax (the dynamic per-tensor scheme). */
+enum { FP8_SCALE_BLOCK = 0, FP8_SCALE_TENSOR = 1 };
+
+/* Operation ids for fp8_workspace_bytes(). */
+enum { FP8_OP_QUANT_ACT = 0, FP8_OP_QUANT_WEIGHT = 1, FP8_OP_GEMM = 2 };
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* fp8_status_str(fp8_status s);
+
+/* Bytes of device workspace a call needs (0 if none).  For op
+ * FP8_OP_QUANT_ACT the shape is (M, K); for FP8_OP_QUANT_WEIGHT it is (N, K)
+ * passed as (rows = M argument, K); FP8_OP_GEMM needs none. */
+size_t fp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int scale_mode);
+
+/* fp8_quant_act -- dynamic activation quantization.
+ * Follows "FP8 Quantization" sections C and D.2 (activation scales computed
+ * at run time per call) and "[vLLM] FP8", block quantization (the block path
+ * takes only a dynamic activation scheme) and scaling strategies (dynamic
+ * 128-group and dynamic per-tensor).
+ *   x      [M, K] bf16, ld_x elements per row                      (input)
+ *   q      [M, K] E4M3 codes, ld_q bytes per row                    (output)
+ *   scales FP8_SCALE_BLOCK : [M, K/128] fp32, ld_s >= K/128         (output)
+ *          FP8_SCALE_TENSOR: scales[0], one fp32                    (output)
+ *   For each group G (1x128 slice of a row, or the whole tensor):
+ *     amax = max |x|, s = fp32(amax) / 448 (IEEE round to nearest),
+ *     code = E4M3_RNE_saturating(fp32(x) / s), the quotient correctly
+ *     rounded; an all-zero group gets s = 0 and codes +-0 by x's sign.
+ *   workspace: FP8_SCALE_TENSOR needs fp8_workspace_bytes(FP8_OP_QUANT_ACT,
+ *     M, 0, K, FP8_SCALE_TENSOR) bytes of device memory (4-byte aligned,
+ *     contents need not be initialized); FP8_SCALE_BLOCK needs none. */
+fp8_status fp8_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                         uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s,
+                         int scale_mode, void* workspace, size_t ws_bytes, void* stream);
+
+/* fp8_quant_weight_block -- weight quantization, done once, offline.
+ * Follows "[vLLM] FP8", block quantization (two-dimensional 128x128 blocks,
+ * one scale each; block mode needs a pre-quantized checkpoint, which this
+ * call produces) and "why this design" item 2 (an outlier stays inside its
+ * block); "FP8 Quantization" D.1 (block size 128).
+ *   w      [N, K] bf16, ld_w elements per row                      (input)
+ *   q      [N, K] E4M3 codes, ld_q bytes per row                    (output)
+ *   scales FP8_SCALE_BLOCK : [N/128, K/128] fp32, ld_s >= K/128     (output)
+ *          FP8_SCALE_TENSOR: scales[0]                               (output)
+ *   block_n, block_k: must both be 128 in FP8_SCALE_BLOCK mode (the block
+ *   size has two dimensions; other sizes give FP8_ERR_BLOCK); ignored in
+ *   FP8_SCALE_TENSOR mode.
+ *   Same per-group rule as fp8_quant_act with G = one 128x128 block (or the
+ *   tensor).  workspace as for fp8_quant_act with M = N. */
+fp8_status fp8_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
+                                  uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s,
+                                  int block_n, int block_k, int scale_mode,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
+/* fp8_block_gemm -- out = A . W^T on FP8 operands.
+ * Follows "FP8 and FP4: Throughput Needs Scaling", kernel-caveat card (FP8
+ * operands straight into the matrix unit, wide accumulation) and "[vLLM]
+ * FP8", block quantization (128x128 weight blocks) with the dynamic
+ * 128-group activation scheme.
+ *   a_q [M, K] codes (ld_a), a_s scales (ld_as), w_q [N, K] codes (ld_w),
+ *   w_s scales (ld_ws), out [M, N] bf16 (ld_out).
+ *   FP8_SCALE_BLOCK : a_s [M, K/128], w_s [N/128, K/128] and
+ *     out[m,n] = bf16_RNE( sum_kb a_s[m,kb] * w_s[n/128,kb] *
+ *                          sum_{k in kb} dec(a_q[m,k]) * dec(w_q[n,k]) )
+ *     accumulated in fp32.
+ *   FP8_SCALE_TENSOR: a_s[0], w_s[0]; out = bf16(a_s * w_s * sum_k ...).
+ *   Mixing a per-tensor activation scale with block weights (or the reverse)
+ *   is not a mode (FP8_ERR_SCHEME).  No workspace is used. */
+fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, int64_t ld_as,
+                          const uint8_t* w_q, int64_t ld_w, const float* w_s, int64_t ld_ws,
+                          uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
+                          int scale_mode, void* workspace, size_t ws_bytes, void* stream);
+
+/* Host-only validation: the argument checks of the three calls above, in the
+ * same order, without touching any device (no device check, no launch). */
+fp8_status fp8_validate_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                  const uint8_t* q, int64_t ld_q, const float* scales,
+                                  int64_t ld_s, int scale_mode, const void* workspace,
+                                  size_t ws_bytes);
+fp8_status fp8_validate_quant_weight_block(const uint16_t* w, int64_t N, int64_t K,
+                                           int64_t ld_w, const uint8_t* q, int64_t ld_q,
+                                           const float* scales, int64_t ld_s, int block_n,
+                                           int block_k, int scale_mode,
+                                           const void* workspace, size_t ws_bytes);
+fp8_status fp8_validate_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s,
+                                   int64_t ld_as, const uint8_t* w_q, int64_t ld_w,
+                                   const float* w_s, int64_t ld_ws, const uint16_t* out,
+                                   int64_t ld_out, int64_t M, int64_t N, int64_t K,
+                                   int scale_mode);
+
+/* fp8_e4m3_encode_f32 -- the device element encoder on its own.
+ * codes[i] = E4M3 of x[i]: round to nearest even, magnitudes above 448 and
+ * infinities saturate to 448, NaN gives the NaN code with x's sign, the sign
+ * of zero is kept.  Format as in "[vLLM] FP8" format table.  Exposed so the
+ * device conversion can be checked value by value.  x: n fp32 (4-byte
+ * aligned), codes: n bytes; n >= 0. */
+fp8_status fp8_e4m3_encode_f32(const float* x, int64_t n, uint8_t* codes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8W8A8_H */

@@ -1,0 +1,399 @@
+"""Parity of the HIP path with the CPU oracle (needs a gfx950 GPU).
+
+Every call goes through the C ABI (libfp8w8a8.so via the ctypes binding).
+Inputs are the seeded workloads; expected values come from oracle/ only.
+Codes and scales must be bit-exact; the GEMM must pass the oracle's
+tolerance gate (elementwise 1e-2 * rms(ref) + half a bf16 ulp, Frobenius
+<= 4e-3).  Full-size workloads are compared on every code and scale where the
+oracle is fast enough, otherwise on sampled rows / block rows and on sampled
+output rows and columns computed by the oracle from the bf16 inputs.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import e4m3, gemm, quant, tolerance
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import fp8_w8a8_block_amd as fp8
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host_u16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def gpu_quant_act(bits, mode="block"):
+    q, s = fp8.quant_act(dev_bf16(bits), mode)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def gpu_quant_weight(bits, mode="block"):
+    q, s = fp8.quant_weight_block(dev_bf16(bits), mode)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def assert_codes_equal(got, want, what):
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got != want)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} code mismatches, first at {i}: "
+                             f"got {got[i]:#04x} want {want[i]:#04x}")
+
+
+def assert_scales_equal(got, want, what):
+    g = np.asarray(got, dtype=np.float32).view(np.uint32)
+    w = np.asarray(want, dtype=np.float32).view(np.uint32)
+    if not np.array_equal(g, w):
+        bad = np.argwhere(g != w)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} scale mismatches, first at {i}: "
+                             f"got {got[i]!r} want {want[i]!r}")
+
+
+# ---------------------------------------------------------------------------
+# element encoder
+
+def test_encoder_targeted_values():
+    t = e4m3.decode_table()
+    pos = t[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    vals = [pos, mids]
+    for ulps in (1, 2, 3):
+        f = mids.astype(np.float32)
+        up = f.copy()
+        dn = f.copy()
+        for _ in range(ulps):
+            up = np.nextafter(up, np.float32(np.inf))
+            dn = np.nextafter(dn, np.float32(-np.inf))
+        vals += [up.astype(np.float64), dn.astype(np.float64)]
+    rng = np.random.default_rng(41)
+    vals.append(np.exp(rng.uniform(np.log(1e-45), np.log(1e3), 200000)))
+    vals.append(np.array([448.0, 448.00003, 455.9, 463.99997, 464.0, 464.00003, 500.0, 1e30,
+                          np.inf, 2.0 ** -10, 2.0 ** -149, 0.0]))
+    v = np.concatenate(vals).astype(np.float32)
+    v = np.concatenate([v, -v, np.array([np.nan, -np.nan], dtype=np.float32)])
+    got = fp8.encode_f32(torch.from_numpy(v).cuda()).cpu().numpy()
+    assert_codes_equal(got, e4m3.encode(v), "encoder")
+
+
+# ---------------------------------------------------------------------------
+# activation quantizer
+
+@pytest.mark.parametrize("case", ["zeros", "negzero", "tiny", "huge", "mixed", "single",
+                                  "ragged_m", "all_amax"])
+def test_quant_act_edge_cases(case):
+    bits = synth.edge_activations()[case]
+    log("quant_act edge", case, bits.shape)
+    q, s = gpu_quant_act(bits)
+    wq, ws = quant.quant_act_ref(bits)
+    assert_scales_equal(s, ws, f"scales[{case}]")
+    assert_codes_equal(q, wq, f"codes[{case}]")
+
+
+def test_quant_act_worked_group():
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "e4m3_worked_group.json")))
+    row = np.zeros(128, dtype=np.float32)
+    row[:len(g["cases"])] = [c["x"] for c in g["cases"]]
+    bits = synth.f32_to_bf16_bits(row)[None, :]
+    q, s = gpu_quant_act(bits)
+    assert s[0, 0] == 1.0
+    assert q[0, :len(g["cases"])].tolist() == [int(c["code"], 16) for c in g["cases"]]
+
+
+def test_quant_act_division_adversarial():
+    import json, os
+    pairs = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                        "div_adversarial.json")))["pairs_amax_bits_x_bits"]
+    rows = np.zeros((len(pairs), 128), dtype=np.uint16)
+    for i, (ab, xb) in enumerate(pairs):
+        rows[i, 0], rows[i, 1] = ab, xb
+    q, s = gpu_quant_act(rows)
+    wq, ws = quant.quant_act_ref(rows)
+    assert_scales_equal(s, ws, "scales")
+    assert_codes_equal(q, wq, "codes")
+
+
+@pytest.mark.parametrize("name,M", [("tiny", None), ("decode", 1), ("decode", 4), ("decode", 16),
+                                    ("prefill", None), ("mlp_down", None)])
+def test_quant_act_configs_full(name, M):
+    c = synth.CONFIGS[name]
+    M = c["M"] if M is None else M
+    ch = synth.outlier_channels(c["cfg"], c["K"], c["n_outliers"])
+    bits = synth.make_activation(c["cfg"], M, c["K"], c["a_kind"], c["a_std"], ch, c["outlier_mult"])
+    log("quant_act", name, bits.shape)
+    q, s = gpu_quant_act(bits)
+    wq, ws = quant.quant_act_ref(bits)
+    assert_scales_equal(s, ws, f"scales[{name}]")
+    assert_codes_equal(q, wq, f"codes[{name}]")
+
+
+def test_quant_act_large_sampled_rows():
+    c = synth.CONFIGS["large"]
+    ch = synth.outlier_channels(c["cfg"], c["K"], c["n_outliers"])
+    bits = synth.make_activation(c["cfg"], c["M"], c["K"], c["a_kind"], c["a_std"], ch,
+                                 c["outlier_mult"])
+    log("quant_act large", bits.shape)
+    q, s = gpu_quant_act(bits)
+    rows = np.random.default_rng(42).choice(c["M"], 256, replace=False)
+    wq, ws = quant.quant_act_ref(bits[rows])
+    assert_scales_equal(s[rows], ws, "scales[large]")
+    assert_codes_equal(q[rows], wq, "codes[large]")
+
+
+def test_quant_act_strided_and_ragged():
+    rng = np.random.default_rng(43)
+    bits = synth.f32_to_bf16_bits(rng.standard_normal((37, 1024)).astype(np.float32))
+    big = np.zeros((37, 1024 + 64), dtype=np.uint16)
+    big[:, :1024] = bits
+    x = dev_bf16(big)[:, :1024]                     # ld_x = 1088
+    qbuf = torch.zeros((37, 1024 + 32), dtype=torch.uint8, device="cuda")
+    sbuf = torch.zeros((37, 11), dtype=torch.float32, device="cuda")
+    q, s = fp8.quant_act(x, "block", q=qbuf[:, :1024], scales=sbuf[:, :8])
+    torch.cuda.synchronize()
+    wq, ws = quant.quant_act_ref(bits)
+    assert_codes_equal(qbuf[:, :1024].cpu().numpy(), wq, "codes")
+    assert_scales_equal(sbuf[:, :8].cpu().numpy(), ws, "scales")
+    assert np.all(qbuf[:, 1024:].cpu().numpy() == 0)     # padding untouched
+    assert np.all(sbuf[:, 8:].cpu().numpy() == 0)
+
+
+def test_quant_act_empty():
+    x = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    q, s = fp8.quant_act(x)
+    assert q.shape == (0, 512) and s.shape == (0, 4)
+
+
+# ---------------------------------------------------------------------------
+# weight quantizer
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "mlp_down"])
+def test_quant_weight_configs_full(name):
+    c = synth.CONFIGS[name]
+    bits = synth.make_weight(c["cfg"], c["N"], c["K"], c["w_std"])
+    log("quant_weight", name, bits.shape)
+    q, s = gpu_quant_weight(bits)
+    wq, ws = quant.quant_weight_block_ref(bits)
+    assert_scales_equal(s, ws, f"wscales[{name}]")
+    assert_codes_equal(q, wq, f"wcodes[{name}]")
+
+
+def test_quant_weight_large_sampled_blocks():
+    c = synth.CONFIGS["large"]
+    bits = synth.make_weight(c["cfg"], c["N"], c["K"], c["w_std"])
+    log("quant_weight large", bits.shape)
+    q, s = gpu_quant_weight(bits)
+    for nb in (0, 77, 223):
+        sl = slice(nb * 128, (nb + 1) * 128)
+        wq, ws = quant.quant_weight_block_ref(bits[sl])
+        assert_scales_equal(s[nb:nb + 1], ws, f"wscales[large:{nb}]")
+        assert_codes_equal(q[sl], wq, f"wcodes[large:{nb}]")
+
+
+def test_quant_weight_edge_blocks():
+    e = synth.edge_activations()
+    # build a 256 x 512 weight from edge rows: zero blocks, tiny blocks, huge blocks
+    w = np.zeros((256, 512), dtype=np.uint16)
+    w[0:2] = e["tiny"][:2]
+    w[128:130] = e["huge"]
+    w[200, 300] = 0x8000
+    q, s = gpu_quant_weight(w)
+    wq, ws = quant.quant_weight_block_ref(w)
+    assert_scales_equal(s, ws, "wscales")
+    assert_codes_equal(q, wq, "wcodes")
+
+
+# ---------------------------------------------------------------------------
+# per-tensor quantization (MLP down-projection variant)
+
+def test_quant_tensor_mlp_down():
+    c = synth.CONFIGS["mlp_down"]
+    ch = synth.outlier_channels(c["cfg"], c["K"], c["n_outliers"])
+    a = synth.make_activation(c["cfg"], c["M"], c["K"], c["a_kind"], c["a_std"], ch, c["outlier_mult"])
+    w = synth.make_weight(c["cfg"], c["N"], c["K"], c["w_std"])
+    qa, sa = gpu_quant_act(a, "tensor")
+    wqa, wsa = quant.quant_tensor_ref(a)
+    assert_scales_equal(sa, wsa, "tensor scale A")
+    assert_codes_equal(qa, wqa, "tensor codes A")
+    qw, sw = gpu_quant_weight(w, "tensor")
+    wqw, wsw = quant.quant_tensor_ref(w)
+    assert_scales_equal(sw, wsw, "tensor scale W")
+    assert_codes_equal(qw, wqw, "tensor codes W")
+
+
+def test_quant_tensor_edges():
+    for case in ("zeros", "negzero", "tiny", "ragged_m"):
+        bits = synth.edge_activations()[case]
+        q, s = gpu_quant_act(bits, "tensor")
+        wq, ws = quant.quant_tensor_ref(bits)
+        assert_scales_equal(s, ws, f"tensor scale {case}")
+        assert_codes_equal(q, wq, f"tensor codes {case}")
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+
+def run_gemm(a_bits, w_bits, mode="block"):
+    """GPU: quantize A and W, then GEMM.  Returns out bits (uint16 [M, N])."""
+    x = dev_bf16(a_bits)
+    wd = dev_bf16(w_bits)
+    wq, ws = fp8.quant_weight_block(wd, mode)
+    aq, as_ = fp8.quant_act(x, mode)
+    out = fp8.block_gemm(aq, as_, wq, ws, mode)
+    torch.cuda.synchronize()
+    return host_u16(out)
+
+
+def oracle_gemm(a_bits, w_bits, mode="block"):
+    if mode == "block":
+        aq, as_ = quant.quant_act_ref(a_bits)
+        wq, ws = quant.quant_weight_block_ref(w_bits)
+        return gemm.gemm_block_ref(aq, as_, wq, ws)
+    aq, as_ = quant.quant_tensor_ref(a_bits)
+    wq, ws = quant.quant_tensor_ref(w_bits)
+    return gemm.gemm_tensor_ref(aq, as_, wq, ws)
+
+
+def check_out(out_bits, ref, what):
+    r = tolerance.check(out_bits, ref)
+    log(what, {k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
+    assert r["ok"], (what, r)
+    return r
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_gemm_decode_full(M):
+    d = synth.make_config("decode", M=M)
+    log("gemm decode", M)
+    out = run_gemm(d["A"], d["W"])
+    check_out(out, oracle_gemm(d["A"], d["W"]), f"decode M={M}")
+
+
+def test_gemm_tiny_full():
+    d = synth.make_config("tiny")
+    out = run_gemm(d["A"], d["W"])
+    check_out(out, oracle_gemm(d["A"], d["W"]), "tiny")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (3, 256, 384), (17, 384, 640), (100, 256, 1024),
+                                   (129, 512, 512), (300, 384, 640), (256, 256, 2304)])
+def test_gemm_ragged_full(M, N, K):
+    rng = np.random.default_rng([M, N, K])
+    a = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
+    log("gemm ragged", M, N, K)
+    out = run_gemm(a, w)
+    check_out(out, oracle_gemm(a, w), f"ragged {M}x{N}x{K}")
+    out_t = run_gemm(a, w, "tensor")
+    check_out(out_t, oracle_gemm(a, w, "tensor"), f"ragged tensor {M}x{N}x{K}")
+
+
+def _sampled(name, rows_n, cols_n, mode="block"):
+    c = synth.CONFIGS[name]
+    d = synth.make_config(name)
+    log("gemm sampled", name, mode, (d["M"], d["N"], d["K"]))
+    out = run_gemm(d["A"], d["W"], mode)
+    rng = np.random.default_rng(44)
+    rows = np.sort(rng.choice(d["M"], rows_n, replace=False))
+    cols = np.sort(rng.choice(d["N"], cols_n, replace=False))
+    if mode == "block":
+        aq, as_ = quant.quant_act_ref(d["A"][rows])
+        wq_rows = np.empty((cols_n, d["K"]), dtype=np.uint8)
+        ws_rows = np.empty((cols_n, d["K"] // 128), dtype=np.float32)
+        for nb in np.unique(cols // 128):
+            sl = slice(nb * 128, (nb + 1) * 128)
+            bq, bs = quant.quant_weight_block_ref(d["W"][sl])
+            sel = np.nonzero(cols // 128 == nb)[0]
+            wq_rows[sel] = bq[cols[sel] - nb * 128]
+            ws_rows[sel] = bs[0]
+        ref = gemm.gemm_block_ref_rows(aq, as_, wq_rows, ws_rows)
+    else:
+        a_amax = quant.tensor_amax_ref(d["A"])
+        w_amax = quant.tensor_amax_ref(d["W"])
+        aq, as_ = quant.quant_tensor_with_amax_ref(d["A"][rows], a_amax)
+        wq, ws = quant.quant_tensor_with_amax_ref(d["W"][cols], w_amax)
+        ref = gemm.gemm_tensor_ref(aq, as_, wq, ws)
+    return check_out(out[np.ix_(rows, cols)], ref, f"{name} {mode} sampled")
+
+
+def test_gemm_prefill_sampled():
+    _sampled("prefill", 96, 1024)
+
+
+def test_gemm_mlp_down_sampled():
+    _sampled("mlp_down", 64, 1024)
+
+
+def test_gemm_mlp_down_tensor_sampled():
+    _sampled("mlp_down", 64, 1024, "tensor")
+
+
+def test_gemm_large_sampled():
+    _sampled("large", 48, 768)
+
+
+def test_gemm_small_integers_exact():
+    """Codes are small integers, unit scales: every partial is exact, so the
+    bf16 output must equal the exact result bit for bit."""
+    rng = np.random.default_rng(45)
+    M, N, K = 40, 256, 512
+    # codes of the integers -4..4 (exactly representable), unit scales
+    ints = rng.integers(-4, 5, size=(M, K)).astype(np.float64)
+    intw = rng.integers(-2, 3, size=(N, K)).astype(np.float64)
+    aq = e4m3.encode(ints)
+    wq = e4m3.encode(intw)
+    exact = ints @ intw.T
+    assert np.all(np.abs(exact) <= 256)
+    a_s = torch.ones((M, K // 128), dtype=torch.float32, device="cuda")
+    w_s = torch.ones((N // 128, K // 128), dtype=torch.float32, device="cuda")
+    out = fp8.block_gemm(torch.from_numpy(aq).cuda(), a_s, torch.from_numpy(wq).cuda(), w_s)
+    got = tolerance.bf16_bits_to_f64(host_u16(out))
+    assert np.array_equal(got, exact)
+    M1 = 5
+    out1 = fp8.block_gemm(torch.from_numpy(aq[:M1]).cuda(), a_s[:M1], torch.from_numpy(wq).cuda(), w_s)
+    assert np.array_equal(tolerance.bf16_bits_to_f64(host_u16(out1)), exact[:M1])
+
+
+def test_gemm_determinism():
+    d = synth.make_config("tiny")
+    o1 = run_gemm(d["A"], d["W"])
+    o2 = run_gemm(d["A"], d["W"])
+    assert np.array_equal(o1, o2)
+    e = synth.make_config("decode", M=16)
+    x = dev_bf16(e["A"])
+    wq, ws = fp8.quant_weight_block(dev_bf16(e["W"]))
+    outs = [host_u16(fp8.linear(x, wq, ws)) for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_gemm_empty_and_errors():
+    wq = torch.zeros((256, 512), dtype=torch.uint8, device="cuda")
+    ws = torch.ones((2, 4), dtype=torch.float32, device="cuda")
+    aq = torch.zeros((0, 512), dtype=torch.uint8, device="cuda")
+    as_ = torch.ones((0, 4), dtype=torch.float32, device="cuda")
+    out = fp8.block_gemm(aq, as_, wq, ws)
+    assert out.shape == (0, 256)
+    with pytest.raises(ValueError):
+        fp8.block_gemm(torch.zeros((4, 500), dtype=torch.uint8, device="cuda"),
+                       torch.ones((4, 4), dtype=torch.float32, device="cuda"),
+                       torch.zeros((256, 500), dtype=torch.uint8, device="cuda"), ws)
+    with pytest.raises(ValueError):
+        fp8.quant_weight_block(torch.zeros((256, 512), dtype=torch.bfloat16, device="cuda"),
+                               block_n=64)
