@@ -13,9 +13,9 @@ Infinity Cache) so the weight really comes from HBM.
 Timing: W warm-up steps, then exactly K steps replayed from HIP graphs (one
 graph per step pattern), bracketed by torch.cuda.synchronize() on both sides
 (one process, one GPU: no barrier needed).  The dominant kernel's average
-launch duration is measured with HIP events around each launch on the
-launch stream, in a pass whose launches are queued behind a GPU-side delay
-so no host gap falls between an event and its kernel.
+launch duration is measured with one HIP event pair on the launch stream
+around a run of back-to-back launches of that kernel, queued behind a
+bounded GPU-side delay so that no host gap falls inside the timed span.
 
 Prints ONE JSON line.
 """
@@ -118,18 +118,13 @@ class Workload:
         from math import gcd
         return self.ncopy // gcd(self.ncopy, self.launches_per_step)
 
-    def step(self, s, on_gemm=None):
+    def step(self, s):
         fp8 = self.fp8
         for j, M in enumerate(self.Ms):
             fp8.quant_act(self.x[j], self.mode, workspace=self.ws_buf, q=self.aq[j],
                           scales=self.as_[j])
-            ev = on_gemm() if on_gemm else None
-            if ev:
-                ev[0].record()
             fp8.block_gemm(self.aq[j], self.as_[j], self.wq[self.copy_index(s, j)], self.ws,
                            self.mode, out=self.out[j])
-            if ev:
-                ev[1].record()
 
     def bytes_per_step(self):
         pt = self.mode == "tensor"
@@ -141,24 +136,25 @@ class Workload:
         return sum(gemm_flops(M, self.N, self.K) for M in self.Ms)
 
 
-def time_gemm_launches(wl, n_steps):
-    """Average duration of the GEMM launches, from HIP event pairs on the launch
-    stream; the launches are queued behind a GPU-side delay first."""
+def time_gemm_launches(wl, n_launches):
+    """Average duration of the GEMM kernel: one HIP event pair on the launch
+    stream around n back-to-back GEMM launches (cycling through the batch
+    sizes and weight copies of the step), all queued behind a bounded
+    GPU-side delay so that no host gap falls inside the timed span."""
     import torch
-    pairs = []
-
-    def mk():
-        p = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        pairs.append(p)
-        return p
-
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     torch.cuda._sleep(int(5e7))          # a bounded GPU-side delay while the host queues work
-    for s in range(n_steps):
-        wl.step(s, on_gemm=mk)
+    e0.record()
+    for i in range(n_launches):
+        j = i % len(wl.Ms)
+        wl.fp8.block_gemm(wl.aq[j], wl.as_[j], wl.wq[i % wl.ncopy], wl.ws, wl.mode,
+                          out=wl.out[j])
+    e1.record()
     torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in pairs])
-    return float(ms.mean()), float(np.median(ms)), len(ms)
+    ms = e0.elapsed_time(e1) / n_launches
+    return float(ms), n_launches
 
 
 def cpu_baseline(wl, target_s):
@@ -251,7 +247,8 @@ def main():
     total_b, q_b, g_b = wl.bytes_per_step()
     flops = wl.flops_per_step()
 
-    g_ms_mean, g_ms_med, n_l = time_gemm_launches(wl, min(K, 64))
+    n_l = 96 if decode else 24
+    g_ms_mean, n_l = time_gemm_launches(wl, n_l)
     gemm_bytes_per_launch = g_b / wl.launches_per_step
     flops_per_launch = flops / wl.launches_per_step
 
@@ -269,7 +266,6 @@ def main():
     roof["traffic"] = None
     roof["kernel"] = "gemm_decode_kernel" if decode else "gemm_tile_kernel"
     roof["avg_launch_us"] = g_ms_mean * 1e3
-    roof["median_launch_us"] = g_ms_med * 1e3
     roof["launches_timed"] = n_l
     roof["algorithmic_bytes_per_launch" if decode else "flop_per_launch"] = (
         gemm_bytes_per_launch if decode else flops_per_launch)

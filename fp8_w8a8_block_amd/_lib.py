@@ -94,7 +94,15 @@ def _rows(t, dtype, name):
         raise ValueError(f"{name} must be a 2-D row-major tensor with unit column stride")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    return t.shape[0], t.shape[1], t.stride(0)
+    # a single row's stride is arbitrary in torch; its leading dimension is its length
+    return t.shape[0], t.shape[1], (t.stride(0) if t.shape[0] > 1 else t.shape[1])
+
+
+def _ld(t):
+    """Leading dimension of a 2-D scale tensor (one row: its length)."""
+    if t.dim() != 2:
+        return 1
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
 def workspace_bytes(op, M, N, K, scale_mode):
@@ -114,13 +122,14 @@ def quant_act(x, scale_mode="block", workspace=None, q=None, scales=None):
         if scales is None:
             shape = (M, K // 128) if mode == SCALE_BLOCK else (1,)
             scales = torch.empty(shape, dtype=torch.float32, device=x.device)
-        ld_s = scales.stride(0) if scales.dim() == 2 else 1
+        ld_s = _ld(scales)
+        ld_q = q.stride(0) if q.shape[0] > 1 else q.shape[1]
         nws = workspace_bytes(OP_QUANT_ACT, M, 0, K, mode)
         if nws and workspace is None:
             workspace = torch.empty(nws, dtype=torch.uint8, device=x.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        _check(lib().fp8_quant_act(x.data_ptr(), M, K, ld_x, q.data_ptr(), q.stride(0),
+        _check(lib().fp8_quant_act(x.data_ptr(), M, K, ld_x, q.data_ptr(), ld_q,
                                    scales.data_ptr(), ld_s, mode, ws_ptr, ws_len, _stream(x)))
     return q, scales
 
@@ -133,7 +142,7 @@ def quant_weight_block(w, scale_mode="block", block_n=128, block_k=128, workspac
         q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
         if mode == SCALE_BLOCK:
             scales = torch.empty((max(N // 128, 0), K // 128), dtype=torch.float32, device=w.device)
-            ld_s = scales.stride(0)
+            ld_s = _ld(scales)
         else:
             scales = torch.empty((1,), dtype=torch.float32, device=w.device)
             ld_s = 1
@@ -141,8 +150,8 @@ def quant_weight_block(w, scale_mode="block", block_n=128, block_k=128, workspac
         if nws and workspace is None:
             workspace = torch.empty(nws, dtype=torch.uint8, device=w.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
-        ws_len = workspace.numel() if workspace is not None else 0
-        _check(lib().fp8_quant_weight_block(w.data_ptr(), N, K, ld_w, q.data_ptr(), q.stride(0),
+        ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        _check(lib().fp8_quant_weight_block(w.data_ptr(), N, K, ld_w, q.data_ptr(), K,
                                             scales.data_ptr(), ld_s, int(block_n), int(block_k),
                                             mode, ws_ptr, ws_len, _stream(w)))
     return q, scales
@@ -158,13 +167,14 @@ def block_gemm(a_q, a_s, w_q, w_s, scale_mode="block", out=None):
     for t, nm in ((a_s, "a_s"), (w_s, "w_s")):
         if t.dtype != torch.float32 or not t.is_cuda:
             raise TypeError(f"{nm} must be a float32 device tensor")
-    ld_as = a_s.stride(0) if a_s.dim() == 2 else 1
-    ld_ws = w_s.stride(0) if w_s.dim() == 2 else 1
+    ld_as = _ld(a_s)
+    ld_ws = _ld(w_s)
     with torch.cuda.device(a_q.device):
         if out is None:
             out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+        ld_out = out.stride(0) if out.shape[0] > 1 else out.shape[1]
         _check(lib().fp8_block_gemm(a_q.data_ptr(), ld_a, a_s.data_ptr(), ld_as, w_q.data_ptr(),
-                                    ld_w, w_s.data_ptr(), ld_ws, out.data_ptr(), out.stride(0),
+                                    ld_w, w_s.data_ptr(), ld_ws, out.data_ptr(), ld_out,
                                     M, N, K, mode, None, 0, _stream(a_q)))
     return out
 

@@ -353,10 +353,11 @@ def test_gemm_small_integers_exact():
     """Codes are small integers, unit scales: every partial is exact, so the
     bf16 output must equal the exact result bit for bit."""
     rng = np.random.default_rng(45)
-    M, N, K = 40, 256, 512
-    # codes of the integers -4..4 (exactly representable), unit scales
-    ints = rng.integers(-4, 5, size=(M, K)).astype(np.float64)
-    intw = rng.integers(-2, 3, size=(N, K)).astype(np.float64)
+    M, N, K = 40, 256, 256
+    # codes of small integers (exactly representable), unit scales; every
+    # partial and final sum is an integer of magnitude <= 256, exact in bf16
+    ints = rng.integers(-3, 4, size=(M, K)).astype(np.float64)
+    intw = rng.integers(-1, 2, size=(N, K)).astype(np.float64)
     aq = e4m3.encode(ints)
     wq = e4m3.encode(intw)
     exact = ints @ intw.T
