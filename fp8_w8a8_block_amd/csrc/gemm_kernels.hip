@@ -25,6 +25,9 @@ namespace fp8k {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+
+// the decode path stages all activation scales of a call in LDS
+constexpr int kDecodeMaxKB = 128;             // K <= 16384
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
@@ -51,63 +54,145 @@ __device__ __forceinline__ v8i zero8() {
 }
 
 // ---------------------------------------------------------------------------
-// Decode shape (M <= 16): HBM-bound on the weight.  One workgroup per 16
-// output columns; its KSPLIT waves take interleaved K blocks, keep UNROLL
-// blocks of W loads in flight, and reduce their 16x16 partial sums in LDS.
-template <int KSPLIT, int UNROLL, bool PER_TENSOR>
+// Decode shape (M <= 16): HBM-bound on the weight (one byte per weight
+// element, read once).  A workgroup owns 16 output columns; its KSPLIT
+// waves each own a contiguous run of K blocks, processed in batches of KBW.
+//
+// Operands never go through registers on their way in: each wave streams
+// its weight fragments (16 rows x 128 bytes per K block) and the matching
+// activation fragments into private LDS buffers with global_load_lds_dwordx4,
+// lane-linear, so every load instruction covers eight whole 128-byte rows.
+// (Loading the MFMA layout straight from memory makes each instruction
+// touch 16 rows x 64 bytes, which streams far below the HBM rate.)  Within
+// a row the eight 16-byte chunks are stored XOR-swizzled by (row & 7), so
+// the fragment reads -- 16 rows at one column per ds_read_b128 phase -- hit
+// distinct banks.  While the MFMAs of batch b run, the loads of batch b+1
+// are in flight.  Activation rows >= M repeat row M - 1 in LDS and are
+// zeroed in registers.  The waves' 16x16 partial sums are reduced in LDS.
+//
+// Dynamic LDS: KSPLIT * KBW * 4 KiB operand buffers, then the reduction
+// buffer (KSPLIT * 1 KiB), then the activation scales (16 * KB floats).
+constexpr int kFrag = 2048;                   // 16 rows x 128 bytes
+
+template <int KSPLIT, int KBW>
+constexpr size_t decode_lds_bytes(int KB, bool per_tensor) {
+  return (size_t)KSPLIT * KBW * 2 * kFrag + (size_t)KSPLIT * 4 * 64 * sizeof(float) +
+         (per_tensor ? 0 : (size_t)16 * KB * sizeof(float));
+}
+
+template <int KSPLIT, int KBW, bool PER_TENSOR>
 __global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
     const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
     uint16_t* __restrict__ out, int64_t ld_out, int M, int KB) {
-  __shared__ float red[KSPLIT][4][64];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int kg = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int nb = (int)(n0 >> 7);
-  const uint8_t* wp = w + (n0 + r16) * ld_w + kg * 32;
   const bool arow = r16 < M;
-  const uint8_t* ap = a + (int64_t)(arow ? r16 : 0) * ld_a + kg * 32;
 
-  // rows of the output this lane accumulates: m = 4 kg + i
-  bool mrow[4];
+  uint8_t* wbuf = lds + (size_t)wave * (KBW * 2 * kFrag);     // this wave's W fragments
+  uint8_t* abuf = wbuf + KBW * kFrag;                          // and A fragments
+  float* red = reinterpret_cast<float*>(lds + (size_t)KSPLIT * KBW * 2 * kFrag);
+  float* s_as = red + KSPLIT * 4 * 64;
+
+  // load slot s = 64 j + lane holds row s / 8, stored chunk s % 8, which is
+  // source chunk (s % 8) ^ (row & 7); rows 8..15 have the same (row & 7).
+  const int drow = lane >> 3;
+  const int dchunk = (lane & 7) ^ (drow & 7);
+  const uint8_t* wsrc0 = w + (n0 + drow) * ld_w + dchunk * 16;
+  const uint8_t* wsrc1 = w + (n0 + 8 + drow) * ld_w + dchunk * 16;
+  const uint8_t* asrc0 = a + (int64_t)min(drow, M - 1) * ld_a + dchunk * 16;
+  const uint8_t* asrc1 = a + (int64_t)min(8 + drow, M - 1) * ld_a + dchunk * 16;
+  // fragment reads: row r16, source chunks 2 kg and 2 kg + 1
+  const int rd0 = r16 * 128 + (((2 * kg) ^ (r16 & 7)) * 16);
+  const int rd1 = r16 * 128 + (((2 * kg + 1) ^ (r16 & 7)) * 16);
+
+  const int per = (KB + KSPLIT - 1) / KSPLIT;
+  const int kb_lo = wave * per;
+  const int kb_hi = min(KB, kb_lo + per);
+
+  auto dma = [&](const uint8_t* src, uint8_t* dst) {
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
+  auto issue = [&](int kb0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) mrow[i] = (4 * kg + i) < M;
+    for (int u = 0; u < KBW; ++u) {
+      const int kb = kb0 + u;
+      if (kb < kb_hi) {                               // wave-uniform
+        const int64_t off = (int64_t)kb * 128;
+        dma(wsrc0 + off, wbuf + u * kFrag);
+        dma(wsrc1 + off, wbuf + u * kFrag + 1024);
+        dma(asrc0 + off, abuf + u * kFrag);
+        dma(asrc1 + off, abuf + u * kFrag + 1024);
+      }
+    }
+  };
+  auto frag = [&](const uint8_t* buf) {
+    const uint4 x = *reinterpret_cast<const uint4*>(buf + rd0);
+    const uint4 y = *reinterpret_cast<const uint4*>(buf + rd1);
+    v8i r;
+    r[0] = (int)x.x; r[1] = (int)x.y; r[2] = (int)x.z; r[3] = (int)x.w;
+    r[4] = (int)y.x; r[5] = (int)y.y; r[6] = (int)y.z; r[7] = (int)y.w;
+    return r;
+  };
+
+  if (kb_lo < kb_hi) issue(kb_lo);
+  if (!PER_TENSOR) {
+    // s_as[kb * 16 + m] = sa[m, kb] (rows >= M read 0); queued behind the
+    // first batch's loads
+    for (int i = threadIdx.x; i < KB * 16; i += 64 * KSPLIT) {
+      const int m = i & 15;
+      const int kb = i >> 4;
+      s_as[i] = m < M ? sa[(int64_t)m * ld_sa + kb] : 0.f;
+    }
+  }
+  __syncthreads();
 
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int kb0 = wave; kb0 < KB; kb0 += KSPLIT * UNROLL) {
-    v8i bw[UNROLL], av[UNROLL];
+  for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += KBW) {    // wave-uniform; no barrier inside
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    v8i av[KBW], bw[KBW];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int kb = kb0 + u * KSPLIT;
-      bw[u] = kb < KB ? load32(wp + (int64_t)kb * 128) : zero8();
+    for (int u = 0; u < KBW; ++u) {
+      av[u] = frag(abuf + u * kFrag);
+      bw[u] = frag(wbuf + u * kFrag);
     }
+    // this batch's combined scales, read before the next batch's LDS writes
+    // are queued (LDS reads are ordered behind those)
+    float sc[KBW][4];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int kb = kb0 + u * KSPLIT;
-      av[u] = (arow && kb < KB) ? load32(ap + (int64_t)kb * 128) : zero8();
+    for (int u = 0; u < KBW; ++u) {
+      const int kb = kb0 + u;
+      const int kbc = min(kb, kb_hi - 1);
+      const float s_w = PER_TENSOR ? 0.f : sw[(int64_t)(n0 >> 7) * ld_sw + kbc];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s_a = PER_TENSOR ? 0.f : s_as[kbc * 16 + 4 * kg + i];
+        sc[u][i] = kb < kb_hi ? s_a * s_w : 0.f;
+      }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (kb0 + KBW < kb_hi) issue(kb0 + KBW);
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int kb = kb0 + u * KSPLIT;
+    for (int u = 0; u < KBW; ++u) {
+      const bool ok = arow && (kb0 + u < kb_hi);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) av[u][e] = ok ? av[u][e] : 0;
       if (PER_TENSOR) {
         acc = mfma_fp8(av[u], bw[u], acc);
       } else {
         v4f p = mfma_fp8(av[u], bw[u], v4f{0.f, 0.f, 0.f, 0.f});
-        if (kb < KB) {
-          const float s_w = sw[(int64_t)nb * ld_sw + kb];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float s_a = mrow[i] ? sa[(int64_t)(4 * kg + i) * ld_sa + kb] : 0.f;
-            acc[i] = __builtin_fmaf(s_a * s_w, p[i], acc[i]);
-          }
-        }
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc[u][i], p[i], acc[i]);
       }
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
+  for (int i = 0; i < 4; ++i) red[(wave * 4 + i) * 64 + lane] = acc[i];
   __syncthreads();
   if (wave == 0) {
     const float st = PER_TENSOR ? sa[0] * sw[0] : 1.0f;
@@ -115,7 +200,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
     for (int i = 0; i < 4; ++i) {
       float v = 0.f;
 #pragma unroll
-      for (int s = 0; s < KSPLIT; ++s) v += red[s][i][lane];
+      for (int s2 = 0; s2 < KSPLIT; ++s2) v += red[(s2 * 4 + i) * 64 + lane];
       if (PER_TENSOR) v *= st;
       const int m = 4 * kg + i;
       if (m < M) out[(int64_t)m * ld_out + n0 + r16] = (uint16_t)f32_to_bf16_rne(v);
@@ -250,15 +335,22 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
                        uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
                        bool per_tensor, hipStream_t st) {
   const int KB = (int)(K / 128);
-  if (M <= 16) {
-    constexpr int KSPLIT = 8, UNROLL = 4;
+  if (M <= 16 && KB <= kDecodeMaxKB) {
+#ifndef FP8_DECODE_KSPLIT
+#define FP8_DECODE_KSPLIT 8
+#endif
+#ifndef FP8_DECODE_KBW
+#define FP8_DECODE_KBW 1
+#endif
+    constexpr int KSPLIT = FP8_DECODE_KSPLIT, KBW = FP8_DECODE_KBW;
     dim3 grid((uint32_t)(N / 16));
+    const size_t lds = decode_lds_bytes<KSPLIT, KBW>(KB, per_tensor);
     if (per_tensor)
-      hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, UNROLL, true>), grid, dim3(64 * KSPLIT), 0, st,
+      hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, KBW, true>), grid, dim3(64 * KSPLIT), lds, st,
                          a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
     else
-      hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, UNROLL, false>), grid, dim3(64 * KSPLIT), 0,
-                         st, a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
+      hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, KBW, false>), grid, dim3(64 * KSPLIT), lds, st,
+                         a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
     return hipGetLastError();
   }
   const int tiles_m = (int)((M + kBM - 1) / kBM);
