@@ -328,6 +328,187 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill shape (large M): MFMA-bound.  Workgroup tile BM x BN (256 x 256),
+// eight waves in a 2 x 4 grid, each computing 128 x 64 = 8 x 4 MFMA tiles
+// into 128 fp32 accumulators.  One K step is one 128-wide scale block.
+//
+// Both operand tiles of a K block (BM and BN rows of 128 bytes) are copied
+// into LDS by global_load_lds_dwordx4, lane-linear (one instruction = eight
+// whole rows) with the chunks of a row XOR-swizzled by (row & 7), so the
+// fragment reads are bank-conflict free.  LDS holds two stages: the copy of
+// block kb + 1 is in flight while block kb is multiplied.  The activation
+// scales of block kb + 1 travel through registers into a small LDS array.
+// Per K block each wave reads its 8 A and 4 B fragments from LDS, issues
+// 32 MFMAs into fresh fp32 partials and folds them into the accumulators
+// with (sa[m, kb] * sw[n / 128, kb]); per-tensor scales accumulate in the
+// matrix unit and scale once at the end.
+//
+// Rows past M (and columns past N in a half-filled last tile) read the
+// last valid row and are never stored.  Tiles are visited in groups of
+// kGroupM tile-rows, and consecutive workgroup ids -- which the dispatcher
+// spreads over the 8 XCDs -- are remapped so that each XCD works on a
+// compact block of tiles and shares their A and B panels in its own L2.
+constexpr int kPM = 256, kPN = 256;           // workgroup tile
+constexpr int kPWavesM = 2, kPWavesN = 4;
+constexpr int kPMF = kPM / kPWavesM / 16;     // 8 MFMA tiles down
+constexpr int kPNF = kPN / kPWavesN / 16;     // 4 MFMA tiles across
+constexpr int kPThreads = 64 * kPWavesM * kPWavesN;
+constexpr int kGroupM = 4;
+
+template <bool PER_TENSOR>
+__global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
+    const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
+    const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
+    uint16_t* __restrict__ out, int64_t ld_out, int M, int N, int KB, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds0[kPM * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds1[kPM * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t b_lds0[kPN * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t b_lds1[kPN * 128];
+  __shared__ __attribute__((aligned(16))) float sa_lds0[kPM];
+  __shared__ __attribute__((aligned(16))) float sa_lds1[kPM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kPWavesN;
+  const int wn = wave % kPWavesN;
+  const int r16 = lane & 15;
+  const int kg = lane >> 4;
+
+  // workgroup id -> tile: XCD-contiguous ranges, then grouped row-major
+  const int tiles = tiles_m * tiles_n;
+  int lin = blockIdx.x;
+  if (tiles % 8 == 0) lin = (lin % 8) * (tiles / 8) + lin / 8;
+  const int group = lin / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int tm = first_m + (lin % (kGroupM * tiles_n)) % gsize;
+  const int tn = (lin % (kGroupM * tiles_n)) / gsize;
+  const int64_t m0 = (int64_t)tm * kPM;
+  const int64_t n0 = (int64_t)tn * kPN;
+
+  // copy assignment: instruction j covers tile rows 8 j .. 8 j + 7; slot
+  // (row, stored chunk lane & 7) holds source chunk (lane & 7) ^ (row & 7)
+  const int crow = lane >> 3;
+  const int cchunk = (lane & 7) ^ (crow & 7);
+  constexpr int kCopies = kPM / 8 / (kPThreads / 64);       // per wave per operand
+  const uint8_t* asrc[kCopies];
+  const uint8_t* bsrc[kCopies];
+#pragma unroll
+  for (int t = 0; t < kCopies; ++t) {
+    const int j = wave + t * (kPThreads / 64);
+    const int64_t ra = min<int64_t>(m0 + 8 * j + crow, (int64_t)M - 1);
+    const int64_t rb = min<int64_t>(n0 + 8 * j + crow, (int64_t)N - 1);
+    asrc[t] = a + ra * ld_a + cchunk * 16;
+    bsrc[t] = w + rb * ld_w + cchunk * 16;
+  }
+  auto issue = [&](int kb, uint8_t* adst, uint8_t* bdst) {
+    const int64_t off = (int64_t)kb * 128;
+#pragma unroll
+    for (int t = 0; t < kCopies; ++t) {
+      const int j = wave + t * (kPThreads / 64);
+      __builtin_amdgcn_global_load_lds((const void*)(asrc[t] + off),
+                                       (__attribute__((address_space(3))) void*)(adst + j * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[t] + off),
+                                       (__attribute__((address_space(3))) void*)(bdst + j * 1024),
+                                       16, 0, 0);
+    }
+  };
+  // activation scale of tile row tid (threads 0 .. BM-1), 0 past M
+  const bool sa_thread = !PER_TENSOR && tid < kPM;
+  const float* sa_row = sa + min<int64_t>(m0 + tid, (int64_t)M - 1) * ld_sa;
+  const bool sa_valid = m0 + tid < M;
+  auto load_sa = [&](int kb) { return sa_valid ? sa_row[kb] : 0.f; };
+
+  // fragment read offsets within a tile: row r16 of a 16-row group, chunks
+  // 2 kg and 2 kg + 1 (the group base is a multiple of 16, so row & 7 = r16 & 7)
+  const int rd0 = r16 * 128 + (((2 * kg) ^ (r16 & 7)) * 16);
+  const int rd1 = r16 * 128 + (((2 * kg + 1) ^ (r16 & 7)) * 16);
+  auto frag = [&](const uint8_t* base) {
+    const uint4 x = *reinterpret_cast<const uint4*>(base + rd0);
+    const uint4 y = *reinterpret_cast<const uint4*>(base + rd1);
+    v8i r;
+    r[0] = (int)x.x; r[1] = (int)x.y; r[2] = (int)x.z; r[3] = (int)x.w;
+    r[4] = (int)y.x; r[5] = (int)y.y; r[6] = (int)y.z; r[7] = (int)y.w;
+    return r;
+  };
+
+  const int nb = min((int)((n0 + wn * (kPN / kPWavesN)) >> 7), N / 128 - 1);
+  v4f acc[kPMF][kPNF];
+#pragma unroll
+  for (int i = 0; i < kPMF; ++i)
+#pragma unroll
+    for (int j = 0; j < kPNF; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // One K block: wait for its copy, publish its scales, then queue the next
+  // block into the other stage and multiply this one.  The two stages are
+  // distinct LDS arrays named statically in each call, so the compiler can
+  // tell the fragment reads of this stage from the copy into the other one
+  // and does not wait for that copy before reading.
+  float sa_next = 0.f;
+  auto step = [&](int kb, const uint8_t* a_cur, const uint8_t* b_cur, float* sa_cur,
+                  uint8_t* a_nxt, uint8_t* b_nxt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (sa_thread) sa_cur[tid] = sa_next;
+    __syncthreads();                 // block kb is in LDS; block kb - 1 is consumed
+    if (kb + 1 < KB) {
+      issue(kb + 1, a_nxt, b_nxt);
+      if (sa_thread) sa_next = load_sa(kb + 1);
+    }
+    const uint8_t* at = a_cur + (wm * (kPM / kPWavesM)) * 128;
+    const uint8_t* bt = b_cur + (wn * (kPN / kPWavesN)) * 128;
+    v8i fb[kPNF];
+#pragma unroll
+    for (int j = 0; j < kPNF; ++j) fb[j] = frag(bt + j * 16 * 128);
+    const float s_w = PER_TENSOR ? 0.f : sw[(int64_t)nb * ld_sw + kb];
+#pragma unroll
+    for (int i = 0; i < kPMF; ++i) {
+      const v8i fa = frag(at + i * 16 * 128);
+      if (PER_TENSOR) {
+#pragma unroll
+        for (int j = 0; j < kPNF; ++j) acc[i][j] = mfma_fp8(fa, fb[j], acc[i][j]);
+      } else {
+        const float4 s4 = *reinterpret_cast<const float4*>(
+            &sa_cur[wm * (kPM / kPWavesM) + i * 16 + 4 * kg]);
+        const float sc[4] = {s4.x * s_w, s4.y * s_w, s4.z * s_w, s4.w * s_w};
+#pragma unroll
+        for (int j = 0; j < kPNF; ++j) {
+          const v4f p = mfma_fp8(fa, fb[j], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(sc[r], p[r], acc[i][j][r]);
+        }
+      }
+    }
+  };
+
+  issue(0, a_lds0, b_lds0);
+  if (sa_thread) sa_next = load_sa(0);
+  for (int kb = 0; kb < KB; kb += 2) {
+    step(kb, a_lds0, b_lds0, sa_lds0, a_lds1, b_lds1);
+    if (kb + 1 < KB) step(kb + 1, a_lds1, b_lds1, sa_lds1, a_lds0, b_lds0);   // KB is uniform
+  }
+
+  const float st = PER_TENSOR ? sa[0] * sw[0] : 1.0f;
+#pragma unroll
+  for (int i = 0; i < kPMF; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t gm = m0 + wm * (kPM / kPWavesM) + i * 16 + 4 * kg + r;
+      if (gm < M) {
+#pragma unroll
+        for (int j = 0; j < kPNF; ++j) {
+          const int64_t gn = n0 + wn * (kPN / kPWavesN) + j * 16 + r16;
+          float v = acc[i][j][r];
+          if (PER_TENSOR) v *= st;
+          if (gn < N) out[gm * ld_out + gn] = (uint16_t)f32_to_bf16_rne(v);
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
@@ -351,6 +532,20 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
     else
       hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, KBW, false>), grid, dim3(64 * KSPLIT), lds, st,
                          a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
+    return hipGetLastError();
+  }
+  if (M > 64) {
+    const int tiles_m = (int)((M + kPM - 1) / kPM);
+    const int tiles_n = (int)((N + kPN - 1) / kPN);
+    dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n);
+    if (per_tensor)
+      hipLaunchKernelGGL(gemm_prefill_kernel<true>, grid, dim3(kPThreads), 0, st, a, ld_a, sa,
+                         ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, (int)N, KB, tiles_m,
+                         tiles_n);
+    else
+      hipLaunchKernelGGL(gemm_prefill_kernel<false>, grid, dim3(kPThreads), 0, st, a, ld_a, sa,
+                         ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, (int)N, KB, tiles_m,
+                         tiles_n);
     return hipGetLastError();
   }
   const int tiles_m = (int)((M + kBM - 1) / kBM);
