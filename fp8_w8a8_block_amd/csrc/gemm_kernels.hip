@@ -46,6 +46,14 @@ __device__ __forceinline__ v8i load32(const uint8_t* p) {
   return r;
 }
 
+// LDS swizzle of 128-byte operand rows: the 16-byte chunk c of row r is
+// stored at chunk position c ^ swz(r).  A fragment read touches 16 rows at
+// one logical chunk per ds_read_b128; with this swizzle the 16 rows land on
+// 16 distinct 16-byte bank groups of a 256-byte bank row, and any 8
+// consecutive rows on 8 distinct groups of a 128-byte bank row, so the read
+// is conflict free whether the LDS serves it 16 or 8 lanes at a time.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
 __device__ __forceinline__ v8i zero8() {
   v8i r;
 #pragma unroll
@@ -64,9 +72,8 @@ __device__ __forceinline__ v8i zero8() {
 // lane-linear, so every load instruction covers eight whole 128-byte rows.
 // (Loading the MFMA layout straight from memory makes each instruction
 // touch 16 rows x 64 bytes, which streams far below the HBM rate.)  Within
-// a row the eight 16-byte chunks are stored XOR-swizzled by (row & 7), so
-// the fragment reads -- 16 rows at one column per ds_read_b128 phase -- hit
-// distinct banks.  While the MFMAs of batch b run, the loads of batch b+1
+// a row the eight 16-byte chunks are stored XOR-swizzled by swz(row), so the
+// fragment reads hit distinct banks.  While the MFMAs of batch b run, the loads of batch b+1
 // are in flight.  Activation rows >= M repeat row M - 1 in LDS and are
 // zeroed in registers.  The waves' 16x16 partial sums are reduced in LDS.
 //
@@ -98,17 +105,18 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
   float* red = reinterpret_cast<float*>(lds + (size_t)KSPLIT * KBW * 2 * kFrag);
   float* s_as = red + KSPLIT * 4 * 64;
 
-  // load slot s = 64 j + lane holds row s / 8, stored chunk s % 8, which is
-  // source chunk (s % 8) ^ (row & 7); rows 8..15 have the same (row & 7).
+  // load slot s = 64 j + lane holds row s / 8 at stored chunk s % 8, which is
+  // source chunk (s % 8) ^ swz(row)
   const int drow = lane >> 3;
-  const int dchunk = (lane & 7) ^ (drow & 7);
-  const uint8_t* wsrc0 = w + (n0 + drow) * ld_w + dchunk * 16;
-  const uint8_t* wsrc1 = w + (n0 + 8 + drow) * ld_w + dchunk * 16;
-  const uint8_t* asrc0 = a + (int64_t)min(drow, M - 1) * ld_a + dchunk * 16;
-  const uint8_t* asrc1 = a + (int64_t)min(8 + drow, M - 1) * ld_a + dchunk * 16;
+  const int dchunk0 = (lane & 7) ^ swz(drow);
+  const int dchunk1 = (lane & 7) ^ swz(8 + drow);
+  const uint8_t* wsrc0 = w + (n0 + drow) * ld_w + dchunk0 * 16;
+  const uint8_t* wsrc1 = w + (n0 + 8 + drow) * ld_w + dchunk1 * 16;
+  const uint8_t* asrc0 = a + (int64_t)min(drow, M - 1) * ld_a + dchunk0 * 16;
+  const uint8_t* asrc1 = a + (int64_t)min(8 + drow, M - 1) * ld_a + dchunk1 * 16;
   // fragment reads: row r16, source chunks 2 kg and 2 kg + 1
-  const int rd0 = r16 * 128 + (((2 * kg) ^ (r16 & 7)) * 16);
-  const int rd1 = r16 * 128 + (((2 * kg + 1) ^ (r16 & 7)) * 16);
+  const int rd0 = r16 * 128 + (((2 * kg) ^ swz(r16)) * 16);
+  const int rd1 = r16 * 128 + (((2 * kg + 1) ^ swz(r16)) * 16);
 
   const int per = (KB + KSPLIT - 1) / KSPLIT;
   const int kb_lo = wave * per;
@@ -329,32 +337,63 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Prefill shape (large M): MFMA-bound.  Workgroup tile BM x BN (256 x 256),
-// eight waves in a 2 x 4 grid, each computing 128 x 64 = 8 x 4 MFMA tiles
-// into 128 fp32 accumulators.  One K step is one 128-wide scale block.
+// Prefill shape (large M): MFMA-bound.  Workgroup tile 256 (M) x 256 (N),
+// eight waves in a 2 x 4 grid, each computing 128 x 64 outputs.  One K step
+// is one 128-wide scale block.
 //
-// Both operand tiles of a K block (BM and BN rows of 128 bytes) are copied
-// into LDS by global_load_lds_dwordx4, lane-linear (one instruction = eight
-// whole rows) with the chunks of a row XOR-swizzled by (row & 7), so the
-// fragment reads are bank-conflict free.  LDS holds two stages: the copy of
-// block kb + 1 is in flight while block kb is multiplied.  The activation
-// scales of block kb + 1 travel through registers into a small LDS array.
-// Per K block each wave reads its 8 A and 4 B fragments from LDS, issues
-// 32 MFMAs into fresh fp32 partials and folds them into the accumulators
-// with (sa[m, kb] * sw[n / 128, kb]); per-tensor scales accumulate in the
-// matrix unit and scale once at the end.
+// The matrix unit computes the transposed tile: its first operand is a
+// 16-row weight fragment, its second a 16-row activation fragment, so lane
+// l holds output column (token row) m = l % 16 and four consecutive weight
+// rows n = 4 (l / 16) + r.  Each lane then needs a single activation scale
+// per 16-row activation fragment (the weight scale is uniform: a wave's 64
+// columns lie in one 128-row weight block), and its four outputs are four
+// adjacent bf16 values of one output row, written with one 8-byte store.
 //
-// Rows past M (and columns past N in a half-filled last tile) read the
-// last valid row and are never stored.  Tiles are visited in groups of
-// kGroupM tile-rows, and consecutive workgroup ids -- which the dispatcher
-// spreads over the 8 XCDs -- are remapped so that each XCD works on a
-// compact block of tiles and shares their A and B panels in its own L2.
+// Both operand tiles of a K block (256 rows of 128 bytes each) are copied
+// into LDS by buffer_load_dwordx4 ... lds, lane-linear (one instruction =
+// eight whole rows) with the chunks of a row XOR-swizzled by swz(row).  The
+// buffer descriptors start at the tile's first row and K block and end at
+// the operand's last row: rows past M (or past N in a half-filled last
+// tile) fall outside, read as zero and are never stored.  LDS holds two
+// stages: the copy of block kb + 1 is in flight while block kb is
+// multiplied.  The activation scales of block kb + 1 travel through
+// registers into LDS, multiplied by the two weight-block scales of the
+// tile and laid out so that a lane's eight scales are 32 contiguous bytes.
+// Per K block a wave holds its 4 weight fragments and streams its 8
+// activation fragments, software-pipelined: the 4 MFMAs of fragment i run
+// in the matrix pipe while the VALU folds the partials of fragment i - 1
+// into the accumulators with sa[m, kb] * sw[n / 128, kb].  Per-tensor
+// scales accumulate in the matrix unit and scale once at the end.
+//
+// Tiles are visited in groups of kGroupM tile-rows, and consecutive
+// workgroup ids -- which the dispatcher spreads over the 8 XCDs -- are
+// remapped so that each XCD works on a compact block of tiles and shares
+// their A and B panels in its own L2.
 constexpr int kPM = 256, kPN = 256;           // workgroup tile
 constexpr int kPWavesM = 2, kPWavesN = 4;
-constexpr int kPMF = kPM / kPWavesM / 16;     // 8 MFMA tiles down
-constexpr int kPNF = kPN / kPWavesN / 16;     // 4 MFMA tiles across
+constexpr int kPWM = kPM / kPWavesM;          // 128 token rows per wave
+constexpr int kPWN = kPN / kPWavesN;          // 64 weight rows per wave
+constexpr int kPMF = kPWM / 16;               // 8 activation fragments
+constexpr int kPNF = kPWN / 16;               // 4 weight fragments
 constexpr int kPThreads = 64 * kPWavesM * kPWavesN;
+constexpr int kPWaves = kPThreads / 64;
+constexpr int kCopies = kPM / 8 / kPWaves;   // copy instructions per wave per operand
 constexpr int kGroupM = 4;
+constexpr int64_t kPrefillMaxLd = ((int64_t)1 << 31) / kPM;   // 32-bit buffer offsets
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;             // raw byte buffer, gfx9
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,
+                                           (int)kRawBufferWord3);
+}
+
+// position of the scale of tile row t (weight block blk) in the staged array:
+// [blk][wave row wm][row within fragment j][fragment mf]
+__device__ __forceinline__ int sc_index(int blk, int t) {
+  const int wm = t / kPWM, mf = (t % kPWM) / 16, j = t % 16;
+  return ((blk * kPWavesM + wm) * 16 + j) * kPMF + mf;
+}
 
 template <bool PER_TENSOR>
 __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
@@ -365,8 +404,8 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t a_lds1[kPM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t b_lds0[kPN * 128];
   __shared__ __attribute__((aligned(16))) uint8_t b_lds1[kPN * 128];
-  __shared__ __attribute__((aligned(16))) float sa_lds0[kPM];
-  __shared__ __attribute__((aligned(16))) float sa_lds1[kPM];
+  __shared__ __attribute__((aligned(16))) float sc_lds0[2 * kPM];
+  __shared__ __attribute__((aligned(16))) float sc_lds1[2 * kPM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -388,44 +427,45 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
   const int64_t m0 = (int64_t)tm * kPM;
   const int64_t n0 = (int64_t)tn * kPN;
 
-  // copy assignment: instruction j covers tile rows 8 j .. 8 j + 7; slot
-  // (row, stored chunk lane & 7) holds source chunk (lane & 7) ^ (row & 7)
+  // copy assignment: instruction t of this wave covers tile rows 8 j .. 8 j + 7
+  // with j = wave + 8 t; slot (row, stored chunk lane & 7) holds source chunk
+  // (lane & 7) ^ swz(row), and row & 15 = 8 (j & 1) + crow with j & 1 = wave & 1
   const int crow = lane >> 3;
-  const int cchunk = (lane & 7) ^ (crow & 7);
-  constexpr int kCopies = kPM / 8 / (kPThreads / 64);       // per wave per operand
-  const uint8_t* asrc[kCopies];
-  const uint8_t* bsrc[kCopies];
-#pragma unroll
-  for (int t = 0; t < kCopies; ++t) {
-    const int j = wave + t * (kPThreads / 64);
-    const int64_t ra = min<int64_t>(m0 + 8 * j + crow, (int64_t)M - 1);
-    const int64_t rb = min<int64_t>(n0 + 8 * j + crow, (int64_t)N - 1);
-    asrc[t] = a + ra * ld_a + cchunk * 16;
-    bsrc[t] = w + rb * ld_w + cchunk * 16;
-  }
+  const int cchunk = (lane & 7) ^ swz(8 * (wave & 1) + crow);
+  const uint8_t* a_tile = a + m0 * ld_a;
+  const uint8_t* w_tile = w + n0 * ld_w;
+  const int64_t a_bytes = ((int64_t)M - m0) * ld_a;
+  const int64_t w_bytes = ((int64_t)N - n0) * ld_w;
   auto issue = [&](int kb, uint8_t* adst, uint8_t* bdst) {
-    const int64_t off = (int64_t)kb * 128;
+    const int64_t koff = (int64_t)kb * 128;
+    const __amdgpu_buffer_rsrc_t ra = raw_buffer(a_tile + koff, a_bytes - koff);
+    const __amdgpu_buffer_rsrc_t rb = raw_buffer(w_tile + koff, w_bytes - koff);
 #pragma unroll
     for (int t = 0; t < kCopies; ++t) {
-      const int j = wave + t * (kPThreads / 64);
-      __builtin_amdgcn_global_load_lds((const void*)(asrc[t] + off),
-                                       (__attribute__((address_space(3))) void*)(adst + j * 1024),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[t] + off),
-                                       (__attribute__((address_space(3))) void*)(bdst + j * 1024),
-                                       16, 0, 0);
+      const int j = wave + t * kPWaves;
+      const int row = 8 * j + crow;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(adst + j * 1024), 16,
+          (int)(row * ld_a + cchunk * 16), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) void*)(bdst + j * 1024), 16,
+          (int)(row * ld_w + cchunk * 16), 0, 0, 0);
     }
   };
-  // activation scale of tile row tid (threads 0 .. BM-1), 0 past M
+  // activation scale of tile row tid (threads 0 .. 255), 0 past M
   const bool sa_thread = !PER_TENSOR && tid < kPM;
   const float* sa_row = sa + min<int64_t>(m0 + tid, (int64_t)M - 1) * ld_sa;
   const bool sa_valid = m0 + tid < M;
+  const int nb0 = (int)(n0 >> 7);
+  const int nb1 = min(nb0 + 1, N / 128 - 1);
+  const int sc_w0 = sc_index(0, tid & (kPM - 1));
+  const int sc_w1 = sc_index(1, tid & (kPM - 1));
   auto load_sa = [&](int kb) { return sa_valid ? sa_row[kb] : 0.f; };
 
-  // fragment read offsets within a tile: row r16 of a 16-row group, chunks
-  // 2 kg and 2 kg + 1 (the group base is a multiple of 16, so row & 7 = r16 & 7)
-  const int rd0 = r16 * 128 + (((2 * kg) ^ (r16 & 7)) * 16);
-  const int rd1 = r16 * 128 + (((2 * kg + 1) ^ (r16 & 7)) * 16);
+  // fragment read offsets within a 16-row group: row r16, chunks 2 kg and
+  // 2 kg + 1 (group bases are multiples of 16, so swz(row) = swz(r16))
+  const int rd0 = r16 * 128 + (((2 * kg) ^ swz(r16)) * 16);
+  const int rd1 = r16 * 128 + (((2 * kg + 1) ^ swz(r16)) * 16);
   auto frag = [&](const uint8_t* base) {
     const uint4 x = *reinterpret_cast<const uint4*>(base + rd0);
     const uint4 y = *reinterpret_cast<const uint4*>(base + rd1);
@@ -434,13 +474,15 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
     r[4] = (int)y.x; r[5] = (int)y.y; r[6] = (int)y.z; r[7] = (int)y.w;
     return r;
   };
+  // this lane's eight scales: weight block of the wave's columns, its token row
+  const int sc_rd = (((wn * kPWN) >> 7) * kPWavesM + wm) * 16 * kPMF + r16 * kPMF;
 
-  const int nb = min((int)((n0 + wn * (kPN / kPWavesN)) >> 7), N / 128 - 1);
-  v4f acc[kPMF][kPNF];
+  // acc[nf][mf]: weight rows 16 nf + 4 kg + r, token row 16 mf + r16
+  v4f acc[kPNF][kPMF];
 #pragma unroll
-  for (int i = 0; i < kPMF; ++i)
+  for (int i = 0; i < kPNF; ++i)
 #pragma unroll
-    for (int j = 0; j < kPNF; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kPMF; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // One K block: wait for its copy, publish its scales, then queue the next
   // block into the other stage and multiply this one.  The two stages are
@@ -448,61 +490,86 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
   // tell the fragment reads of this stage from the copy into the other one
   // and does not wait for that copy before reading.
   float sa_next = 0.f;
-  auto step = [&](int kb, const uint8_t* a_cur, const uint8_t* b_cur, float* sa_cur,
+  auto step = [&](int kb, const uint8_t* a_cur, const uint8_t* b_cur, float* sc_cur,
                   uint8_t* a_nxt, uint8_t* b_nxt) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (sa_thread) sa_cur[tid] = sa_next;
+    if (sa_thread) {
+      sc_cur[sc_w0] = sa_next * sw[(int64_t)nb0 * ld_sw + kb];
+      sc_cur[sc_w1] = sa_next * sw[(int64_t)nb1 * ld_sw + kb];
+    }
     __syncthreads();                 // block kb is in LDS; block kb - 1 is consumed
     if (kb + 1 < KB) {
       issue(kb + 1, a_nxt, b_nxt);
       if (sa_thread) sa_next = load_sa(kb + 1);
     }
-    const uint8_t* at = a_cur + (wm * (kPM / kPWavesM)) * 128;
-    const uint8_t* bt = b_cur + (wn * (kPN / kPWavesN)) * 128;
-    v8i fb[kPNF];
+    const uint8_t* at = a_cur + (wm * kPWM) * 128;
+    const uint8_t* bt = b_cur + (wn * kPWN) * 128;
+    v8i fw[kPNF];
 #pragma unroll
-    for (int j = 0; j < kPNF; ++j) fb[j] = frag(bt + j * 16 * 128);
-    const float s_w = PER_TENSOR ? 0.f : sw[(int64_t)nb * ld_sw + kb];
+    for (int i = 0; i < kPNF; ++i) fw[i] = frag(bt + i * 16 * 128);
+    if (PER_TENSOR) {
+      v8i fa = frag(at);
 #pragma unroll
-    for (int i = 0; i < kPMF; ++i) {
-      const v8i fa = frag(at + i * 16 * 128);
-      if (PER_TENSOR) {
+      for (int j = 0; j < kPMF; ++j) {
+        const v8i fa_next = j + 1 < kPMF ? frag(at + (j + 1) * 16 * 128) : fa;
 #pragma unroll
-        for (int j = 0; j < kPNF; ++j) acc[i][j] = mfma_fp8(fa, fb[j], acc[i][j]);
-      } else {
-        const float4 s4 = *reinterpret_cast<const float4*>(
-            &sa_cur[wm * (kPM / kPWavesM) + i * 16 + 4 * kg]);
-        const float sc[4] = {s4.x * s_w, s4.y * s_w, s4.z * s_w, s4.w * s_w};
-#pragma unroll
-        for (int j = 0; j < kPNF; ++j) {
-          const v4f p = mfma_fp8(fa, fb[j], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(sc[r], p[r], acc[i][j][r]);
-        }
+        for (int i = 0; i < kPNF; ++i) acc[i][j] = mfma_fp8(fw[i], fa, acc[i][j]);
+        fa = fa_next;
       }
+    } else {
+      const float4 s_lo = *reinterpret_cast<const float4*>(sc_cur + sc_rd);
+      const float4 s_hi = *reinterpret_cast<const float4*>(sc_cur + sc_rd + 4);
+      const float sc[kPMF] = {s_lo.x, s_lo.y, s_lo.z, s_lo.w, s_hi.x, s_hi.y, s_hi.z, s_hi.w};
+      v8i fa = frag(at);
+      v4f pp[kPNF];
+#pragma unroll
+      for (int j = 0; j < kPMF; ++j) {
+        const v8i fa_next = j + 1 < kPMF ? frag(at + (j + 1) * 16 * 128) : fa;
+        v4f pc[kPNF];
+#pragma unroll
+        for (int i = 0; i < kPNF; ++i) pc[i] = mfma_fp8(fw[i], fa, v4f{0.f, 0.f, 0.f, 0.f});
+        if (j > 0) {
+#pragma unroll
+          for (int i = 0; i < kPNF; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[i][j - 1][r] = __builtin_fmaf(sc[j - 1], pp[i][r], acc[i][j - 1][r]);
+        }
+#pragma unroll
+        for (int i = 0; i < kPNF; ++i) pp[i] = pc[i];
+        fa = fa_next;
+      }
+#pragma unroll
+      for (int i = 0; i < kPNF; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[i][kPMF - 1][r] = __builtin_fmaf(sc[kPMF - 1], pp[i][r], acc[i][kPMF - 1][r]);
     }
   };
 
   issue(0, a_lds0, b_lds0);
   if (sa_thread) sa_next = load_sa(0);
   for (int kb = 0; kb < KB; kb += 2) {
-    step(kb, a_lds0, b_lds0, sa_lds0, a_lds1, b_lds1);
-    if (kb + 1 < KB) step(kb + 1, a_lds1, b_lds1, sa_lds1, a_lds0, b_lds0);   // KB is uniform
+    step(kb, a_lds0, b_lds0, sc_lds0, a_lds1, b_lds1);
+    if (kb + 1 < KB) step(kb + 1, a_lds1, b_lds1, sc_lds1, a_lds0, b_lds0);   // KB is uniform
   }
 
+  // epilogue: lane writes 4 adjacent bf16 of token row m per weight fragment
   const float st = PER_TENSOR ? sa[0] * sw[0] : 1.0f;
 #pragma unroll
-  for (int i = 0; i < kPMF; ++i) {
+  for (int j = 0; j < kPMF; ++j) {
+    const int64_t gm = m0 + wm * kPWM + j * 16 + r16;
+    if (gm < M) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t gm = m0 + wm * (kPM / kPWavesM) + i * 16 + 4 * kg + r;
-      if (gm < M) {
+      for (int i = 0; i < kPNF; ++i) {
+        const int64_t gn = n0 + wn * kPWN + i * 16 + 4 * kg;
+        if (gn < N) {
+          float v[4];
 #pragma unroll
-        for (int j = 0; j < kPNF; ++j) {
-          const int64_t gn = n0 + wn * (kPN / kPWavesN) + j * 16 + r16;
-          float v = acc[i][j][r];
-          if (PER_TENSOR) v *= st;
-          if (gn < N) out[gm * ld_out + gn] = (uint16_t)f32_to_bf16_rne(v);
+          for (int r = 0; r < 4; ++r) v[r] = PER_TENSOR ? acc[i][j][r] * st : acc[i][j][r];
+          const uint2 packed = make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                          f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+          *reinterpret_cast<uint2*>(out + gm * ld_out + gn) = packed;
         }
       }
     }
@@ -534,7 +601,7 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
                          a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
     return hipGetLastError();
   }
-  if (M > 64) {
+  if (M > 64 && ld_a < kPrefillMaxLd && ld_w < kPrefillMaxLd) {
     const int tiles_m = (int)((M + kPM - 1) / kPM);
     const int tiles_n = (int)((N + kPN - 1) / kPN);
     dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n);
