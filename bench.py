@@ -35,6 +35,36 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 N_WCOPIES = 8
+CALIB_COPY_BYTES = 256 << 20   # plain device copy whose counters calibrate FETCH/WRITE_SIZE
+KERNEL_SOURCES = ("fp8_w8a8_block_amd/csrc/gemm_kernels.hip",
+                  "fp8_w8a8_block_amd/csrc/device_common.h")
+TRAFFIC_FILE = os.path.join("profiles", "traffic.json")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def dominant_kernel(workload, decode):
+    return "gemm_decode_kernel" if decode or workload == "tiny" else "gemm_prefill_kernel"
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def quant_bytes(M, K):
@@ -62,6 +92,8 @@ def parse():
                    choices=["decode", "prefill", "mlp_down", "mlp_down_tensor", "large", "tiny"])
     p.add_argument("--cpu-baseline-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="skip the secondary prefill measurement of the decode run")
     return p.parse_args()
 
 
@@ -157,6 +189,34 @@ def time_gemm_launches(wl, n_launches):
     return float(ms), n_launches
 
 
+def calibration_copy():
+    """One plain device-to-device copy of known size; under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE give the scale factor for the kernels' counters."""
+    import torch
+    src = torch.empty(CALIB_COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def secondary_prefill(steps=20):
+    """GEMM-only TFLOP/s of the 4096^3 prefill shape, as context in the decode line."""
+    import torch
+    wl = Workload("prefill")
+    for s in range(3):
+        wl.step(s)
+    torch.cuda.synchronize()
+    ms, n = time_gemm_launches(wl, steps)
+    tf = wl.flops_per_step() / (ms * 1e-3) / 1e12
+    del wl
+    torch.cuda.empty_cache()
+    return {"workload": "prefill M=N=K=4096", "kernel": "gemm_prefill_kernel",
+            "gemm_us": ms * 1e3, "TFLOP/s": tf, "frac_of_5000": tf / FP8_PEAK_TFLOPS}
+
+
 def cpu_baseline(wl, target_s):
     """Oracle timed on the host on a bounded sample of the same step."""
     from oracle import gemm, quant
@@ -213,6 +273,7 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    calibration_copy()
     wl = Workload(args.workload)
     decode = len(wl.Ms) > 1
 
@@ -246,6 +307,7 @@ def main():
 
     total_b, q_b, g_b = wl.bytes_per_step()
     flops = wl.flops_per_step()
+    Ms, N_, K_, mode, ncopy = wl.Ms, wl.N, wl.K, wl.mode, wl.ncopy
 
     n_l = 96 if decode else 24
     g_ms_mean, n_l = time_gemm_launches(wl, n_l)
@@ -263,22 +325,27 @@ def main():
         roof = {"bound": "mfma", "achieved": flops_per_launch / (g_ms_mean * 1e-3) / 1e12,
                 "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = "gemm_decode_kernel" if decode else "gemm_tile_kernel"
+    roof["traffic"] = measured_traffic(args.workload)
+    roof["kernel"] = dominant_kernel(args.workload, decode)
     roof["avg_launch_us"] = g_ms_mean * 1e3
     roof["launches_timed"] = n_l
     roof["algorithmic_bytes_per_launch" if decode else "flop_per_launch"] = (
         gemm_bytes_per_launch if decode else flops_per_launch)
+    roof["kernel_source_hash"] = kernel_source_hash()
 
     cpu = None
     if args.cpu_baseline_seconds > 0:
         cpu = cpu_baseline(wl, args.cpu_baseline_seconds)
+    secondary = None
+    if decode and not args.no_secondary:
+        del wl
+        torch.cuda.empty_cache()
+        secondary = secondary_prefill()
 
-    c = wl.cfg
-    config = {"workload": args.workload, "M": wl.Ms if decode else wl.Ms[0], "N": wl.N, "K": wl.K,
-              "scales": "per-tensor" if wl.mode == "tensor" else "A 1x128, W 128x128",
+    config = {"workload": args.workload, "M": Ms if decode else Ms[0], "N": N_, "K": K_,
+              "scales": "per-tensor" if mode == "tensor" else "A 1x128, W 128x128",
               "step": "quant_act + block_gemm" + (" for each M" if decode else ""),
-              "weight_copies": wl.ncopy}
+              "weight_copies": ncopy}
     line = {
         "metric": ("FP8 block-scaled GEMM TFLOPS (prefill) & GB/s (decode) as % of MI355X "
                    "roofline"),
@@ -299,6 +366,7 @@ def main():
         "step_bytes": {"total": total_b, "quant_act": q_b, "gemm": g_b},
         "step_flop": flops,
         "tflops_per_step": flops / (sec / K) / 1e12,
+        "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
 
