@@ -22,6 +22,7 @@ SCALE_TENSOR = 1
 OP_QUANT_ACT = 0
 OP_QUANT_WEIGHT = 1
 OP_GEMM = 2
+OP_LINEAR = 3
 
 _MODES = {"block": SCALE_BLOCK, "tensor": SCALE_TENSOR}
 
@@ -45,6 +46,8 @@ _SIGS = {
     "fp8_validate_block_gemm": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                                        _i64, _i64, _i64, _int]),
     "fp8_e4m3_encode_f32": (_int, [_vp, _i64, _vp, _vp]),
+    "fp8_linear": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp,
+                          _sz, _vp]),
 }
 
 _lib = None
@@ -179,10 +182,32 @@ def block_gemm(a_q, a_s, w_q, w_s, scale_mode="block", out=None):
     return out
 
 
-def linear(x, w_q, w_s, scale_mode="block"):
-    """One W8A8 linear call: dynamic activation quantization, then the GEMM."""
-    a_q, a_s = quant_act(x, scale_mode)
-    return block_gemm(a_q, a_s, w_q, w_s, scale_mode)
+def linear(x, w_q, w_s, scale_mode="block", out=None, workspace=None):
+    """One W8A8 linear call in one library call: out = GEMM(quant_act(x), W).
+
+    Bit-identical to quant_act followed by block_gemm.  Block scales with
+    M <= 16 run fused (no workspace); otherwise a workspace is used (allocated
+    here unless given).
+    """
+    mode = _mode(scale_mode)
+    M, K, ld_x = _rows(x, torch.bfloat16, "x")
+    N, K2, ld_w = _rows(w_q, torch.uint8, "w_q")
+    if K2 != K:
+        raise ValueError(f"K mismatch: x has {K}, w_q has {K2}")
+    if w_s.dtype != torch.float32 or not w_s.is_cuda:
+        raise TypeError("w_s must be a float32 device tensor")
+    with torch.cuda.device(x.device):
+        if out is None:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        ld_out = out.stride(0) if out.shape[0] > 1 else out.shape[1]
+        nws = workspace_bytes(OP_LINEAR, M, N, K, mode)
+        if nws and workspace is None:
+            workspace = torch.empty(nws, dtype=torch.uint8, device=x.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        _check(lib().fp8_linear(x.data_ptr(), ld_x, w_q.data_ptr(), ld_w, w_s.data_ptr(), _ld(w_s),
+                                out.data_ptr(), ld_out, M, N, K, mode, ws_ptr, ws_len, _stream(x)))
+    return out
 
 
 def encode_f32(x):

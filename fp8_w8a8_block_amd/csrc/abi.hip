@@ -102,6 +102,27 @@ fp8_status check_device() {
 
 fp8_status launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH; }
 
+// Workspace of the unfused fp8_linear path: activation codes [M, ld = K
+// rounded up to 16], then the scales (block: [M, K/128]; tensor: one float),
+// then the per-tensor partials.  Every piece starts 256-byte aligned.
+struct LinearLayout {
+  size_t codes, scales, partials, total;
+  int64_t ld_q;
+};
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+LinearLayout linear_layout(int64_t M, int64_t K, int scale_mode) {
+  LinearLayout l;
+  l.ld_q = (K + 15) / 16 * 16;
+  l.codes = 0;
+  l.scales = align256((size_t)M * (size_t)l.ld_q);
+  const size_t nscales = scale_mode == FP8_SCALE_BLOCK ? (size_t)M * (size_t)(K / 128) : 1;
+  l.partials = align256(l.scales + nscales * sizeof(float));
+  l.total = scale_mode == FP8_SCALE_TENSOR
+                ? l.partials + (size_t)fp8k::kTensorPartials * sizeof(uint32_t)
+                : l.partials;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,9 +145,14 @@ const char* fp8_status_str(fp8_status s) {
 }
 
 size_t fp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int scale_mode) {
-  (void)M; (void)N; (void)K;
+  (void)N;
   if ((op == FP8_OP_QUANT_ACT || op == FP8_OP_QUANT_WEIGHT) && scale_mode == FP8_SCALE_TENSOR)
     return (size_t)fp8k::kTensorPartials * sizeof(uint32_t);
+  if (op == FP8_OP_LINEAR) {
+    if (scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, K)) return 0;
+    if (M <= 0 || K <= 0) return 0;
+    return linear_layout(M, K, scale_mode).total;
+  }
   return 0;
 }
 
@@ -197,6 +223,54 @@ fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, in
   if ((st = check_device()) != FP8_OK) return st;
   return launched(fp8k::launch_gemm(a_q, ld_a, a_s, ld_as, w_q, ld_w, w_s, ld_ws, out, ld_out, M,
                                     N, K, scale_mode == FP8_SCALE_TENSOR, (hipStream_t)stream));
+}
+
+fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
+                      const float* w_s, int64_t ld_ws, uint16_t* out, int64_t ld_out,
+                      int64_t M, int64_t N, int64_t K, int scale_mode, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  if (scale_mode != FP8_SCALE_BLOCK && scale_mode != FP8_SCALE_TENSOR) return FP8_ERR_SCHEME;
+  if (M < 0 || M >= kMaxDim || !shape_ok_kn(K) || !shape_ok_kn(N)) return FP8_ERR_SHAPE;
+  if (M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems) return FP8_ERR_SHAPE;
+  if (M == 0) return FP8_OK;
+  if (!x || !w_q || !w_s || !out) return FP8_ERR_NULL;
+  const int64_t KB = K / 128;
+  if (ld_x < K || ld_w < K || ld_out < N) return FP8_ERR_STRIDE;
+  if (scale_mode == FP8_SCALE_BLOCK && ld_ws < KB) return FP8_ERR_STRIDE;
+  if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(out, 16) || !aligned(w_s, 4))
+    return FP8_ERR_ALIGN;
+  if (ld_x % 8 != 0 || ld_w % 16 != 0 || ld_out % 8 != 0) return FP8_ERR_ALIGN;
+  Range ro = range_of(out, M, N, ld_out, 2);
+  Range rx = range_of(x, M, K, ld_x, 2), rw = range_of(w_q, N, K, ld_w, 1);
+  Range rws = scale_mode == FP8_SCALE_BLOCK ? range_of(w_s, N / 128, KB, ld_ws, 4)
+                                            : range_of(w_s, 1, 1, 1, 4);
+  if (overlap(ro, rx) || overlap(ro, rw) || overlap(ro, rws)) return FP8_ERR_ALIAS;
+  const bool fused = scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, K);
+  LinearLayout lay = linear_layout(M, K, scale_mode);
+  if (!fused) {
+    if (!workspace || ws_bytes < lay.total || !aligned(workspace, 16)) return FP8_ERR_WORKSPACE;
+    Range rws2 = {(uintptr_t)workspace, (uintptr_t)workspace + lay.total};
+    if (overlap(rws2, ro) || overlap(rws2, rx) || overlap(rws2, rw) || overlap(rws2, rws))
+      return FP8_ERR_ALIAS;
+  }
+  fp8_status st = check_device();
+  if (st != FP8_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (fused)
+    return launched(fp8k::launch_linear_decode(x, ld_x, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N,
+                                               K, s));
+  uint8_t* ws8 = (uint8_t*)workspace;
+  uint8_t* q = ws8 + lay.codes;
+  float* sa = (float*)(ws8 + lay.scales);
+  hipError_t e;
+  if (scale_mode == FP8_SCALE_BLOCK)
+    e = fp8k::launch_quant_act_block(x, M, K, ld_x, q, lay.ld_q, sa, KB, s);
+  else
+    e = fp8k::launch_quant_tensor(x, M, K, ld_x, q, lay.ld_q, sa, (uint32_t*)(ws8 + lay.partials),
+                                  s);
+  if (e != hipSuccess) return FP8_ERR_LAUNCH;
+  return launched(fp8k::launch_gemm(q, lay.ld_q, sa, KB, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N,
+                                    K, scale_mode == FP8_SCALE_TENSOR, s));
 }
 
 fp8_status fp8_e4m3_encode_f32(const float* x, int64_t n, uint8_t* codes, void* stream) {

@@ -119,6 +119,29 @@ __device__ __forceinline__ uint8_t e4m3_encode_one(float x) {
   return (uint8_t)((w & 0xff) | sign);
 }
 
+// Quantize the 8 bf16 values a lane holds (uint4) with the group divisor;
+// returns the 8 codes as a uint2 (byte i = element i).
+__device__ __forceinline__ uint2 quant8(const uint4 v, const GroupDivisor& d) {
+  uint32_t c0 = e4m3_pack4_mag(quotient_abs(bf16_lo(v.x), d), quotient_abs(bf16_hi(v.x), d),
+                               quotient_abs(bf16_lo(v.y), d), quotient_abs(bf16_hi(v.y), d));
+  uint32_t c1 = e4m3_pack4_mag(quotient_abs(bf16_lo(v.z), d), quotient_abs(bf16_hi(v.z), d),
+                               quotient_abs(bf16_lo(v.w), d), quotient_abs(bf16_hi(v.w), d));
+  c0 |= bf16x4_signs(v.x, v.y);
+  c1 |= bf16x4_signs(v.z, v.w);
+  return make_uint2(c0, c1);
+}
+
+// Largest |x| of 8 bf16 values, as fp32 bits.
+__device__ __forceinline__ uint32_t absmax8_bits(const uint4 v) {
+  uint32_t a = bf16x2_absmax_bits(v.x);
+  uint32_t b = bf16x2_absmax_bits(v.y);
+  uint32_t c = bf16x2_absmax_bits(v.z);
+  uint32_t e = bf16x2_absmax_bits(v.w);
+  a = a > b ? a : b;
+  c = c > e ? c : e;
+  return a > c ? a : c;
+}
+
 // ---- fp32 -> bf16 round to nearest even (finite values) ------------------
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -28,6 +28,14 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 
 // the decode path stages all activation scales of a call in LDS
 constexpr int kDecodeMaxKB = 128;             // K <= 16384
+
+// decode split: waves per workgroup and K blocks per wave batch
+#ifndef FP8_DECODE_KSPLIT
+#define FP8_DECODE_KSPLIT 8
+#endif
+#ifndef FP8_DECODE_KBW
+#define FP8_DECODE_KBW 1
+#endif
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
@@ -436,21 +444,26 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
   const uint8_t* w_tile = w + n0 * ld_w;
   const int64_t a_bytes = ((int64_t)M - m0) * ld_a;
   const int64_t w_bytes = ((int64_t)N - n0) * ld_w;
+  // copy instruction t (0 .. kCopies-1) of both operands for K block kb: tile
+  // rows 8 j + crow with j = wave + 8 t.  The uniform part of the offset
+  // (64 t rows and the K block) goes into the descriptor base, so every copy
+  // uses the same per-lane offset; the descriptor still ends at the last row.
+  const int a_lane_off = (8 * wave + crow) * (int)ld_a + cchunk * 16;
+  const int w_lane_off = (8 * wave + crow) * (int)ld_w + cchunk * 16;
+  auto issue_part = [&](int kb, int t, uint8_t* adst, uint8_t* bdst) {
+    const int j = wave + t * kPWaves;
+    const int64_t a_off = (int64_t)kb * 128 + (int64_t)t * 8 * kPWaves * ld_a;
+    const int64_t w_off = (int64_t)kb * 128 + (int64_t)t * 8 * kPWaves * ld_w;
+    const __amdgpu_buffer_rsrc_t ra = raw_buffer(a_tile + a_off, a_bytes - a_off);
+    const __amdgpu_buffer_rsrc_t rb = raw_buffer(w_tile + w_off, w_bytes - w_off);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        ra, (__attribute__((address_space(3))) void*)(adst + j * 1024), 16, a_lane_off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (__attribute__((address_space(3))) void*)(bdst + j * 1024), 16, w_lane_off, 0, 0, 0);
+  };
   auto issue = [&](int kb, uint8_t* adst, uint8_t* bdst) {
-    const int64_t koff = (int64_t)kb * 128;
-    const __amdgpu_buffer_rsrc_t ra = raw_buffer(a_tile + koff, a_bytes - koff);
-    const __amdgpu_buffer_rsrc_t rb = raw_buffer(w_tile + koff, w_bytes - koff);
 #pragma unroll
-    for (int t = 0; t < kCopies; ++t) {
-      const int j = wave + t * kPWaves;
-      const int row = 8 * j + crow;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(adst + j * 1024), 16,
-          (int)(row * ld_a + cchunk * 16), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (__attribute__((address_space(3))) void*)(bdst + j * 1024), 16,
-          (int)(row * ld_w + cchunk * 16), 0, 0, 0);
-    }
+    for (int t = 0; t < kCopies; ++t) issue_part(kb, t, adst, bdst);
   };
   // activation scale of tile row tid (threads 0 .. 255), 0 past M
   const bool sa_thread = !PER_TENSOR && tid < kPM;
@@ -576,7 +589,163 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused decode linear (M <= 16): the decode GEMM above with the dynamic 1x128
+// activation quantization done inside it, one launch per call.  Each wave
+// quantizes the groups of its own K blocks just in time: the bf16 loads of
+// block kb are issued before its weight copy, so the quantization (VALU)
+// runs while the weight is still streaming.  Quantization uses the same lane
+// layout and device functions as quant_act_block_kernel (16 lanes x 8 values
+// per group, 16-lane DPP max), so the codes and scales are bit-identical to
+// fp8_quant_act's; the MFMA, fold and reduction order equal the decode
+// GEMM's, so the output is bit-identical to quantizing and then calling the
+// GEMM.  Codes land in the wave's LDS A fragment (swizzled like the copies);
+// rows >= M stay zero, as do their scales.
+//
+// Dynamic LDS per wave: W fragment (2 KiB), A fragment (2 KiB), 16 scales;
+// then the reduction buffer (KSPLIT * 1 KiB).
+template <int KSPLIT>
+constexpr size_t linear_decode_lds_bytes() {
+  return (size_t)KSPLIT * (2 * kFrag + 64) + (size_t)KSPLIT * 4 * 64 * sizeof(float);
+}
+
+template <int KSPLIT>
+__global__ __launch_bounds__(64 * KSPLIT) void linear_decode_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, const uint8_t* __restrict__ w, int64_t ld_w,
+    const float* __restrict__ sw, int64_t ld_sw, uint16_t* __restrict__ out, int64_t ld_out,
+    int M, int KB) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;
+  const int kg = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const bool arow = r16 < M;
+
+  uint8_t* wbuf = lds + (size_t)wave * (2 * kFrag + 64);
+  uint8_t* abuf = wbuf + kFrag;
+  float* sbuf = reinterpret_cast<float*>(abuf + kFrag);
+  float* red = reinterpret_cast<float*>(lds + (size_t)KSPLIT * (2 * kFrag + 64));
+
+  // rows >= M of the A fragment and their scales stay zero
+  for (int i = lane; i < kFrag / 16; i += 64)
+    reinterpret_cast<uint4*>(abuf)[i] = make_uint4(0, 0, 0, 0);
+  if (lane < 16) sbuf[lane] = 0.f;
+
+  // weight copy slots and fragment reads as in gemm_decode_kernel
+  const int drow = lane >> 3;
+  const uint8_t* wsrc0 = w + (n0 + drow) * ld_w + ((lane & 7) ^ swz(drow)) * 16;
+  const uint8_t* wsrc1 = w + (n0 + 8 + drow) * ld_w + ((lane & 7) ^ swz(8 + drow)) * 16;
+  const int rd0 = r16 * 128 + (((2 * kg) ^ swz(r16)) * 16);
+  const int rd1 = r16 * 128 + (((2 * kg + 1) ^ swz(r16)) * 16);
+
+  // quantization: pass p covers rows 4 p + (lane >> 4); lane & 15 holds 8
+  // values of the row's 128-group.  Rows past M in a pass read row M - 1 and
+  // are not written.
+  const int q_row = lane >> 4;
+  const int q_l16 = lane & 15;
+  const int npass = (M + 3) >> 2;                     // uniform, 1..4
+
+  const int per = (KB + KSPLIT - 1) / KSPLIT;
+  const int kb_lo = wave * per;
+  const int kb_hi = min(KB, kb_lo + per);
+
+  uint4 xv[4];
+  auto issue = [&](int kb) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (p < npass) {
+        const int m = min(4 * p + q_row, M - 1);
+        xv[p] = *reinterpret_cast<const uint4*>(x + (int64_t)m * ld_x + (int64_t)kb * 128 + q_l16 * 8);
+      }
+    }
+    const int64_t off = (int64_t)kb * 128;
+    __builtin_amdgcn_global_load_lds((const void*)(wsrc0 + off),
+                                     (__attribute__((address_space(3))) void*)wbuf, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(wsrc1 + off),
+                                     (__attribute__((address_space(3))) void*)(wbuf + 1024), 16, 0, 0);
+  };
+  auto frag = [&](const uint8_t* buf) {
+    const uint4 a0 = *reinterpret_cast<const uint4*>(buf + rd0);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(buf + rd1);
+    v8i r;
+    r[0] = (int)a0.x; r[1] = (int)a0.y; r[2] = (int)a0.z; r[3] = (int)a0.w;
+    r[4] = (int)a1.x; r[5] = (int)a1.y; r[6] = (int)a1.z; r[7] = (int)a1.w;
+    return r;
+  };
+
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  if (kb_lo < kb_hi) issue(kb_lo);
+  for (int kb = kb_lo; kb < kb_hi; ++kb) {            // wave-uniform; no barrier inside
+    // the activation loads of block kb went out before its two weight copies
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (p < npass) {
+        const uint32_t amax = row16_max(absmax8_bits(xv[p]));
+        const GroupDivisor d = make_divisor(__uint_as_float(amax));
+        const uint2 c = quant8(xv[p], d);
+        const int m = 4 * p + q_row;
+        if (m < M) {
+          *reinterpret_cast<uint2*>(abuf + m * 128 + (((q_l16 >> 1) ^ swz(m)) * 16) +
+                                    (q_l16 & 1) * 8) = c;
+          if (q_l16 == 0) sbuf[m] = d.s;
+        }
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the weight fragment has landed
+    v8i av = frag(abuf);
+    const v8i bw = frag(wbuf);
+    const float s_w = sw[(int64_t)(n0 >> 7) * ld_sw + kb];
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = sbuf[4 * kg + i] * s_w;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (kb + 1 < kb_hi) issue(kb + 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) av[e] = arow ? av[e] : 0;
+    const v4f p = mfma_fp8(av, bw, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc[i], p[i], acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[(wave * 4 + i) * 64 + lane] = acc[i];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < KSPLIT; ++s2) v += red[(s2 * 4 + i) * 64 + lane];
+      const int m = 4 * kg + i;
+      if (m < M) out[(int64_t)m * ld_out + n0 + r16] = (uint16_t)f32_to_bf16_rne(v);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_linear_decode(const uint16_t* x, int64_t ld_x, const uint8_t* w, int64_t ld_w,
+                                const float* sw, int64_t ld_sw, uint16_t* out, int64_t ld_out,
+                                int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  // the same split as the decode GEMM, so the two paths agree bit for bit
+  constexpr int KSPLIT = FP8_DECODE_KSPLIT;
+  dim3 grid((uint32_t)(N / 16));
+  hipLaunchKernelGGL((linear_decode_kernel<KSPLIT>), grid, dim3(64 * KSPLIT),
+                     linear_decode_lds_bytes<KSPLIT>(), st, x, ld_x, w, ld_w, sw, ld_sw, out,
+                     ld_out, (int)M, (int)(K / 128));
+  return hipGetLastError();
+}
+
+// Above this M the per-wave quantization costs more than the separate
+// quantizer launch it saves (measured on MI355X at N = 11008, K = 4096).
+#ifndef FP8_LINEAR_FUSED_MAX_M
+#define FP8_LINEAR_FUSED_MAX_M 4
+#endif
+
+bool linear_decode_supported(int64_t M, int64_t K) {
+  return M >= 1 && M <= FP8_LINEAR_FUSED_MAX_M && K / 128 <= kDecodeMaxKB;
+}
 
 hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                        const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
@@ -584,12 +753,6 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
                        bool per_tensor, hipStream_t st) {
   const int KB = (int)(K / 128);
   if (M <= 16 && KB <= kDecodeMaxKB) {
-#ifndef FP8_DECODE_KSPLIT
-#define FP8_DECODE_KSPLIT 8
-#endif
-#ifndef FP8_DECODE_KBW
-#define FP8_DECODE_KBW 1
-#endif
     constexpr int KSPLIT = FP8_DECODE_KSPLIT, KBW = FP8_DECODE_KBW;
     dim3 grid((uint32_t)(N / 16));
     const size_t lds = decode_lds_bytes<KSPLIT, KBW>(KB, per_tensor);

@@ -30,4 +30,12 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
                        uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
                        bool per_tensor, hipStream_t st);
 
+// Fused decode linear: dynamic 1x128 quantization of x inside the decode GEMM
+// (block scales).  Supported for 1 <= M <= 16 and K <= 16384; the result is
+// bit-identical to launch_quant_act_block followed by launch_gemm.
+bool linear_decode_supported(int64_t M, int64_t K);
+hipError_t launch_linear_decode(const uint16_t* x, int64_t ld_x, const uint8_t* w, int64_t ld_w,
+                                const float* sw, int64_t ld_sw, uint16_t* out, int64_t ld_out,
+                                int64_t M, int64_t N, int64_t K, hipStream_t st);
+
 }  // namespace fp8k

@@ -18,28 +18,6 @@ namespace fp8k {
 
 namespace {
 
-// Quantize the 8 bf16 values a lane holds (uint4) with the group divisor;
-// returns the 8 codes as a uint2.
-__device__ __forceinline__ uint2 quant8(const uint4 v, const GroupDivisor& d) {
-  uint32_t c0 = e4m3_pack4_mag(quotient_abs(bf16_lo(v.x), d), quotient_abs(bf16_hi(v.x), d),
-                               quotient_abs(bf16_lo(v.y), d), quotient_abs(bf16_hi(v.y), d));
-  uint32_t c1 = e4m3_pack4_mag(quotient_abs(bf16_lo(v.z), d), quotient_abs(bf16_hi(v.z), d),
-                               quotient_abs(bf16_lo(v.w), d), quotient_abs(bf16_hi(v.w), d));
-  c0 |= bf16x4_signs(v.x, v.y);
-  c1 |= bf16x4_signs(v.z, v.w);
-  return make_uint2(c0, c1);
-}
-
-__device__ __forceinline__ uint32_t absmax8_bits(const uint4 v) {
-  uint32_t a = bf16x2_absmax_bits(v.x);
-  uint32_t b = bf16x2_absmax_bits(v.y);
-  uint32_t c = bf16x2_absmax_bits(v.z);
-  uint32_t e = bf16x2_absmax_bits(v.w);
-  a = a > b ? a : b;
-  c = c > e ? c : e;
-  return a > c ? a : c;
-}
-
 // ---------------------------------------------------------------------------
 // 1x128 activation groups.  Block = 256 threads = 16 groups per slot; each
 // thread handles GPT groups (GPT loads in flight).  The grid is one run of

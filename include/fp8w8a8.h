@@ -69,14 +69,15 @@ typedef enum {
 enum { FP8_SCALE_BLOCK = 0, FP8_SCALE_TENSOR = 1 };
 
 /* Operation ids for fp8_workspace_bytes(). */
-enum { FP8_OP_QUANT_ACT = 0, FP8_OP_QUANT_WEIGHT = 1, FP8_OP_GEMM = 2 };
+enum { FP8_OP_QUANT_ACT = 0, FP8_OP_QUANT_WEIGHT = 1, FP8_OP_GEMM = 2, FP8_OP_LINEAR = 3 };
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* fp8_status_str(fp8_status s);
 
 /* Bytes of device workspace a call needs (0 if none).  For op
  * FP8_OP_QUANT_ACT the shape is (M, K); for FP8_OP_QUANT_WEIGHT it is (N, K)
- * passed as (rows = M argument, K); FP8_OP_GEMM needs none. */
+ * passed as (rows = M argument, K); FP8_OP_GEMM needs none; FP8_OP_LINEAR
+ * takes (M, N, K) and needs none on its fused path. */
 size_t fp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int scale_mode);
 
 /* fp8_quant_act -- dynamic activation quantization.
@@ -136,6 +137,25 @@ fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, in
                           const uint8_t* w_q, int64_t ld_w, const float* w_s, int64_t ld_ws,
                           uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
                           int scale_mode, void* workspace, size_t ws_bytes, void* stream);
+
+/* fp8_linear -- one W8A8 linear call: dynamic activation quantization of x
+ * followed by the FP8 GEMM against pre-quantized weights.  The pages describe
+ * the two as one runtime step: activation scales computed per call ("FP8
+ * Quantization" §D.2, and "fp8-serving-slower-than-bf16" on per-step scale
+ * overhead) feeding the FP8 matrix unit ("FP8 and FP4: Throughput Needs
+ * Scaling", kernel-caveat card).
+ *   x [M, K] bf16 (ld_x), w_q / w_s as for fp8_block_gemm, out [M, N] bf16.
+ *   The result is bit-identical to fp8_quant_act (same scale_mode) followed
+ *   by fp8_block_gemm.
+ *   FP8_SCALE_BLOCK with 1 <= M <= 16 and K <= 16384 runs as one fused
+ *   launch (quantization inside the decode GEMM) and needs no workspace.
+ *   Any other call quantizes into the workspace and then multiplies; it
+ *   needs fp8_workspace_bytes(FP8_OP_LINEAR, M, N, K, scale_mode) bytes of
+ *   device memory (16-byte aligned, not initialized, not read afterwards). */
+fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
+                      const float* w_s, int64_t ld_ws, uint16_t* out, int64_t ld_out,
+                      int64_t M, int64_t N, int64_t K, int scale_mode, void* workspace,
+                      size_t ws_bytes, void* stream);
 
 /* Host-only validation: the argument checks of the three calls above, in the
  * same order, without touching any device (no device check, no launch). */

@@ -32,7 +32,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = header_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -49,6 +49,13 @@ def test_workspace_bytes():
     assert _lib.workspace_bytes(_lib.OP_QUANT_ACT, 16, 0, 4096, "tensor") == 4096
     assert _lib.workspace_bytes(_lib.OP_QUANT_WEIGHT, 4096, 0, 4096, "tensor") == 4096
     assert _lib.workspace_bytes(_lib.OP_GEMM, 16, 256, 4096, "tensor") == 0
+    # fused decode linear needs none; other shapes hold codes + scales
+    assert _lib.workspace_bytes(_lib.OP_LINEAR, 4, 11008, 4096, "block") == 0
+    assert _lib.workspace_bytes(_lib.OP_LINEAR, 16, 11008, 4096, "block") >= 16 * 4096
+    assert _lib.workspace_bytes(_lib.OP_LINEAR, 1, 256, 512, "block") == 0
+    n = _lib.workspace_bytes(_lib.OP_LINEAR, 100, 256, 512, "block")
+    assert n >= 100 * 512 + 4 * 100 * 4
+    assert _lib.workspace_bytes(_lib.OP_LINEAR, 4, 256, 512, "tensor") >= 4 * 512 + 4 + 4096
 
 
 def vq(x=X, M=16, K=512, ld_x=None, q=Q, ld_q=None, s=S, ld_s=None, mode=0, ws=None, ws_bytes=0):

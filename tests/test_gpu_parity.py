@@ -398,3 +398,61 @@ def test_gemm_empty_and_errors():
     with pytest.raises(ValueError):
         fp8.quant_weight_block(torch.zeros((256, 512), dtype=torch.bfloat16, device="cuda"),
                                block_n=64)
+
+
+# ---------------------------------------------------------------------------
+# one-call linear (fused decode path and workspace path)
+
+def _two_call(x, wq, ws, mode):
+    aq, as_ = fp8.quant_act(x, mode)
+    return host_u16(fp8.block_gemm(aq, as_, wq, ws, mode))
+
+
+@pytest.mark.parametrize("K", [512, 4096])
+def test_linear_fused_matches_two_calls(K):
+    """The fused decode path is bit-identical to quant_act + block_gemm."""
+    rng = np.random.default_rng([K, 7])
+    N = 512
+    w = synth.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    wq, ws = fp8.quant_weight_block(dev_bf16(w))
+    for M in (1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16):
+        a = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+        a[:, 3] = synth.f32_to_bf16_bits(np.full(M, 60.0, dtype=np.float32))
+        x = dev_bf16(a)
+        got = host_u16(fp8.linear(x, wq, ws))
+        want = _two_call(x, wq, ws, "block")
+        assert np.array_equal(got, want), f"M={M} K={K}"
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_linear_decode_vs_oracle(M):
+    d = synth.make_config("decode", M=M)
+    wq, ws = fp8.quant_weight_block(dev_bf16(d["W"]))
+    out = host_u16(fp8.linear(dev_bf16(d["A"]), wq, ws))
+    check_out(out, oracle_gemm(d["A"], d["W"]), f"linear decode M={M}")
+
+
+@pytest.mark.parametrize("M,mode", [(17, "block"), (100, "block"), (300, "block"), (3, "tensor"),
+                                    (100, "tensor")])
+def test_linear_workspace_path(M, mode):
+    rng = np.random.default_rng([M, 8])
+    N, K = 384, 640
+    a = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
+    wq, ws = fp8.quant_weight_block(dev_bf16(w), mode)
+    x = dev_bf16(a)
+    got = host_u16(fp8.linear(x, wq, ws, mode))
+    assert np.array_equal(got, _two_call(x, wq, ws, mode))
+    check_out(got, oracle_gemm(a, w, mode), f"linear {mode} M={M}")
+
+
+def test_linear_errors():
+    x = torch.zeros((100, 512), dtype=torch.bfloat16, device="cuda")
+    wq = torch.zeros((256, 512), dtype=torch.uint8, device="cuda")
+    ws = torch.ones((2, 4), dtype=torch.float32, device="cuda")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        fp8.linear(x, wq, ws, workspace=small)          # workspace too small
+    with pytest.raises(ValueError):
+        fp8.linear(x[:, :500], wq[:, :500], ws)          # K not a multiple of 128
+    assert fp8.linear(x[:0], wq, ws).shape == (0, 256)
