@@ -36,6 +36,14 @@ constexpr int kDecodeMaxKB = 128;             // K <= 16384
 #ifndef FP8_DECODE_KBW
 #define FP8_DECODE_KBW 1
 #endif
+// prefill: the hand-scheduled K loop (prefill_asm.inc) instead of the C++ one
+#ifndef FP8_PREFILL_ASM
+#define FP8_PREFILL_ASM 1
+#endif
+// prefill: hold the MFMA / scale-fold interleave with scheduling barriers
+#ifndef FP8_PREFILL_SCHED
+#define FP8_PREFILL_SCHED 0
+#endif
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
@@ -539,6 +547,26 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
       for (int j = 0; j < kPMF; ++j) {
         const v8i fa_next = j + 1 < kPMF ? frag(at + (j + 1) * 16 * 128) : fa;
         v4f pc[kPNF];
+#if FP8_PREFILL_SCHED
+        // each MFMA of fragment j is followed by the four folds of the same
+        // weight fragment's partials of fragment j - 1 (issued four MFMAs
+        // earlier, so already complete); the scheduler is held to that order
+#pragma unroll
+        for (int i = 0; i < kPNF; ++i) {
+          pc[i] = mfma_fp8(fw[i], fa, v4f{0.f, 0.f, 0.f, 0.f});
+          if (j > 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[i][j - 1][r] = __builtin_fmaf(sc[j - 1], pp[i][r], acc[i][j - 1][r]);
+          }
+        }
+        if (j + 1 < kPMF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next A reads
+#pragma unroll
+        for (int i = 0; i < kPNF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (j > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+#else
 #pragma unroll
         for (int i = 0; i < kPNF; ++i) pc[i] = mfma_fp8(fw[i], fa, v4f{0.f, 0.f, 0.f, 0.f});
         if (j > 0) {
@@ -548,6 +576,7 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
             for (int r = 0; r < 4; ++r)
               acc[i][j - 1][r] = __builtin_fmaf(sc[j - 1], pp[i][r], acc[i][j - 1][r]);
         }
+#endif
 #pragma unroll
         for (int i = 0; i < kPNF; ++i) pp[i] = pc[i];
         fa = fa_next;
@@ -586,6 +615,195 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill shape, hand-scheduled: the same tile, wave grid and MFMA roles as
+// gemm_prefill_kernel, with the K loop as generated gfx950 assembly
+// (prefill_asm.inc, written by gen_prefill_asm.py).  C++ below only sets up
+// the operands; the assembly issues every copy, fragment read, MFMA and
+// scale fold in a fixed order:
+//
+//  * one K step = 32 MFMA slots; the activation fragment of slot group j + 1
+//    is read while group j multiplies, each partial product is folded four
+//    MFMAs after it was issued (six partial-product slots in rotation);
+//  * the weight fragments are double-buffered in registers, so the next
+//    step's fragments are read as soon as its copy is visible, and the
+//    barrier that releases a stage sits before the last fragment group's
+//    MFMAs rather than after them (the matrix unit does not drain on it);
+//  * the copies of K block kb + 2 (and its activation scales) go out one per
+//    slot after that barrier; the block index is clamped to the last block,
+//    so no copy ever addresses past the operands' K extent.
+//
+// Activation scales travel by DMA too, four K blocks at a time: every fourth
+// step waves 0-3 copy sa[m0 + row, g .. g + 3] (16 bytes per row, one row per
+// lane) into one of two group buffers; per step each lane gathers its eight
+// fragments' scales with two ds_read2 pairs.  (One float per row per step
+// costs a cache line per row per step.)  The K loop therefore runs on K
+// blocks in multiples of four (K % 512 == 0); other K take the C++ kernel.
+// The two weight blocks' scales for every K block are copied into an LDS
+// table once.  Per step the lane
+// multiplies its eight activation scales by its weight block's scale
+// (fp32), then folds acc = fma(scale, partial, acc): the arithmetic of the
+// C++ kernel, operation for operation.
+//
+// Buffer descriptors carry the row range of each copy (rows >= M or >= N read
+// as zero); the K offset is a scalar offset within the row.  The bf16 stores
+// go through a descriptor that ends at row M, and a wave whose 64 columns
+// start at or past N skips its stores.
+#include "prefill_asm.inc"
+
+// LDS byte offsets (mirrors the constants of gen_prefill_asm.py)
+constexpr int kPfLdsBytes = FP8_PREFILL_LDS_BYTES;
+constexpr int kPfLdsW = FP8_PREFILL_LDS_W;
+constexpr int kPfLdsSa = FP8_PREFILL_LDS_SA;
+constexpr int kPfSaGroup = FP8_PREFILL_LDS_SA_GROUP_BYTES;
+constexpr int kPfLdsSw = FP8_PREFILL_LDS_SW;
+constexpr int kPfKbGroup = FP8_PREFILL_KB_GROUP;   // K blocks per activation-scale copy
+constexpr int kPrefillMaxKB = 256;            // weight-scale table rows: K <= 32768
+static_assert(kPfLdsW == 2 * kPM * 128, "two activation stages precede the weight stages");
+static_assert(kPfLdsSa == kPfLdsW + 2 * kPN * 128, "scale groups follow the operand stages");
+static_assert(kPfSaGroup == kPM * kPfKbGroup * 4, "a scale group holds 4 K blocks of 256 rows");
+static_assert(kPfLdsSw == kPfLdsSa + 2 * kPfSaGroup, "weight-scale table follows the groups");
+static_assert(kPfLdsBytes == kPfLdsSw + 2 * kPrefillMaxKB * 4, "table ends the layout");
+static_assert(kPfLdsBytes <= 160 * 1024, "LDS of one CU");
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// pair-preserving swizzle: chunk pairs (2c, 2c + 1) stay adjacent, so the two
+// 16-byte halves of a lane's fragment are 16 bytes apart in LDS; any eight
+// consecutive rows still land on eight distinct 16-byte bank groups
+__device__ __forceinline__ int swz_pair(int r) { return 2 * ((r >> 1) & 3); }
+
+// the scalar operands of the assembly must sit in SGPRs: every one passes
+// through readfirstlane (the values are wave-uniform by construction)
+__device__ __forceinline__ int pf_uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint32_t pf_uni(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+
+// raw buffer descriptor over [base, base + bytes), bytes clamped to [0, 2^31 - 1]
+__device__ __forceinline__ v4i pf_desc(const void* base, int64_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  v4i d;
+  d[0] = pf_uni((int)(uint32_t)b);
+  d[1] = pf_uni((int)((uint32_t)(b >> 32) & 0xffffu));
+  d[2] = pf_uni((int)n);
+  d[3] = (int)kRawBufferWord3;
+  return d;
+}
+
+template <bool PER_TENSOR>
+__global__ __launch_bounds__(kPThreads) void gemm_prefill_asm_kernel(
+    const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
+    const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
+    uint16_t* __restrict__ out, int64_t ld_out, int M, int N, int KB, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kPfLdsBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kPWavesN;
+  const int wn = wave % kPWavesN;
+  const int r16 = lane & 15;
+  const int kg = lane >> 4;
+
+  // workgroup id -> tile, as gemm_prefill_kernel
+  const int tiles = tiles_m * tiles_n;
+  int lin = blockIdx.x;
+  if (tiles % 8 == 0) lin = (lin % 8) * (tiles / 8) + lin / 8;
+  const int group = lin / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int tm = first_m + (lin % (kGroupM * tiles_n)) % gsize;
+  const int tn = (lin % (kGroupM * tiles_n)) / gsize;
+  const int64_t m0 = (int64_t)tm * kPM;
+  const int64_t n0 = (int64_t)tn * kPN;
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+
+  // copies: wave w, copy t covers tile rows 8 (w + 8 t) + (lane >> 3); lane
+  // stores 16-byte chunk (lane & 7) of the row, which holds source chunk
+  // (lane & 7) ^ swz_pair(row % 16), row % 16 = 8 (w & 1) + (lane >> 3)
+  const int crow = lane >> 3;
+  const int cchunk = (lane & 7) ^ swz_pair(8 * (wave & 1) + crow);
+  const uint32_t offA = (uint32_t)((8 * wave + crow) * ld_a + cchunk * 16);
+  const uint32_t offW = (uint32_t)((8 * wave + crow) * ld_w + cchunk * 16);
+  const uint8_t* a_tile = a + m0 * ld_a;
+  const uint8_t* w_tile = w + n0 * ld_w;
+  const int64_t a_bytes = ((int64_t)M - m0) * ld_a;
+  const int64_t w_bytes = ((int64_t)N - n0) * ld_w;
+  const v4i dA0 = pf_desc(a_tile, a_bytes), dA1 = pf_desc(a_tile + 64 * ld_a, a_bytes - 64 * ld_a);
+  const v4i dA2 = pf_desc(a_tile + 128 * ld_a, a_bytes - 128 * ld_a);
+  const v4i dA3 = pf_desc(a_tile + 192 * ld_a, a_bytes - 192 * ld_a);
+  const v4i dW0 = pf_desc(w_tile, w_bytes), dW1 = pf_desc(w_tile + 64 * ld_w, w_bytes - 64 * ld_w);
+  const v4i dW2 = pf_desc(w_tile + 128 * ld_w, w_bytes - 128 * ld_w);
+  const v4i dW3 = pf_desc(w_tile + 192 * ld_w, w_bytes - 192 * ld_w);
+  const uint32_t wave1k = pf_uni(lds0 + (uint32_t)wave * 1024u);
+
+  // fragment reads: row r16 of the wave's 16-row group, stored chunk
+  // (2 kg) ^ swz_pair(r16) and the next one
+  const int p0 = (2 * kg) ^ swz_pair(r16);
+  const uint32_t rdA = lds0 + (uint32_t)(wm * kPWM * 128 + r16 * 128 + p0 * 16);
+  const uint32_t rdW = lds0 + (uint32_t)(kPfLdsW + wn * kPWN * 128 + r16 * 128 + p0 * 16);
+
+  // activation scales, copied by waves 0..3 every four K blocks: lane
+  // r = 64 wave + lane copies the 16 bytes sa[m0 + r, g .. g + 3] to 16 r of a
+  // group buffer, so the scale of tile row r for block g + u sits at
+  // 16 r + 4 u; lane r16 of wave row wm reads rows 128 wm + 16 j + r16,
+  // fragments 0-3 from scL and 4-7 from scH (1 KiB above)
+  const uint32_t offSa = (uint32_t)((64 * (wave & 3) + lane) * ld_sa * 4);
+  const v4i dSa = pf_desc(sa + m0 * ld_sa, ((int64_t)M - m0) * ld_sa * 4);
+  const int wsa = pf_uni(wave < 4 ? 1 : 0);
+  const uint32_t sam0 = pf_uni(lds0 + (uint32_t)(kPfLdsSa + (wave & 3) * 1024));
+  const uint32_t scL0 = lds0 + (uint32_t)(kPfLdsSa + (wm * kPWM + r16) * 16);
+  const uint32_t scH0 = scL0 + 4u * 16u * 16u;
+  const uint32_t scL1 = scL0 + (uint32_t)kPfSaGroup;
+  const uint32_t scH1 = scH0 + (uint32_t)kPfSaGroup;
+
+  // weight-scale table [2][kPrefillMaxKB]: wave w copies row w / 4, blocks
+  // 64 (w % 4) + lane; the descriptor ends at the last weight block's last
+  // K block, entries past it read zero and are never used
+  const int nb0 = (int)(n0 >> 7);
+  const uint32_t offSw = (uint32_t)(((wave >> 2) * ld_sw + 64 * (wave & 3) + lane) * 4);
+  const v4i dSw = pf_desc(sw + (int64_t)nb0 * ld_sw, (((int64_t)(N / 128) - nb0 - 1) * ld_sw + KB) * 4);
+  const uint32_t swm0 = pf_uni(lds0 + (uint32_t)(kPfLdsSw + wave * 256));
+  uint32_t swrd = lds0 + (uint32_t)(kPfLdsSw + (wn >> 1) * kPrefillMaxKB * 4);
+
+  // output: lane writes 4 adjacent bf16 of token row wm*128 + 16 j + r16
+  const uint32_t offOut = (uint32_t)((wm * kPWM + r16) * ld_out * 2 + (wn * kPWN + 4 * kg) * 2);
+  const v4i dOut = pf_desc(out + m0 * ld_out + n0, ((int64_t)M - m0) * ld_out * 2 - n0 * 2);
+  const uint32_t ldo16 = pf_uni((uint32_t)(16 * ld_out * 2));
+  const int colok = pf_uni((n0 + wn * kPWN < N) ? 1 : 0);
+  const int st = pf_uni(__builtin_bit_cast(int, PER_TENSOR ? sa[0] * sw[0] : 1.0f));
+  const int kb = pf_uni(KB);
+  const int kbm1 = pf_uni(KB - 1);
+  const int kbm4 = pf_uni(KB - kPfKbGroup);
+
+  if (PER_TENSOR) {
+    asm volatile(FP8_PREFILL_ASM_TENSOR
+                 : [swrd] "+v"(swrd)
+                 : [rdA] "v"(rdA), [rdW] "v"(rdW), [offA] "v"(offA), [offW] "v"(offW),
+                   [offOut] "v"(offOut), [dA0] "s"(dA0), [dA1] "s"(dA1), [dA2] "s"(dA2),
+                   [dA3] "s"(dA3), [dW0] "s"(dW0), [dW1] "s"(dW1), [dW2] "s"(dW2), [dW3] "s"(dW3),
+                   [dOut] "s"(dOut), [wave1k] "s"(wave1k), [kb] "s"(kb), [kbm1] "s"(kbm1),
+                   [ldo16] "s"(ldo16), [colok] "s"(colok), [st] "s"(st)
+                 : FP8_PREFILL_ASM_CLOBBERS);
+  } else {
+    asm volatile(FP8_PREFILL_ASM_BLOCK
+                 : [swrd] "+v"(swrd)
+                 : [rdA] "v"(rdA), [rdW] "v"(rdW), [offA] "v"(offA), [offW] "v"(offW),
+                   [offSa] "v"(offSa), [scL0] "v"(scL0), [scH0] "v"(scH0), [scL1] "v"(scL1),
+                   [scH1] "v"(scH1),
+                   [offSw] "v"(offSw), [offOut] "v"(offOut),
+                   [dA0] "s"(dA0), [dA1] "s"(dA1), [dA2] "s"(dA2), [dA3] "s"(dA3),
+                   [dW0] "s"(dW0), [dW1] "s"(dW1), [dW2] "s"(dW2), [dW3] "s"(dW3),
+                   [dSa] "s"(dSa), [dSw] "s"(dSw), [dOut] "s"(dOut), [wave1k] "s"(wave1k),
+                   [sam0] "s"(sam0), [wsa] "s"(wsa), [swm0] "s"(swm0), [kb] "s"(kb),
+                   [kbm1] "s"(kbm1), [kbm4] "s"(kbm4), [ldo16] "s"(ldo16), [colok] "s"(colok)
+                 : FP8_PREFILL_ASM_CLOBBERS);
   }
 }
 
@@ -762,6 +980,23 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
     else
       hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, KBW, false>), grid, dim3(64 * KSPLIT), lds, st,
                          a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
+    return hipGetLastError();
+  }
+  if (FP8_PREFILL_ASM && M > 64 && KB % kPfKbGroup == 0 && KB <= kPrefillMaxKB &&
+      ld_a < kPrefillMaxLd &&
+      ld_w < kPrefillMaxLd && ld_out < kPrefillMaxLd / 2 && ld_sa < kPrefillMaxLd / 4 &&
+      ld_sw < kPrefillMaxLd) {
+    const int tiles_m = (int)((M + kPM - 1) / kPM);
+    const int tiles_n = (int)((N + kPN - 1) / kPN);
+    dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n);
+    if (per_tensor)
+      hipLaunchKernelGGL(gemm_prefill_asm_kernel<true>, grid, dim3(kPThreads), 0, st, a, ld_a,
+                         sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, (int)N, KB, tiles_m,
+                         tiles_n);
+    else
+      hipLaunchKernelGGL(gemm_prefill_asm_kernel<false>, grid, dim3(kPThreads), 0, st, a, ld_a,
+                         sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, (int)N, KB, tiles_m,
+                         tiles_n);
     return hipGetLastError();
   }
   if (M > 64 && ld_a < kPrefillMaxLd && ld_w < kPrefillMaxLd) {

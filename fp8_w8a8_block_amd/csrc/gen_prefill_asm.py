@@ -1,0 +1,400 @@
+"""Writes prefill_asm.inc: the K loop of the prefill GEMM as gfx950 assembly.
+
+The loop is emitted as the text of one inline-asm statement per scale mode
+(block scales, per-tensor scales).  gemm_kernels.hip prepares the operands
+(tile origin, buffer descriptors, per-lane offsets) in C++ and hands them to
+that statement; everything that touches the accumulators -- the copies into
+LDS, the fragment reads, the MFMAs, the per-K-block scale fold and the bf16
+stores -- is scheduled here instruction by instruction.
+
+Why a generator: the instruction order is the performance.  The matrix unit
+should never wait for the fragment reads or the copies, and the compiler's
+scheduler, short of registers at 248 VGPRs, folds every partial product the
+moment it is produced and waits on the matrix unit with s_nop.  Here each
+K step is 32 MFMA slots (4 weight x 8 activation fragments of the wave's
+128 x 64 tile); memory operations are spread over the slots, each partial is
+folded four MFMAs after it was issued, and every LDS counter wait is computed
+from the issue order.
+
+M0 is written by the copies and not listed as clobbered (the compiler reserves
+it): the statement is the last thing the kernel does.
+
+Run:  python gen_prefill_asm.py   (rewrites prefill_asm.inc next to it)
+"""
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+OUT = os.path.join(HERE, "prefill_asm.inc")
+
+# ---------------------------------------------------------------------------
+# LDS layout (bytes from the kernel's LDS base).  Kept in step with the
+# constants in gemm_kernels.hip (kPfLds*), which static_asserts them.
+A_STAGE = (0, 32768)              # 256 activation rows x 128 B per stage
+W_STAGE = (65536, 98304)          # 256 weight rows x 128 B per stage
+SA_GROUP = (131072, 135168)       # activation scales of 4 K blocks x 256 rows (permuted), x2
+SW_TABLE = 139264                 # weight scales [2][256] of the tile's two weight blocks
+LDS_BYTES = 141312
+KB_GROUP = 4                      # K blocks per activation-scale copy
+
+# ---------------------------------------------------------------------------
+# Register map (fixed physical VGPRs; the operands handed in from C++ are
+# allocated by the compiler above these).
+ACC0 = 0                          # acc[i][j][r] = v[(i * 8 + j) * 4 + r], 128 VGPRs
+FW0 = 128                         # weight fragments, two sets of 4 x 8 VGPRs
+FA0 = 192                         # activation fragments, two buffers of 8 VGPRs
+P0 = 208                          # six partial-product slots of 4 VGPRs
+SC0 = 232                         # eight activation scales (times the weight scale)
+SPREV = 240                       # scale of fragment 7 of the previous K step
+SWN = 241                         # weight scale of the next K step
+NUM_FIXED_VGPR = 242
+# scalar scratch
+S_KB, S_DK, S_DK4, S_T = "s84", "s85", "s86", "s87"
+CLOBBER_SGPR = (84, 88)
+
+# partial-product slot of MFMA q (0..31) of a K step: every 5 consecutive
+# MFMAs (cyclically, across K steps) use distinct slots, so a partial is
+# folded 4 MFMAs after it was issued and its slot is free again by then.
+SLOT_SEQ = [0, 1, 2, 3, 4] * 5 + [0, 5, 1, 2, 3, 4, 5]
+FOLD_LAG = 4
+assert len(SLOT_SEQ) == 32
+_cyc = SLOT_SEQ + SLOT_SEQ[:FOLD_LAG]
+assert all(len(set(_cyc[q:q + FOLD_LAG + 1])) == FOLD_LAG + 1 for q in range(32))
+
+LGKM_MAX = 15                     # 4-bit counter on gfx9
+
+
+def acc(i, j, r=0):
+    return ACC0 + (i * 8 + j) * 4 + r
+
+
+def vr(a, n):
+    return f"v[{a}:{a + n - 1}]"
+
+
+def fw(setn, i):
+    return FW0 + 32 * setn + 8 * i
+
+
+def fa(buf):
+    return FA0 + 8 * buf
+
+
+def pslot(q):
+    return P0 + 4 * SLOT_SEQ[q % 32]
+
+
+class Program:
+    """Straight-line emitter with LDS-counter bookkeeping."""
+
+    def __init__(self):
+        self.lines = []
+        self.issued = 0                 # LDS ops issued
+        self.done_upto = 0              # LDS ops known complete (waited for)
+        self.where = {}                 # key -> index (1-based) of its last LDS op
+        self.max_out = 0
+
+    def emit(self, *ls):
+        self.lines.extend(ls)
+
+    def lds(self, key, *ls):
+        self.emit(*ls)
+        self.issued += len(ls)
+        self.where[key] = self.issued
+        self.max_out = max(self.max_out, self.issued - self.done_upto)
+        assert self.issued - self.done_upto <= LGKM_MAX, ("too many LDS ops in flight", key)
+
+    def need(self, *keys):
+        idx = [self.where[k] for k in keys if k in self.where]
+        if not idx:
+            return
+        last = max(idx)
+        if last <= self.done_upto:
+            return
+        n = self.issued - last
+        self.emit(f"s_waitcnt lgkmcnt({n})")
+        self.done_upto = last
+
+    def wait_all_lds(self):
+        if self.done_upto < self.issued:
+            self.emit("s_waitcnt lgkmcnt(0)")
+            self.done_upto = self.issued
+
+
+# ---------------------------------------------------------------------------
+def frag_read(prog, key, dst, base, off):
+    prog.lds(key, f"ds_read_b128 {vr(dst, 4)}, %[{base}] offset:{off}",
+             f"ds_read_b128 {vr(dst + 4, 4)}, %[{base}] offset:{off + 16}")
+
+
+def dma_copy(prog, op, t, stage):
+    """Copy t (rows 8 (wave + 8 t) .. + 7) of operand op for K block S_DK into stage."""
+    base = (A_STAGE if op == "A" else W_STAGE)[stage] + t * 8192
+    prog.emit(f"s_add_u32 m0, %[wave1k], {base}",
+              "s_nop 0",
+              f"buffer_load_dwordx4 %[off{op}], %[d{op}{t}], {S_DK} offen lds")
+
+
+_label = [0]
+
+
+def dma_scale_group(prog, buf, tag, first=None):
+    """Waves 0-3: each lane copies the 16 bytes sa[row, g .. g + 3] of its row,
+    g = min(first K block of the next group, KB - 4) (or `first`), into group
+    buffer `buf`.  Waves 4-7 branch around."""
+    _label[0] += 1
+    skip = f"fp8pf_sa_{tag}_{_label[0]}"
+    prog.emit("s_cmp_eq_u32 %[wsa], 0", f"s_cbranch_scc1 {skip}")
+    if first is None:
+        prog.emit(f"s_add_u32 {S_T}, {S_KB}, {KB_GROUP - 1}",
+                  f"s_and_b32 {S_T}, {S_T}, {-KB_GROUP & 0xffffffff}",
+                  f"s_min_u32 {S_T}, {S_T}, %[kbm4]",
+                  f"s_lshl_b32 {S_T}, {S_T}, 2")
+    else:
+        prog.emit(f"s_mov_b32 {S_T}, {4 * first}")
+    prog.emit(f"s_add_u32 m0, %[sam0], {SA_GROUP[buf] - SA_GROUP[0]}",
+              "s_nop 0",
+              f"buffer_load_dwordx4 %[offSa], %[dSa], {S_T} offen lds",
+              f"{skip}:")
+
+
+def scale_reads(prog, key, kb_next, half):
+    """ds_read2 of the lane's activation scales of K block kb_next: fragments
+    4 half .. 4 half + 3 into SC0 + 4 half .. .  Entry (tile row r, block u)
+    of a group buffer sits at 16 r + 4 u; the lane's rows are
+    128 wm + 16 j + r16, so fragment j is 64 j + u dwords above the lane's
+    base (one base per buffer and half: the read2 offsets are 8-bit), and the
+    16 rows of a fragment fall on 16 distinct banks."""
+    buf = (kb_next // KB_GROUP) % 2
+    u = kb_next % KB_GROUP
+    base = f"%[sc{'LH'[half]}{buf}]"
+    ls = []
+    for k in range(2):
+        jj = 2 * k                       # fragment within the half
+        ls.append(f"ds_read2_b32 {vr(SC0 + 4 * half + jj, 2)}, {base} "
+                  f"offset0:{64 * jj + u} offset1:{64 * (jj + 1) + u}")
+    prog.lds(key, *ls)
+
+
+def set_dk(prog, ahead):
+    """S_DK = 128 * min(kb + ahead, KB - 1), S_DK4 = 4 * the same block."""
+    prog.emit(f"s_add_u32 {S_DK}, {S_KB}, {ahead}",
+              f"s_min_u32 {S_DK}, {S_DK}, %[kbm1]",
+              f"s_lshl_b32 {S_DK4}, {S_DK}, 2",
+              f"s_lshl_b32 {S_DK}, {S_DK}, 7")
+
+
+def gen_loop(block):
+    """Steady-state K steps.  Returns the text of 2 x KB_GROUP consecutive
+    steps as two halves (K blocks 0 .. 7 mod 8: LDS stages alternate every
+    step, activation-scale group buffers every four), taken from the middle
+    of a longer run so that the counter waits see the operations the
+    previous steps left in flight."""
+    prog = Program()
+    sched = {}
+
+    def at(gslot, fn):
+        sched.setdefault(gslot, []).append(fn)
+
+    nsteps = 6 * KB_GROUP
+    bar_slot = 26
+    for st in range(nsteps):
+        p = st % 2                   # LDS stage of this step = weight-fragment set
+        base = 32 * st
+        # activation fragment j (1..7) of this step: after the last MFMA of
+        # fragment j - 2 (same buffer), five slots before its first use
+        for j in range(1, 8):
+            at(base + 4 * j - 5, lambda st=st, j=j, p=p: frag_read(
+                prog, ("fa", st, j), fa(j % 2), "rdA", A_STAGE[p] - A_STAGE[0] + j * 2048))
+
+        def barrier(st=st):
+            prog.wait_all_lds()
+            prog.emit("s_waitcnt vmcnt(0)", "s_barrier")
+            set_dk(prog, 2)
+        at(base + bar_slot, barrier)
+        q = 1 - p
+        at(base + 27, lambda st=st, q=q: (
+            frag_read(prog, ("fa", st + 1, 0), fa(0), "rdA", A_STAGE[q] - A_STAGE[0]),
+            frag_read(prog, ("fw", st + 1, 0), fw(q, 0), "rdW", W_STAGE[q] - W_STAGE[0])))
+        at(base + 28, lambda st=st, q=q: frag_read(
+            prog, ("fw", st + 1, 1), fw(q, 1), "rdW", W_STAGE[q] - W_STAGE[0] + 2048))
+        at(base + 29, lambda st=st, q=q: frag_read(
+            prog, ("fw", st + 1, 2), fw(q, 2), "rdW", W_STAGE[q] - W_STAGE[0] + 4096))
+        at(base + 30, lambda st=st, q=q: frag_read(
+            prog, ("fw", st + 1, 3), fw(q, 3), "rdW", W_STAGE[q] - W_STAGE[0] + 6144))
+        if block:
+            def scales_lo(st=st):
+                prog.emit(f"v_mov_b32 v{SPREV}, v{SC0 + 7}")
+                scale_reads(prog, ("salo", st + 1), st + 1, 0)
+                prog.emit("v_add_u32 %[swrd], 4, %[swrd]")
+                prog.lds(("swn", st + 1), f"ds_read_b32 v{SWN}, %[swrd]")
+            at(base + 28, scales_lo)
+            # the second half at slot 4 of the next step (needed from slot 20)
+            at(base + 32 + 4, lambda st=st: scale_reads(prog, ("sahi", st + 1), st + 1, 1))
+
+            def mul_lo(st=st):
+                prog.need(("salo", st), ("swn", st))
+                for r in range(4):
+                    prog.emit(f"v_mul_f32_e32 v{SC0 + r}, v{SWN}, v{SC0 + r}")
+
+            def mul_hi(st=st):
+                prog.need(("sahi", st), ("swn", st))
+                for r in range(4, 8):
+                    prog.emit(f"v_mul_f32_e32 v{SC0 + r}, v{SWN}, v{SC0 + r}")
+            at(base + 2, mul_lo)
+            at(base + 12, mul_hi)
+            if st % KB_GROUP == 1:
+                nbuf = (st // KB_GROUP + 1) % 2
+                at(base + 30, lambda nbuf=nbuf: dma_scale_group(prog, nbuf, "blk"))
+        # copies of K block kb + 2 into this step's stage (released at the barrier)
+        for k, (op, t) in enumerate([("A", 0), ("W", 0), ("A", 1), ("W", 1),
+                                     ("A", 2), ("W", 2), ("A", 3), ("W", 3)]):
+            at(base + 28 + k, lambda op=op, t=t, p=p: dma_copy(prog, op, t, p))
+
+    total = 32 * nsteps
+    marks = {}
+    for gs in range(total):
+        st, qq = divmod(gs, 32)
+        if qq == 0:
+            marks[st] = len(prog.lines)
+        j, i = divmod(qq, 4)
+        c = st % 2
+        prog.need(("fa", st, j), ("fw", st, i))
+        if block:
+            prog.emit(f"v_mfma_f32_16x16x128_f8f6f4 {vr(pslot(qq), 4)}, {vr(fw(c, i), 8)}, "
+                      f"{vr(fa(j % 2), 8)}, 0")
+            pq = qq - FOLD_LAG
+            jj, ii = divmod(pq % 32, 4)
+            s = f"v{SC0 + jj}" if pq >= 0 else f"v{SPREV}"
+            for r in range(4):
+                prog.emit(f"v_fmac_f32_e32 v{acc(ii, jj, r)}, {s}, v{pslot(pq) + r}")
+        else:
+            prog.emit(f"v_mfma_f32_16x16x128_f8f6f4 {vr(acc(i, j), 4)}, {vr(fw(c, i), 8)}, "
+                      f"{vr(fa(j % 2), 8)}, {vr(acc(i, j), 4)}")
+        for fn in sched.get(gs, []):
+            fn()
+        if qq == 31:
+            prog.emit(f"s_add_u32 {S_KB}, {S_KB}, 1")
+    marks[nsteps] = len(prog.lines)
+    first = prog.lines[marks[2 * KB_GROUP]:marks[3 * KB_GROUP]]
+    second = prog.lines[marks[3 * KB_GROUP]:marks[4 * KB_GROUP]]
+    return first, second, prog.max_out
+
+
+def gen_prologue(block):
+    # some scalar operands were just written by v_readfirstlane; VMEM reads of
+    # an SGPR written by the VALU need wait states
+    L = ["s_nop 7"]
+    for k in range(128):
+        L.append(f"v_mov_b32 v{ACC0 + k}, 0")
+    if block:
+        for k in range(24):
+            L.append(f"v_mov_b32 v{P0 + k}, 0")
+        L.append(f"v_mov_b32 v{SPREV}, 0")
+        # weight-scale table: row b (this tile's weight blocks), blocks 64 (w % 4) + lane
+        L += ["s_mov_b32 m0, %[swm0]", "s_nop 0", "buffer_load_dword %[offSw], %[dSw], 0 offen lds"]
+    L.append(f"s_mov_b32 {S_KB}, 0")
+    prog = Program()
+    prog.emit(*L)
+    if block:
+        dma_scale_group(prog, 0, "pro", first=0)
+    # K blocks 0 and 1 into stages 0 and 1
+    for stage, ahead in ((0, 0), (1, 1)):
+        set_dk(prog, ahead)
+        for op, t in [(o, t) for t in range(4) for o in ("A", "W")]:
+            dma_copy(prog, op, t, stage)
+    prog.emit("s_waitcnt vmcnt(8)", "s_barrier")
+    # leave S_DK on block 1: the first step re-issues the tail of that copy
+    for i in range(4):
+        frag_read(prog, None, fw(0, i), "rdW", i * 2048)
+    frag_read(prog, None, fa(0), "rdA", 0)
+    frag_read(prog, None, fa(1), "rdA", 2048)
+    if block:
+        prog.wait_all_lds()
+        scale_reads(prog, None, 0, 0)
+        scale_reads(prog, None, 0, 1)
+        prog.emit(f"ds_read_b32 v{SWN}, %[swrd]")
+    prog.emit("s_waitcnt lgkmcnt(0)")
+    return prog.lines
+
+
+def gen_epilogue(block, tag):
+    # the last MFMAs' results are read by the VALU below: drain first
+    L = ["s_nop 7", "s_nop 7"]
+    if block:
+        # fold fragment 7 of the last K step
+        for q in range(28, 32):
+            jj, ii = divmod(q, 4)
+            for r in range(4):
+                L.append(f"v_fmac_f32_e32 v{acc(ii, jj, r)}, v{SPREV}, v{pslot(q) + r}")
+    L.append("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    if not block:
+        for k in range(128):
+            L.append(f"v_mul_f32_e32 v{ACC0 + k}, %[st], v{ACC0 + k}")
+    L += ["s_cmp_eq_u32 %[colok], 0", f"s_cbranch_scc1 fp8pf_done_{tag}"]
+    L.append(f"v_mov_b32 v{P0}, %[offOut]")
+    tmp = P0 + 4
+    n = 0
+    for j in range(8):
+        for i in range(4):
+            t = tmp + 2 * (n % 8)
+            L += [f"v_cvt_pk_bf16_f32 v{t}, v{acc(i, j, 0)}, v{acc(i, j, 1)}",
+                  f"v_cvt_pk_bf16_f32 v{t + 1}, v{acc(i, j, 2)}, v{acc(i, j, 3)}",
+                  f"buffer_store_dwordx2 {vr(t, 2)}, v{P0}, %[dOut], 0 offen offset:{i * 32}"]
+            n += 1
+        L.append(f"v_add_u32 v{P0}, %[ldo16], v{P0}")
+    L.append(f"fp8pf_done_{tag}:")
+    return L
+
+
+def gen(block):
+    """KB must be a positive multiple of KB_GROUP (the caller checks)."""
+    tag = "blk" if block else "pt"
+    _label[0] = 0
+    first, second, max_out = gen_loop(block)
+    L = gen_prologue(block)
+    L.append(f"fp8pf_loop_{tag}:")
+    L += first
+    L += [f"s_cmp_eq_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_tail_{tag}"]
+    L += second
+    L += [f"s_cmp_lt_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_loop_{tag}"]
+    L.append(f"fp8pf_tail_{tag}:")
+    L += gen_epilogue(block, tag)
+    return L, max_out
+
+
+def c_string(lines):
+    return "\n".join(f'  "{l}\\n\\t"' for l in lines)
+
+
+def main(path=OUT):
+    out = ["// Generated by gen_prefill_asm.py; do not edit by hand.",
+           "// K loop of gemm_prefill_kernel as gfx950 assembly (see that file).",
+           "#pragma once", ""]
+    for block in (True, False):
+        lines, max_out = gen(block)
+        name = "FP8_PREFILL_ASM_BLOCK" if block else "FP8_PREFILL_ASM_TENSOR"
+        out.append(f"// {len(lines)} lines; at most {max_out} LDS reads in flight")
+        out.append(f"#define {name} \\")
+        out.append(c_string(lines).replace("\n", " \\\n"))
+        out.append("")
+    vg = ", ".join(f'"v{k}"' for k in range(NUM_FIXED_VGPR))
+    sg = ", ".join(f'"s{k}"' for k in range(*CLOBBER_SGPR))
+    out.append(f'#define FP8_PREFILL_ASM_CLOBBERS {vg}, {sg}, "scc", "memory"')
+    out.append(f"#define FP8_PREFILL_ASM_FIXED_VGPRS {NUM_FIXED_VGPR}")
+    out.append(f"#define FP8_PREFILL_LDS_BYTES {LDS_BYTES}")
+    out.append(f"#define FP8_PREFILL_LDS_SA {SA_GROUP[0]}")
+    out.append(f"#define FP8_PREFILL_LDS_SA_GROUP_BYTES {SA_GROUP[1] - SA_GROUP[0]}")
+    out.append(f"#define FP8_PREFILL_LDS_SW {SW_TABLE}")
+    out.append(f"#define FP8_PREFILL_KB_GROUP {KB_GROUP}")
+    out.append(f"#define FP8_PREFILL_LDS_W {W_STAGE[0]}")
+    text = "\n".join(out) + "\n"
+    if path is None:
+        return text
+    with open(path, "w") as f:
+        f.write(text)
+    return text
+
+
+if __name__ == "__main__":
+    main(sys.argv[1] if len(sys.argv) > 1 else OUT)

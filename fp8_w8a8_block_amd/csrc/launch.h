@@ -31,7 +31,7 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
                        bool per_tensor, hipStream_t st);
 
 // Fused decode linear: dynamic 1x128 quantization of x inside the decode GEMM
-// (block scales).  Supported for 1 <= M <= 16 and K <= 16384; the result is
+// (block scales).  Dispatched for 1 <= M <= 4 and K <= 16384; the result is
 // bit-identical to launch_quant_act_block followed by launch_gemm.
 bool linear_decode_supported(int64_t M, int64_t K);
 hipError_t launch_linear_decode(const uint16_t* x, int64_t ld_x, const uint8_t* w, int64_t ld_w,

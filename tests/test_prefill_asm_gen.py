@@ -1,0 +1,50 @@
+"""The committed K-loop assembly (prefill_asm.inc) is what its generator writes.
+
+gen_prefill_asm.py asserts its own scheduling invariants while it runs
+(partial-product slots never reused before they are folded, never more than
+15 LDS reads in flight for the 4-bit counter); this test runs it and checks
+that the include file the library is built from is its current output."""
+import importlib.util
+import os
+import re
+
+CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                    "fp8_w8a8_block_amd", "csrc")
+
+
+def _gen():
+    spec = importlib.util.spec_from_file_location("gen_prefill_asm",
+                                                  os.path.join(CSRC, "gen_prefill_asm.py"))
+    g = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(g)
+    return g
+
+
+def test_include_is_generator_output():
+    g = _gen()
+    text = g.main(None)
+    with open(os.path.join(CSRC, "prefill_asm.inc")) as f:
+        assert f.read() == text, "prefill_asm.inc is stale: run gen_prefill_asm.py"
+
+
+def test_fixed_registers_and_lds_fit():
+    g = _gen()
+    assert g.NUM_FIXED_VGPR + 12 <= 256          # fixed map plus the C++ operands
+    assert g.LDS_BYTES <= 160 * 1024
+    for block in (True, False):
+        lines, max_out = g.gen(block)
+        assert max_out <= 15
+        regs = [int(m) for l in lines for m in re.findall(r"\bv(\d+)\b", l)]
+        regs += [int(b) for l in lines for a, b in re.findall(r"\bv\[(\d+):(\d+)\]", l)]
+        assert max(regs) < g.NUM_FIXED_VGPR
+
+
+def test_every_lds_wait_names_a_smaller_count():
+    # counts in s_waitcnt lgkmcnt(n) stay encodable (4 bits)
+    g = _gen()
+    for block in (True, False):
+        lines, _ = g.gen(block)
+        for l in lines:
+            m = re.match(r"s_waitcnt lgkmcnt\((\d+)\)", l)
+            if m:
+                assert int(m.group(1)) <= 15
