@@ -40,10 +40,6 @@ constexpr int kDecodeMaxKB = 128;             // K <= 16384
 #ifndef FP8_PREFILL_ASM
 #define FP8_PREFILL_ASM 1
 #endif
-// prefill: hold the MFMA / scale-fold interleave with scheduling barriers
-#ifndef FP8_PREFILL_SCHED
-#define FP8_PREFILL_SCHED 0
-#endif
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
@@ -547,26 +543,6 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
       for (int j = 0; j < kPMF; ++j) {
         const v8i fa_next = j + 1 < kPMF ? frag(at + (j + 1) * 16 * 128) : fa;
         v4f pc[kPNF];
-#if FP8_PREFILL_SCHED
-        // each MFMA of fragment j is followed by the four folds of the same
-        // weight fragment's partials of fragment j - 1 (issued four MFMAs
-        // earlier, so already complete); the scheduler is held to that order
-#pragma unroll
-        for (int i = 0; i < kPNF; ++i) {
-          pc[i] = mfma_fp8(fw[i], fa, v4f{0.f, 0.f, 0.f, 0.f});
-          if (j > 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[i][j - 1][r] = __builtin_fmaf(sc[j - 1], pp[i][r], acc[i][j - 1][r]);
-          }
-        }
-        if (j + 1 < kPMF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next A reads
-#pragma unroll
-        for (int i = 0; i < kPNF; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (j > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
-#else
 #pragma unroll
         for (int i = 0; i < kPNF; ++i) pc[i] = mfma_fp8(fw[i], fa, v4f{0.f, 0.f, 0.f, 0.f});
         if (j > 0) {
@@ -576,7 +552,6 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
             for (int r = 0; r < 4; ++r)
               acc[i][j - 1][r] = __builtin_fmaf(sc[j - 1], pp[i][r], acc[i][j - 1][r]);
         }
-#endif
 #pragma unroll
         for (int i = 0; i < kPNF; ++i) pp[i] = pc[i];
         fa = fa_next;
