@@ -624,9 +624,11 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
 // C++ kernel, operation for operation.
 //
 // Buffer descriptors carry the row range of each copy (rows >= M or >= N read
-// as zero); the K offset is a scalar offset within the row.  The bf16 stores
-// go through a descriptor that ends at row M, and a wave whose 64 columns
-// start at or past N skips its stores.
+// as zero); the K offset is a scalar offset within the row.  The bf16 output
+// is staged through LDS (after a final barrier frees the stages) so every
+// store writes 16 contiguous bytes of a row; the stores go through a
+// descriptor that ends at row M, and a wave whose 64 columns start at or
+// past N skips its stores.
 #include "prefill_asm.inc"
 
 // LDS byte offsets (mirrors the constants of gen_prefill_asm.py)
@@ -756,6 +758,8 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_asm_kernel(
   const int kb = pf_uni(KB);
   const int kbm1 = pf_uni(KB - 1);
   const int kbm4 = pf_uni(KB - kPfKbGroup);
+  const int wave_s = pf_uni(wave);
+  const uint32_t ldsb = pf_uni(lds0);
 
   if (PER_TENSOR) {
     asm volatile(FP8_PREFILL_ASM_TENSOR
@@ -764,7 +768,8 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_asm_kernel(
                    [offOut] "v"(offOut), [dA0] "s"(dA0), [dA1] "s"(dA1), [dA2] "s"(dA2),
                    [dA3] "s"(dA3), [dW0] "s"(dW0), [dW1] "s"(dW1), [dW2] "s"(dW2), [dW3] "s"(dW3),
                    [dOut] "s"(dOut), [wave1k] "s"(wave1k), [kb] "s"(kb), [kbm1] "s"(kbm1),
-                   [ldo16] "s"(ldo16), [colok] "s"(colok), [st] "s"(st)
+                   [ldo16] "s"(ldo16), [colok] "s"(colok), [st] "s"(st), [wave] "s"(wave_s),
+                   [ldsb] "s"(ldsb)
                  : FP8_PREFILL_ASM_CLOBBERS);
   } else {
     asm volatile(FP8_PREFILL_ASM_BLOCK
@@ -777,7 +782,8 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_asm_kernel(
                    [dW0] "s"(dW0), [dW1] "s"(dW1), [dW2] "s"(dW2), [dW3] "s"(dW3),
                    [dSa] "s"(dSa), [dSw] "s"(dSw), [dOut] "s"(dOut), [wave1k] "s"(wave1k),
                    [sam0] "s"(sam0), [wsa] "s"(wsa), [swm0] "s"(swm0), [kb] "s"(kb),
-                   [kbm1] "s"(kbm1), [kbm4] "s"(kbm4), [ldo16] "s"(ldo16), [colok] "s"(colok)
+                   [kbm1] "s"(kbm1), [kbm4] "s"(kbm4), [ldo16] "s"(ldo16), [colok] "s"(colok),
+                   [wave] "s"(wave_s), [ldsb] "s"(ldsb)
                  : FP8_PREFILL_ASM_CLOBBERS);
   }
 }

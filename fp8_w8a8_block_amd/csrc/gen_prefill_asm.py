@@ -318,7 +318,17 @@ def gen_prologue(block):
     return prog.lines
 
 
+EP_PITCH = 144                    # bytes per staged output row (64 bf16 + 16 B pad)
+EP_HALF = 64 * EP_PITCH           # one wave's staging area: 64 rows
+
+
 def gen_epilogue(block, tag):
+    """Fold the last fragment, round to bf16 and store.  The wave's 128 x 64
+    outputs go out in two halves of 64 rows, each staged through LDS so that
+    a lane stores 16 contiguous bytes and an instruction covers eight whole
+    128-byte row segments (the MFMA layout gives a lane 4 adjacent values,
+    i.e. 8-byte pieces of 16 rows).  The staged rows are 144 bytes apart:
+    16 lanes writing 8 bytes each to 16 rows hit 16 distinct bank pairs."""
     # the last MFMAs' results are read by the VALU below: drain first
     L = ["s_nop 7", "s_nop 7"]
     if block:
@@ -327,22 +337,65 @@ def gen_epilogue(block, tag):
             jj, ii = divmod(q, 4)
             for r in range(4):
                 L.append(f"v_fmac_f32_e32 v{acc(ii, jj, r)}, v{SPREV}, v{pslot(q) + r}")
-    L.append("s_waitcnt vmcnt(0) lgkmcnt(0)")
-    if not block:
+    else:
         for k in range(128):
             L.append(f"v_mul_f32_e32 v{ACC0 + k}, %[st], v{ACC0 + k}")
-    L += ["s_cmp_eq_u32 %[colok], 0", f"s_cbranch_scc1 fp8pf_done_{tag}"]
-    L.append(f"v_mov_b32 v{P0}, %[offOut]")
-    tmp = P0 + 4
+    # every wave's copies and fragment reads are done: the stages are free
+    L += ["s_waitcnt vmcnt(0) lgkmcnt(0)", "s_barrier",
+          "s_cmp_eq_u32 %[colok], 0", f"s_cbranch_scc1 fp8pf_done_{tag}"]
+    vl, vt, vk, vw, vrd, vo = (FW0 + k for k in range(6))
+    buf = FW0 + 8                      # 32 VGPRs of read-back data
+    s_reg, s_ldo2, s_uni, s_step = S_KB, S_DK, S_DK4, S_T
+    L += [f"v_mbcnt_lo_u32_b32 v{vl}, -1, 0",
+          f"v_mbcnt_hi_u32_b32 v{vl}, -1, v{vl}",
+          # staging area of this wave
+          f"s_mul_i32 {s_reg}, %[wave], {EP_HALF}",
+          f"s_add_u32 {s_reg}, {s_reg}, %[ldsb]",
+          # write base: row r16, 8-byte piece kg
+          f"v_and_b32 v{vt}, 15, v{vl}",
+          f"v_mul_u32_u24 v{vt}, {EP_PITCH}, v{vt}",
+          f"v_lshrrev_b32 v{vk}, 4, v{vl}",
+          f"v_lshl_add_u32 v{vw}, v{vk}, 3, v{vt}",
+          f"v_add_u32 v{vw}, {s_reg}, v{vw}",
+          # read base: row lane / 8, 16-byte chunk lane % 8
+          f"v_lshrrev_b32 v{vt}, 3, v{vl}",
+          f"v_mul_u32_u24 v{vt}, {EP_PITCH}, v{vt}",
+          f"v_and_b32 v{vk}, 7, v{vl}",
+          f"v_lshl_add_u32 v{vrd}, v{vk}, 4, v{vt}",
+          f"v_add_u32 v{vrd}, {s_reg}, v{vrd}",
+          # store offset: row 128 wm + lane / 8, columns 64 wn + 8 (lane % 8)
+          f"s_lshr_b32 {s_ldo2}, %[ldo16], 4",
+          f"s_lshr_b32 {s_uni}, %[wave], 2",
+          f"s_mul_i32 {s_uni}, {s_uni}, 128",
+          f"s_mul_i32 {s_uni}, {s_uni}, {s_ldo2}",
+          f"s_and_b32 {s_step}, %[wave], 3",
+          f"s_lshl_b32 {s_step}, {s_step}, 7",
+          f"s_add_u32 {s_uni}, {s_uni}, {s_step}",
+          f"v_lshrrev_b32 v{vt}, 3, v{vl}",
+          f"v_mul_lo_u32 v{vt}, {s_ldo2}, v{vt}",
+          f"v_lshl_add_u32 v{vo}, v{vk}, 4, v{vt}",
+          f"v_add_u32 v{vo}, {s_uni}, v{vo}",
+          f"s_lshr_b32 {s_step}, %[ldo16], 1"]          # 8 rows
+    tmp = P0
     n = 0
-    for j in range(8):
-        for i in range(4):
-            t = tmp + 2 * (n % 8)
-            L += [f"v_cvt_pk_bf16_f32 v{t}, v{acc(i, j, 0)}, v{acc(i, j, 1)}",
-                  f"v_cvt_pk_bf16_f32 v{t + 1}, v{acc(i, j, 2)}, v{acc(i, j, 3)}",
-                  f"buffer_store_dwordx2 {vr(t, 2)}, v{P0}, %[dOut], 0 offen offset:{i * 32}"]
-            n += 1
-        L.append(f"v_add_u32 v{P0}, %[ldo16], v{P0}")
+    for h in range(2):
+        for j in range(4 * h, 4 * h + 4):
+            for i in range(4):
+                t = tmp + 2 * (n % 12)
+                off = (j - 4 * h) * 16 * EP_PITCH + i * 32
+                L += [f"v_cvt_pk_bf16_f32 v{t}, v{acc(i, j, 0)}, v{acc(i, j, 1)}",
+                      f"v_cvt_pk_bf16_f32 v{t + 1}, v{acc(i, j, 2)}, v{acc(i, j, 3)}",
+                      f"ds_write_b64 v{vw}, {vr(t, 2)} offset:{off}"]
+                n += 1
+        for q in range(8):
+            L.append(f"ds_read_b128 {vr(buf + 4 * q, 4)}, v{vrd} offset:{q * 8 * EP_PITCH}")
+        L.append("s_waitcnt lgkmcnt(0)")
+        for q in range(8):
+            # a VALU write right after a 16-byte store of the registers it reads
+            # needs a wait state
+            L.append(f"buffer_store_dwordx4 {vr(buf + 4 * q, 4)}, v{vo}, %[dOut], 0 offen")
+            L.append("s_nop 0")
+            L.append(f"v_add_u32 v{vo}, {s_step}, v{vo}")
     L.append(f"fp8pf_done_{tag}:")
     return L
 
