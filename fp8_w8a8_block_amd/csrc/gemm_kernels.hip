@@ -17,6 +17,8 @@
 // K block.  A and B use the same assignment, so every k pairs a[m, k] with
 // w[n, k] whatever order the unit walks the 32 bytes in.  The 16x16 fp32
 // result sits in lane n + 16 (m / 4), register m % 4.
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -672,18 +674,23 @@ __device__ __forceinline__ v4i pf_desc(const void* base, int64_t bytes) {
   return d;
 }
 
-template <bool PER_TENSOR>
-__global__ __launch_bounds__(kPThreads) void gemm_prefill_asm_kernel(
+// NW = 8: 256 x 256 tiles, two waves per SIMD.  NW = 4: 256 x 128 tiles, one
+// wave per SIMD, for grids that would otherwise leave CUs idle (the same
+// 128 x 64 wave tile, so the K loop is the same schedule).
+template <bool PER_TENSOR, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
     const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
     uint16_t* __restrict__ out, int64_t ld_out, int M, int N, int KB, int tiles_m, int tiles_n) {
+  constexpr int kTN = 32 * NW;                 // tile width (weight rows)
+  constexpr int kWN = NW / 2;                  // waves along N
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kPfLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / kPWavesN;
-  const int wn = wave % kPWavesN;
+  const int wm = wave / kWN;
+  const int wn = wave % kWN;
   const int r16 = lane & 15;
   const int kg = lane >> 4;
 
@@ -697,27 +704,22 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_asm_kernel(
   const int tm = first_m + (lin % (kGroupM * tiles_n)) % gsize;
   const int tn = (lin % (kGroupM * tiles_n)) / gsize;
   const int64_t m0 = (int64_t)tm * kPM;
-  const int64_t n0 = (int64_t)tn * kPN;
+  const int64_t n0 = (int64_t)tn * kTN;
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
 
-  // copies: wave w, copy t covers tile rows 8 (w + 8 t) + (lane >> 3); lane
+  // copies: wave w, copy t covers tile rows 8 (w + NW t) + (lane >> 3); lane
   // stores 16-byte chunk (lane & 7) of the row, which holds source chunk
-  // (lane & 7) ^ swz_pair(row % 16), row % 16 = 8 (w & 1) + (lane >> 3)
+  // (lane & 7) ^ swz_pair(row % 16), row % 16 = 8 (w & 1) + (lane >> 3).  The
+  // descriptors end at row M (N); copy t adds t * rs to the lane offset.
   const int crow = lane >> 3;
   const int cchunk = (lane & 7) ^ swz_pair(8 * (wave & 1) + crow);
   const uint32_t offA = (uint32_t)((8 * wave + crow) * ld_a + cchunk * 16);
   const uint32_t offW = (uint32_t)((8 * wave + crow) * ld_w + cchunk * 16);
-  const uint8_t* a_tile = a + m0 * ld_a;
-  const uint8_t* w_tile = w + n0 * ld_w;
-  const int64_t a_bytes = ((int64_t)M - m0) * ld_a;
-  const int64_t w_bytes = ((int64_t)N - n0) * ld_w;
-  const v4i dA0 = pf_desc(a_tile, a_bytes), dA1 = pf_desc(a_tile + 64 * ld_a, a_bytes - 64 * ld_a);
-  const v4i dA2 = pf_desc(a_tile + 128 * ld_a, a_bytes - 128 * ld_a);
-  const v4i dA3 = pf_desc(a_tile + 192 * ld_a, a_bytes - 192 * ld_a);
-  const v4i dW0 = pf_desc(w_tile, w_bytes), dW1 = pf_desc(w_tile + 64 * ld_w, w_bytes - 64 * ld_w);
-  const v4i dW2 = pf_desc(w_tile + 128 * ld_w, w_bytes - 128 * ld_w);
-  const v4i dW3 = pf_desc(w_tile + 192 * ld_w, w_bytes - 192 * ld_w);
+  const v4i dA = pf_desc(a + m0 * ld_a, ((int64_t)M - m0) * ld_a);
+  const v4i dW = pf_desc(w + n0 * ld_w, ((int64_t)N - n0) * ld_w);
+  const uint32_t rsA = pf_uni((uint32_t)(NW * 8 * ld_a));
+  const uint32_t rsW = pf_uni((uint32_t)(NW * 8 * ld_w));
   const uint32_t wave1k = pf_uni(lds0 + (uint32_t)wave * 1024u);
 
   // fragment reads: row r16 of the wave's 16-row group, stored chunk
@@ -747,10 +749,10 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_asm_kernel(
   const uint32_t offSw = (uint32_t)(((wave >> 2) * ld_sw + 64 * (wave & 3) + lane) * 4);
   const v4i dSw = pf_desc(sw + (int64_t)nb0 * ld_sw, (((int64_t)(N / 128) - nb0 - 1) * ld_sw + KB) * 4);
   const uint32_t swm0 = pf_uni(lds0 + (uint32_t)(kPfLdsSw + wave * 256));
-  uint32_t swrd = lds0 + (uint32_t)(kPfLdsSw + (wn >> 1) * kPrefillMaxKB * 4);
+  uint32_t swrd = lds0 + (uint32_t)(kPfLdsSw + ((wn * kPWN) >> 7) * kPrefillMaxKB * 4);
 
-  // output: lane writes 4 adjacent bf16 of token row wm*128 + 16 j + r16
-  const uint32_t offOut = (uint32_t)((wm * kPWM + r16) * ld_out * 2 + (wn * kPWN + 4 * kg) * 2);
+  // output: bf16 rows from m0, columns from n0; the epilogue derives its
+  // lane offsets from the lane id
   const v4i dOut = pf_desc(out + m0 * ld_out + n0, ((int64_t)M - m0) * ld_out * 2 - n0 * 2);
   const uint32_t ldo16 = pf_uni((uint32_t)(16 * ld_out * 2));
   const int colok = pf_uni((n0 + wn * kPWN < N) ? 1 : 0);
@@ -761,31 +763,75 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_asm_kernel(
   const int wave_s = pf_uni(wave);
   const uint32_t ldsb = pf_uni(lds0);
 
+#define FP8_PF_COMMON_OPERANDS                                                                  \
+  [rdA] "v"(rdA), [rdW] "v"(rdW), [offA] "v"(offA), [offW] "v"(offW), [dA] "s"(dA),            \
+      [dW] "s"(dW), [rsA] "s"(rsA), [rsW] "s"(rsW), [dOut] "s"(dOut), [wave1k] "s"(wave1k),     \
+      [kb] "s"(kb), [kbm1] "s"(kbm1), [ldo16] "s"(ldo16), [colok] "s"(colok),                  \
+      [wave] "s"(wave_s), [ldsb] "s"(ldsb)
+#define FP8_PF_BLOCK_OPERANDS                                                                   \
+  [offSa] "v"(offSa), [scL0] "v"(scL0), [scH0] "v"(scH0), [scL1] "v"(scL1), [scH1] "v"(scH1),  \
+      [offSw] "v"(offSw), [dSa] "s"(dSa), [dSw] "s"(dSw), [sam0] "s"(sam0), [wsa] "s"(wsa),     \
+      [swm0] "s"(swm0), [kbm4] "s"(kbm4)
   if (PER_TENSOR) {
-    asm volatile(FP8_PREFILL_ASM_TENSOR
-                 : [swrd] "+v"(swrd)
-                 : [rdA] "v"(rdA), [rdW] "v"(rdW), [offA] "v"(offA), [offW] "v"(offW),
-                   [offOut] "v"(offOut), [dA0] "s"(dA0), [dA1] "s"(dA1), [dA2] "s"(dA2),
-                   [dA3] "s"(dA3), [dW0] "s"(dW0), [dW1] "s"(dW1), [dW2] "s"(dW2), [dW3] "s"(dW3),
-                   [dOut] "s"(dOut), [wave1k] "s"(wave1k), [kb] "s"(kb), [kbm1] "s"(kbm1),
-                   [ldo16] "s"(ldo16), [colok] "s"(colok), [st] "s"(st), [wave] "s"(wave_s),
-                   [ldsb] "s"(ldsb)
-                 : FP8_PREFILL_ASM_CLOBBERS);
+    if (NW == 8)
+      asm volatile(FP8_PREFILL_ASM_TENSOR_W8
+                   : [swrd] "+v"(swrd)
+                   : FP8_PF_COMMON_OPERANDS, [st] "s"(st)
+                   : FP8_PREFILL_ASM_CLOBBERS);
+    else
+      asm volatile(FP8_PREFILL_ASM_TENSOR_W4
+                   : [swrd] "+v"(swrd)
+                   : FP8_PF_COMMON_OPERANDS, [st] "s"(st)
+                   : FP8_PREFILL_ASM_CLOBBERS);
   } else {
-    asm volatile(FP8_PREFILL_ASM_BLOCK
-                 : [swrd] "+v"(swrd)
-                 : [rdA] "v"(rdA), [rdW] "v"(rdW), [offA] "v"(offA), [offW] "v"(offW),
-                   [offSa] "v"(offSa), [scL0] "v"(scL0), [scH0] "v"(scH0), [scL1] "v"(scL1),
-                   [scH1] "v"(scH1),
-                   [offSw] "v"(offSw), [offOut] "v"(offOut),
-                   [dA0] "s"(dA0), [dA1] "s"(dA1), [dA2] "s"(dA2), [dA3] "s"(dA3),
-                   [dW0] "s"(dW0), [dW1] "s"(dW1), [dW2] "s"(dW2), [dW3] "s"(dW3),
-                   [dSa] "s"(dSa), [dSw] "s"(dSw), [dOut] "s"(dOut), [wave1k] "s"(wave1k),
-                   [sam0] "s"(sam0), [wsa] "s"(wsa), [swm0] "s"(swm0), [kb] "s"(kb),
-                   [kbm1] "s"(kbm1), [kbm4] "s"(kbm4), [ldo16] "s"(ldo16), [colok] "s"(colok),
-                   [wave] "s"(wave_s), [ldsb] "s"(ldsb)
-                 : FP8_PREFILL_ASM_CLOBBERS);
+    if (NW == 8)
+      asm volatile(FP8_PREFILL_ASM_BLOCK_W8
+                   : [swrd] "+v"(swrd)
+                   : FP8_PF_COMMON_OPERANDS, FP8_PF_BLOCK_OPERANDS
+                   : FP8_PREFILL_ASM_CLOBBERS);
+    else
+      asm volatile(FP8_PREFILL_ASM_BLOCK_W4
+                   : [swrd] "+v"(swrd)
+                   : FP8_PF_COMMON_OPERANDS, FP8_PF_BLOCK_OPERANDS
+                   : FP8_PREFILL_ASM_CLOBBERS);
   }
+#undef FP8_PF_COMMON_OPERANDS
+#undef FP8_PF_BLOCK_OPERANDS
+}
+
+template <int NW>
+hipError_t launch_prefill_asm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
+                              const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
+                              uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int KB,
+                              bool per_tensor, hipStream_t st) {
+  const int tiles_m = (int)((M + kPM - 1) / kPM);
+  const int tiles_n = (int)((N + 32 * NW - 1) / (32 * NW));
+  dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n);
+  if (per_tensor)
+    hipLaunchKernelGGL((gemm_prefill_asm_kernel<true, NW>), grid, dim3(64 * NW), 0, st, a, ld_a,
+                       sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, (int)N, KB, tiles_m,
+                       tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_prefill_asm_kernel<false, NW>), grid, dim3(64 * NW), 0, st, a, ld_a,
+                       sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, (int)N, KB, tiles_m,
+                       tiles_n);
+  return hipGetLastError();
+}
+
+// compute units of the current device (looked up once per device; every
+// thread that races on the first lookup stores the same value)
+std::atomic<int> g_device_cus[64];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = g_device_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    g_device_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 // ---------------------------------------------------------------------------
@@ -967,18 +1013,14 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
       ld_a < kPrefillMaxLd &&
       ld_w < kPrefillMaxLd && ld_out < kPrefillMaxLd / 2 && ld_sa < kPrefillMaxLd / 4 &&
       ld_sw < kPrefillMaxLd) {
-    const int tiles_m = (int)((M + kPM - 1) / kPM);
-    const int tiles_n = (int)((N + kPN - 1) / kPN);
-    dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n);
-    if (per_tensor)
-      hipLaunchKernelGGL(gemm_prefill_asm_kernel<true>, grid, dim3(kPThreads), 0, st, a, ld_a,
-                         sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, (int)N, KB, tiles_m,
-                         tiles_n);
-    else
-      hipLaunchKernelGGL(gemm_prefill_asm_kernel<false>, grid, dim3(kPThreads), 0, st, a, ld_a,
-                         sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, (int)N, KB, tiles_m,
-                         tiles_n);
-    return hipGetLastError();
+    // 256 x 256 tiles unless they would occupy at most half of the CUs: then
+    // 256 x 128 tiles (twice the workgroups, one wave per SIMD)
+    const int64_t tiles256 = ((M + kPM - 1) / kPM) * ((N + kPN - 1) / kPN);
+    if (2 * tiles256 <= device_cus())
+      return launch_prefill_asm<4>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N, KB,
+                                   per_tensor, st);
+    return launch_prefill_asm<8>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N, KB,
+                                 per_tensor, st);
   }
   if (M > 64 && ld_a < kPrefillMaxLd && ld_w < kPrefillMaxLd) {
     const int tiles_m = (int)((M + kPM - 1) / kPM);

@@ -47,10 +47,31 @@ P0 = 208                          # six partial-product slots of 4 VGPRs
 SC0 = 232                         # eight activation scales (times the weight scale)
 SPREV = 240                       # scale of fragment 7 of the previous K step
 SWN = 241                         # weight scale of the next K step
-NUM_FIXED_VGPR = 242
+VCOPY = (242, 243)                # per-copy source offsets (alternating)
+NUM_FIXED_VGPR = 244
 # scalar scratch
-S_KB, S_DK, S_DK4, S_T = "s84", "s85", "s86", "s87"
-CLOBBER_SGPR = (84, 88)
+S_KB, S_DK, S_DK4, S_T, S_R = "s84", "s85", "s86", "s87", "s88"
+CLOBBER_SGPR = (84, 89)
+
+# Workgroup shapes: NW waves in a 2 x (NW / 2) grid of 128 x 64 wave tiles,
+# so the workgroup tile is 256 x (32 NW).  Copy t of wave w carries tile rows
+# 8 (w + NW t) .. + 7; the activation tile takes 32 / NW copies per wave, the
+# weight tile 4.
+SHAPES = (8, 4)
+
+
+def copies(nw):
+    """Order of one K block's copies: activation and weight interleaved."""
+    na = 32 // nw
+    a = [("A", t) for t in range(na)]
+    w = [("W", t) for t in range(4)]
+    out = []
+    for k in range(max(na, 4)):
+        if k < na:
+            out.append(a[k])
+        if k < 4:
+            out.append(w[k])
+    return out
 
 # partial-product slot of MFMA q (0..31) of a K step: every 5 consecutive
 # MFMAs (cyclically, across K steps) use distinct slots, so a partial is
@@ -127,12 +148,21 @@ def frag_read(prog, key, dst, base, off):
              f"ds_read_b128 {vr(dst + 4, 4)}, %[{base}] offset:{off + 16}")
 
 
-def dma_copy(prog, op, t, stage):
-    """Copy t (rows 8 (wave + 8 t) .. + 7) of operand op for K block S_DK into stage."""
-    base = (A_STAGE if op == "A" else W_STAGE)[stage] + t * 8192
+def dma_copy(prog, op, t, stage, nw, k):
+    """Copy t (tile rows 8 (wave + nw t) .. + 7) of operand op, K block S_DK,
+    into stage.  The row offset t * nw * 8 * ld is added to the lane's offset
+    in a VGPR (the descriptor's range check sees it: rows past M or N read
+    zero); the K offset is the scalar offset."""
+    base = (A_STAGE if op == "A" else W_STAGE)[stage] + t * nw * 1024
+    v = VCOPY[k % 2]
+    if t == 0:
+        prog.emit(f"v_mov_b32 v{v}, %[off{op}]")
+    else:
+        prog.emit(f"s_mul_i32 {S_R}, %[rs{op}], {t}",
+                  f"v_add_u32 v{v}, {S_R}, %[off{op}]")
     prog.emit(f"s_add_u32 m0, %[wave1k], {base}",
               "s_nop 0",
-              f"buffer_load_dwordx4 %[off{op}], %[d{op}{t}], {S_DK} offen lds")
+              f"buffer_load_dwordx4 v{v}, %[d{op}], {S_DK} offen lds")
 
 
 _label = [0]
@@ -184,7 +214,7 @@ def set_dk(prog, ahead):
               f"s_lshl_b32 {S_DK}, {S_DK}, 7")
 
 
-def gen_loop(block):
+def gen_loop(block, nw):
     """Steady-state K steps.  Returns the text of 2 x KB_GROUP consecutive
     steps as two halves (K blocks 0 .. 7 mod 8: LDS stages alternate every
     step, activation-scale group buffers every four), taken from the middle
@@ -245,11 +275,11 @@ def gen_loop(block):
             at(base + 12, mul_hi)
             if st % KB_GROUP == 1:
                 nbuf = (st // KB_GROUP + 1) % 2
-                at(base + 30, lambda nbuf=nbuf: dma_scale_group(prog, nbuf, "blk"))
-        # copies of K block kb + 2 into this step's stage (released at the barrier)
-        for k, (op, t) in enumerate([("A", 0), ("W", 0), ("A", 1), ("W", 1),
-                                     ("A", 2), ("W", 2), ("A", 3), ("W", 3)]):
-            at(base + 28 + k, lambda op=op, t=t, p=p: dma_copy(prog, op, t, p))
+                at(base + 30, lambda nbuf=nbuf: dma_scale_group(prog, nbuf, f"blk{nw}"))
+        # copies of K block kb + 2 into this step's stage (released at the
+        # barrier), one per slot from slot 28 on
+        for k, (op, t) in enumerate(copies(nw)):
+            at(base + 28 + k, lambda op=op, t=t, p=p, k=k: dma_copy(prog, op, t, p, nw, k))
 
     total = 32 * nsteps
     marks = {}
@@ -281,7 +311,7 @@ def gen_loop(block):
     return first, second, prog.max_out
 
 
-def gen_prologue(block):
+def gen_prologue(block, nw):
     # some scalar operands were just written by v_readfirstlane; VMEM reads of
     # an SGPR written by the VALU need wait states
     L = ["s_nop 7"]
@@ -297,13 +327,13 @@ def gen_prologue(block):
     prog = Program()
     prog.emit(*L)
     if block:
-        dma_scale_group(prog, 0, "pro", first=0)
+        dma_scale_group(prog, 0, f"pro{nw}", first=0)
     # K blocks 0 and 1 into stages 0 and 1
     for stage, ahead in ((0, 0), (1, 1)):
         set_dk(prog, ahead)
-        for op, t in [(o, t) for t in range(4) for o in ("A", "W")]:
-            dma_copy(prog, op, t, stage)
-    prog.emit("s_waitcnt vmcnt(8)", "s_barrier")
+        for k, (op, t) in enumerate(copies(nw)):
+            dma_copy(prog, op, t, stage, nw, k)
+    prog.emit(f"s_waitcnt vmcnt({len(copies(nw))})", "s_barrier")
     # leave S_DK on block 1: the first step re-issues the tail of that copy
     for i in range(4):
         frag_read(prog, None, fw(0, i), "rdW", i * 2048)
@@ -322,7 +352,7 @@ EP_PITCH = 144                    # bytes per staged output row (64 bf16 + 16 B 
 EP_HALF = 64 * EP_PITCH           # one wave's staging area: 64 rows
 
 
-def gen_epilogue(block, tag):
+def gen_epilogue(block, tag, nw):
     """Fold the last fragment, round to bf16 and store.  The wave's 128 x 64
     outputs go out in two halves of 64 rows, each staged through LDS so that
     a lane stores 16 contiguous bytes and an instruction covers eight whole
@@ -365,10 +395,10 @@ def gen_epilogue(block, tag):
           f"v_add_u32 v{vrd}, {s_reg}, v{vrd}",
           # store offset: row 128 wm + lane / 8, columns 64 wn + 8 (lane % 8)
           f"s_lshr_b32 {s_ldo2}, %[ldo16], 4",
-          f"s_lshr_b32 {s_uni}, %[wave], 2",
+          f"s_lshr_b32 {s_uni}, %[wave], {(nw // 2).bit_length() - 1}",
           f"s_mul_i32 {s_uni}, {s_uni}, 128",
           f"s_mul_i32 {s_uni}, {s_uni}, {s_ldo2}",
-          f"s_and_b32 {s_step}, %[wave], 3",
+          f"s_and_b32 {s_step}, %[wave], {nw // 2 - 1}",
           f"s_lshl_b32 {s_step}, {s_step}, 7",
           f"s_add_u32 {s_uni}, {s_uni}, {s_step}",
           f"v_lshrrev_b32 v{vt}, 3, v{vl}",
@@ -400,19 +430,19 @@ def gen_epilogue(block, tag):
     return L
 
 
-def gen(block):
+def gen(block, nw=8):
     """KB must be a positive multiple of KB_GROUP (the caller checks)."""
-    tag = "blk" if block else "pt"
+    tag = ("blk" if block else "pt") + str(nw)
     _label[0] = 0
-    first, second, max_out = gen_loop(block)
-    L = gen_prologue(block)
+    first, second, max_out = gen_loop(block, nw)
+    L = gen_prologue(block, nw)
     L.append(f"fp8pf_loop_{tag}:")
     L += first
     L += [f"s_cmp_eq_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_tail_{tag}"]
     L += second
     L += [f"s_cmp_lt_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_loop_{tag}"]
     L.append(f"fp8pf_tail_{tag}:")
-    L += gen_epilogue(block, tag)
+    L += gen_epilogue(block, tag, nw)
     return L, max_out
 
 
@@ -424,9 +454,9 @@ def main(path=OUT):
     out = ["// Generated by gen_prefill_asm.py; do not edit by hand.",
            "// K loop of gemm_prefill_kernel as gfx950 assembly (see that file).",
            "#pragma once", ""]
-    for block in (True, False):
-        lines, max_out = gen(block)
-        name = "FP8_PREFILL_ASM_BLOCK" if block else "FP8_PREFILL_ASM_TENSOR"
+    for nw, block in [(nw, b) for nw in SHAPES for b in (True, False)]:
+        lines, max_out = gen(block, nw)
+        name = ("FP8_PREFILL_ASM_BLOCK" if block else "FP8_PREFILL_ASM_TENSOR") + f"_W{nw}"
         out.append(f"// {len(lines)} lines; at most {max_out} LDS reads in flight")
         out.append(f"#define {name} \\")
         out.append(c_string(lines).replace("\n", " \\\n"))

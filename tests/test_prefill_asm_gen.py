@@ -29,10 +29,10 @@ def test_include_is_generator_output():
 
 def test_fixed_registers_and_lds_fit():
     g = _gen()
-    assert g.NUM_FIXED_VGPR + 12 <= 256          # fixed map plus the C++ operands
+    assert g.NUM_FIXED_VGPR + 11 <= 256          # fixed map plus the C++ operands
     assert g.LDS_BYTES <= 160 * 1024
-    for block in (True, False):
-        lines, max_out = g.gen(block)
+    for nw, block in [(nw, b) for nw in g.SHAPES for b in (True, False)]:
+        lines, max_out = g.gen(block, nw)
         assert max_out <= 15
         regs = [int(m) for l in lines for m in re.findall(r"\bv(\d+)\b", l)]
         regs += [int(b) for l in lines for a, b in re.findall(r"\bv\[(\d+):(\d+)\]", l)]
@@ -42,8 +42,8 @@ def test_fixed_registers_and_lds_fit():
 def test_every_lds_wait_names_a_smaller_count():
     # counts in s_waitcnt lgkmcnt(n) stay encodable (4 bits)
     g = _gen()
-    for block in (True, False):
-        lines, _ = g.gen(block)
+    for nw, block in [(nw, b) for nw in g.SHAPES for b in (True, False)]:
+        lines, _ = g.gen(block, nw)
         for l in lines:
             m = re.match(r"s_waitcnt lgkmcnt\((\d+)\)", l)
             if m:
