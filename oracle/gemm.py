@@ -14,7 +14,10 @@ list) the value of out[m, n] is
     C_kb[m, n] = sum_{k in block kb}  dec(qa[m, k]) * dec(qw[n, k])
 
 with W stored [N, K] (out = A . W^T).  Per-tensor scales give
-out = sA * sW * sum_k dec(qa[m, k]) * dec(qw[n, k]).
+out = sA * sW * sum_k dec(qa[m, k]) * dec(qw[n, k]); per-row scales (one per
+token, one per output channel; "[vLLM] FP8", scaling strategies, and "FP8
+Quantization", channel-wise weights) give
+out[m, n] = sA[m] * sW[n] * sum_k dec(qa[m, k]) * dec(qw[n, k]).
 
 Exactness: every decoded code is a multiple of 2**-9 with magnitude <= 448,
 so each product is a multiple of 2**-18 below 2**18 and a 128-term block sum
@@ -71,3 +74,22 @@ def gemm_tensor_ref(a_codes, a_scale, w_codes, w_scale):
     sa = float(np.asarray(a_scale, dtype=np.float32).reshape(-1)[0])
     sw = float(np.asarray(w_scale, dtype=np.float32).reshape(-1)[0])
     return (sa * sw) * (a @ w.T)
+
+
+def gemm_rows_ref(a_codes, a_row_scales, w_codes, w_row_scales):
+    """Per-row-scaled reference, float64 [M, N].
+
+    a_row_scales: float32, M values (one per activation row) or one value
+    for all rows; w_row_scales: float32, N values (one per weight row, i.e.
+    per output column) or one value.  out[m, n] = sa[m] * sw[n] * S[m, n],
+    S the exact full-K sum of decoded products.
+    """
+    a = e4m3.decode(np.asarray(a_codes, dtype=np.uint8))
+    w = e4m3.decode(np.asarray(w_codes, dtype=np.uint8))
+    M, N = a.shape[0], w.shape[0]
+    sa = np.asarray(a_row_scales, dtype=np.float32).astype(np.float64).reshape(-1)
+    sw = np.asarray(w_row_scales, dtype=np.float32).astype(np.float64).reshape(-1)
+    sa = np.broadcast_to(sa, (M,)) if sa.size == 1 else sa
+    sw = np.broadcast_to(sw, (N,)) if sw.size == 1 else sw
+    assert sa.shape == (M,) and sw.shape == (N,)
+    return (sa[:, None] * sw[None, :]) * (a @ w.T)

@@ -146,3 +146,27 @@ def test_tolerance_gate_and_floor():
     sc = tolerance.bf16_rne(ref * 1.01)
     sbits = torch.from_numpy(sc.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert not tolerance.check(sbits, ref)["frob_ok"]
+
+
+def test_exact_brute_force_rows():
+    # per-token x per-channel scales; M != N so a swapped scale vector fails
+    rng = np.random.default_rng(23)
+    a, _, w, _ = _random_operands(rng, 3, 128, 256)
+    sa = rng.uniform(0.1, 2.0, 3).astype(np.float32)
+    sw = rng.uniform(0.001, 0.1, 128).astype(np.float32)
+    ref = gemm.gemm_rows_ref(a, sa, w, sw)
+    assert ref.shape == (3, 128)
+    t = e4m3.decode_table()
+    for m in range(3):
+        for n in range(0, 128, 5):
+            s = sum(Fraction(float(t[a[m, k]])) * Fraction(float(t[w[n, k]])) for k in range(256))
+            e = float(Fraction(float(sa[m])) * Fraction(float(sw[n])) * s)
+            assert abs(ref[m, n] - e) <= 2 * np.spacing(abs(e) + 1e-300)
+
+
+def test_rows_broadcast_is_per_tensor():
+    rng = np.random.default_rng(24)
+    a, _, w, _ = _random_operands(rng, 4, 256, 384)
+    sa = np.array([0.25], dtype=np.float32)
+    sw = np.array([0.0625], dtype=np.float32)
+    assert np.array_equal(gemm.gemm_rows_ref(a, sa, w, sw), gemm.gemm_tensor_ref(a, sa, w, sw))

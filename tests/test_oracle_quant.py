@@ -203,3 +203,61 @@ def test_true_division_adversarial(golden_dir):
         want, ws = _brute_group(xf[i, :2])
         assert s[i, 0] == ws
         assert codes[i, :2].tolist() == want, pairs[i]
+
+
+def test_rows_brute_force_small():
+    # per-row quantization: each row is its own group (brute force per row)
+    rng = np.random.default_rng(14)
+    x = (rng.standard_normal((5, 384)) * 1.5).astype(np.float32)
+    x[1, 17] = 99.0
+    x[3, :] = 0.0
+    x[3, 5] = -0.0
+    bits = f32_bits_to_bf16(x)
+    codes, s = quant.quant_rows_ref(bits)
+    assert codes.shape == (5, 384) and s.shape == (5,)
+    xf = quant.bf16_bits_to_f32(bits)
+    for r in range(5):
+        want, ws = _brute_group(xf[r])
+        assert s[r] == ws
+        assert codes[r].tolist() == want
+
+
+def test_rows_special_cases_reduce_to_pinned_quantizers():
+    rng = np.random.default_rng(15)
+    x = f32_bits_to_bf16((rng.standard_normal((6, 128)) * 3).astype(np.float32))
+    # K = 128: one row is one 1x128 group
+    c_rows, s_rows = quant.quant_rows_ref(x)
+    c_act, s_act = quant.quant_act_ref(x)
+    assert np.array_equal(c_rows, c_act) and np.array_equal(s_rows, s_act[:, 0])
+    # one row: the whole tensor
+    y = f32_bits_to_bf16((rng.standard_normal((1, 640)) * 0.1).astype(np.float32))
+    c1, s1 = quant.quant_rows_ref(y)
+    c2, s2 = quant.quant_tensor_ref(y)
+    assert np.array_equal(c1, c2) and s1[0] == s2[0]
+
+
+def test_static_equals_dynamic_at_the_dynamic_scale():
+    rng = np.random.default_rng(16)
+    x = f32_bits_to_bf16((rng.standard_normal((7, 256)) * 2).astype(np.float32))
+    c_dyn, s_dyn = quant.quant_tensor_ref(x)
+    assert np.array_equal(quant.quant_static_ref(x, s_dyn), c_dyn)
+
+
+def test_static_brute_force_and_saturation():
+    rng = np.random.default_rng(17)
+    xf = (rng.standard_normal(300) * 4).astype(np.float32)
+    bits = f32_bits_to_bf16(xf)
+    xf = quant.bf16_bits_to_f32(bits)
+    s = np.float32(0.0123)           # values up to ~16 / 0.0123 = 1300: many saturate
+    got = quant.quant_static_ref(bits, s)
+    t = e4m3.decode_table()
+    for v, c in zip(xf.tolist(), got.tolist()):
+        q = float(np.float32(v / float(s)))          # fp64 divide rounded once to fp32
+        a = min(abs(q), 448.0)
+        best, bd = 0, None
+        for k in range(0x7F):
+            d = abs(t[k] - a)
+            if bd is None or d < bd or (d == bd and k % 2 == 0):
+                best, bd = k, d
+        assert c == (best | (0x80 if math.copysign(1.0, q) < 0 else 0))
+    assert np.any(got & 0x7F == 0x7E)                 # some saturated to 448
