@@ -19,12 +19,13 @@ LIB_PATH = os.path.join(_PKG, "libfp8w8a8.so")
 FP8_OK = 0
 SCALE_BLOCK = 0
 SCALE_TENSOR = 1
+SCALE_ROW = 2
 OP_QUANT_ACT = 0
 OP_QUANT_WEIGHT = 1
 OP_GEMM = 2
 OP_LINEAR = 3
 
-_MODES = {"block": SCALE_BLOCK, "tensor": SCALE_TENSOR}
+_MODES = {"block": SCALE_BLOCK, "tensor": SCALE_TENSOR, "row": SCALE_ROW}
 
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
@@ -48,6 +49,8 @@ _SIGS = {
     "fp8_e4m3_encode_f32": (_int, [_vp, _i64, _vp, _vp]),
     "fp8_linear": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp,
                           _sz, _vp]),
+    "fp8_quant_act_static": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "fp8_validate_quant_act_static": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp]),
 }
 
 _lib = None
@@ -108,6 +111,11 @@ def _ld(t):
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
+def _vec_ld(t):
+    """Element stride of a row-mode scale vector; a single value is stride 0."""
+    return 0 if t.numel() == 1 else t.stride(0)
+
+
 def workspace_bytes(op, M, N, K, scale_mode):
     return int(lib().fp8_workspace_bytes(int(op), int(M), int(N), int(K), _mode(scale_mode)))
 
@@ -115,7 +123,8 @@ def workspace_bytes(op, M, N, K, scale_mode):
 def quant_act(x, scale_mode="block", workspace=None, q=None, scales=None):
     """Dynamic activation quantization of bf16 x [M, K] -> (codes uint8 [M, K], scales fp32).
 
-    Block mode gives scales [M, K/128]; tensor mode a 1-element tensor.
+    Block mode gives scales [M, K/128]; row (per-token) mode [M]; tensor mode
+    a 1-element tensor.
     """
     mode = _mode(scale_mode)
     M, K, ld_x = _rows(x, torch.bfloat16, "x")
@@ -123,9 +132,9 @@ def quant_act(x, scale_mode="block", workspace=None, q=None, scales=None):
         if q is None:
             q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
         if scales is None:
-            shape = (M, K // 128) if mode == SCALE_BLOCK else (1,)
+            shape = (M, K // 128) if mode == SCALE_BLOCK else (M,) if mode == SCALE_ROW else (1,)
             scales = torch.empty(shape, dtype=torch.float32, device=x.device)
-        ld_s = _ld(scales)
+        ld_s = scales.stride(0) if mode == SCALE_ROW and scales.dim() == 1 else _ld(scales)
         ld_q = q.stride(0) if q.shape[0] > 1 else q.shape[1]
         nws = workspace_bytes(OP_QUANT_ACT, M, 0, K, mode)
         if nws and workspace is None:
@@ -138,7 +147,11 @@ def quant_act(x, scale_mode="block", workspace=None, q=None, scales=None):
 
 
 def quant_weight_block(w, scale_mode="block", block_n=128, block_k=128, workspace=None):
-    """Weight quantization of bf16 w [N, K] -> (codes uint8 [N, K], scales fp32 [N/128, K/128])."""
+    """Weight quantization of bf16 w [N, K] -> (codes uint8 [N, K], scales fp32).
+
+    Block mode gives scales [N/128, K/128]; row (per-channel) mode [N];
+    tensor mode a 1-element tensor.
+    """
     mode = _mode(scale_mode)
     N, K, ld_w = _rows(w, torch.bfloat16, "w")
     with torch.cuda.device(w.device):
@@ -146,6 +159,9 @@ def quant_weight_block(w, scale_mode="block", block_n=128, block_k=128, workspac
         if mode == SCALE_BLOCK:
             scales = torch.empty((max(N // 128, 0), K // 128), dtype=torch.float32, device=w.device)
             ld_s = _ld(scales)
+        elif mode == SCALE_ROW:
+            scales = torch.empty((N,), dtype=torch.float32, device=w.device)
+            ld_s = 1
         else:
             scales = torch.empty((1,), dtype=torch.float32, device=w.device)
             ld_s = 1
@@ -170,8 +186,10 @@ def block_gemm(a_q, a_s, w_q, w_s, scale_mode="block", out=None):
     for t, nm in ((a_s, "a_s"), (w_s, "w_s")):
         if t.dtype != torch.float32 or not t.is_cuda:
             raise TypeError(f"{nm} must be a float32 device tensor")
-    ld_as = _ld(a_s)
-    ld_ws = _ld(w_s)
+    if mode == SCALE_ROW:
+        ld_as, ld_ws = _vec_ld(a_s.reshape(-1)), _vec_ld(w_s.reshape(-1))
+    else:
+        ld_as, ld_ws = _ld(a_s), _ld(w_s)
     with torch.cuda.device(a_q.device):
         if out is None:
             out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
@@ -186,8 +204,9 @@ def linear(x, w_q, w_s, scale_mode="block", out=None, workspace=None):
     """One W8A8 linear call in one library call: out = GEMM(quant_act(x), W).
 
     Bit-identical to quant_act followed by block_gemm.  Block scales with
-    M <= 16 run fused (no workspace); otherwise a workspace is used (allocated
-    here unless given).
+    M <= 4 run fused (no workspace); otherwise a workspace is used (allocated
+    here unless given).  Row mode: per-token activation scales, per-channel
+    weight scales w_s [N] (or one value).
     """
     mode = _mode(scale_mode)
     M, K, ld_x = _rows(x, torch.bfloat16, "x")
@@ -205,9 +224,25 @@ def linear(x, w_q, w_s, scale_mode="block", out=None, workspace=None):
             workspace = torch.empty(nws, dtype=torch.uint8, device=x.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        _check(lib().fp8_linear(x.data_ptr(), ld_x, w_q.data_ptr(), ld_w, w_s.data_ptr(), _ld(w_s),
+        ld_ws = _vec_ld(w_s.reshape(-1)) if mode == SCALE_ROW else _ld(w_s)
+        _check(lib().fp8_linear(x.data_ptr(), ld_x, w_q.data_ptr(), ld_w, w_s.data_ptr(), ld_ws,
                                 out.data_ptr(), ld_out, M, N, K, mode, ws_ptr, ws_len, _stream(x)))
     return out
+
+
+def quant_act_static(x, scale, q=None):
+    """Static activation quantization of bf16 x [M, K] with a calibrated
+    scale (a 1-element float32 device tensor) -> codes uint8 [M, K]."""
+    M, K, ld_x = _rows(x, torch.bfloat16, "x")
+    if scale.dtype != torch.float32 or not scale.is_cuda or scale.numel() != 1:
+        raise TypeError("scale must be a 1-element float32 device tensor")
+    with torch.cuda.device(x.device):
+        if q is None:
+            q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        ld_q = q.stride(0) if q.shape[0] > 1 else q.shape[1]
+        _check(lib().fp8_quant_act_static(x.data_ptr(), M, K, ld_x, q.data_ptr(), ld_q,
+                                          scale.data_ptr(), _stream(x)))
+    return q
 
 
 def encode_f32(x):

@@ -30,10 +30,15 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 bool shape_ok_kn(int64_t K) { return K > 0 && K % 128 == 0 && K < kMaxDim; }
 
+bool mode_ok(int scale_mode) {
+  return scale_mode == FP8_SCALE_BLOCK || scale_mode == FP8_SCALE_TENSOR ||
+         scale_mode == FP8_SCALE_ROW;
+}
+
 fp8_status validate_quant(const uint16_t* x, int64_t R, int64_t K, int64_t ld_x,
                           const uint8_t* q, int64_t ld_q, const float* scales, int64_t ld_s,
                           int scale_mode, const void* ws, size_t ws_bytes, bool rows_blocked) {
-  if (scale_mode != FP8_SCALE_BLOCK && scale_mode != FP8_SCALE_TENSOR) return FP8_ERR_SCHEME;
+  if (!mode_ok(scale_mode)) return FP8_ERR_SCHEME;
   if (R < 0 || R >= kMaxDim || !shape_ok_kn(K)) return FP8_ERR_SHAPE;
   if (rows_blocked && scale_mode == FP8_SCALE_BLOCK && R % 128 != 0) return FP8_ERR_SHAPE;
   if (R > 0 && R * K > kMaxElems) return FP8_ERR_SHAPE;
@@ -42,11 +47,13 @@ fp8_status validate_quant(const uint16_t* x, int64_t R, int64_t K, int64_t ld_x,
   const int64_t groups = K / 128;
   if (ld_x < K || ld_q < K) return FP8_ERR_STRIDE;
   if (scale_mode == FP8_SCALE_BLOCK && ld_s < groups) return FP8_ERR_STRIDE;
+  if (scale_mode == FP8_SCALE_ROW && ld_s < 1) return FP8_ERR_STRIDE;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4)) return FP8_ERR_ALIGN;
   if (ld_x % 8 != 0 || ld_q % 16 != 0) return FP8_ERR_ALIGN;
-  const int64_t srows = scale_mode == FP8_SCALE_BLOCK ? (rows_blocked ? R / 128 : R) : 1;
+  const int64_t srows = scale_mode == FP8_SCALE_BLOCK ? (rows_blocked ? R / 128 : R)
+                        : scale_mode == FP8_SCALE_ROW ? R : 1;
   const int64_t scols = scale_mode == FP8_SCALE_BLOCK ? groups : 1;
-  const int64_t sld = scale_mode == FP8_SCALE_BLOCK ? ld_s : 1;
+  const int64_t sld = scale_mode == FP8_SCALE_TENSOR ? 1 : ld_s;
   Range rx = range_of(x, R, K, ld_x, 2), rq = range_of(q, R, K, ld_q, 1);
   Range rs = range_of(scales, srows, scols, sld, 4);
   if (overlap(rx, rq) || overlap(rx, rs) || overlap(rq, rs)) return FP8_ERR_ALIAS;
@@ -59,11 +66,16 @@ fp8_status validate_quant(const uint16_t* x, int64_t R, int64_t K, int64_t ld_x,
   return FP8_OK;
 }
 
+// Scale vectors of the row mode: n entries at stride ld (ld = 0: one entry).
+Range row_scales(const float* p, int64_t n, int64_t ld) {
+  return ld == 0 ? range_of(p, 1, 1, 1, 4) : range_of(p, n, 1, ld, 4);
+}
+
 fp8_status validate_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, int64_t ld_as,
                          const uint8_t* w_q, int64_t ld_w, const float* w_s, int64_t ld_ws,
                          const uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
                          int scale_mode) {
-  if (scale_mode != FP8_SCALE_BLOCK && scale_mode != FP8_SCALE_TENSOR) return FP8_ERR_SCHEME;
+  if (!mode_ok(scale_mode)) return FP8_ERR_SCHEME;
   if (M < 0 || M >= kMaxDim || !shape_ok_kn(K) || !shape_ok_kn(N)) return FP8_ERR_SHAPE;
   if (M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems) return FP8_ERR_SHAPE;
   if (M == 0) return FP8_OK;
@@ -71,13 +83,19 @@ fp8_status validate_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, int
   const int64_t KB = K / 128;
   if (ld_a < K || ld_w < K || ld_out < N) return FP8_ERR_STRIDE;
   if (scale_mode == FP8_SCALE_BLOCK && (ld_as < KB || ld_ws < KB)) return FP8_ERR_STRIDE;
+  if (scale_mode == FP8_SCALE_ROW && (ld_as < 0 || ld_ws < 0 || ld_as >= kMaxDim ||
+                                      ld_ws >= kMaxDim))
+    return FP8_ERR_STRIDE;
   if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(out, 16)) return FP8_ERR_ALIGN;
   if (!aligned(a_s, 4) || !aligned(w_s, 4)) return FP8_ERR_ALIGN;
   if (ld_a % 16 != 0 || ld_w % 16 != 0 || ld_out % 8 != 0) return FP8_ERR_ALIGN;
   Range ro = range_of(out, M, N, ld_out, 2);
   Range ra = range_of(a_q, M, K, ld_a, 1), rw = range_of(w_q, N, K, ld_w, 1);
-  Range ras = scale_mode == FP8_SCALE_BLOCK ? range_of(a_s, M, KB, ld_as, 4) : range_of(a_s, 1, 1, 1, 4);
+  Range ras = scale_mode == FP8_SCALE_BLOCK ? range_of(a_s, M, KB, ld_as, 4)
+              : scale_mode == FP8_SCALE_ROW ? row_scales(a_s, M, ld_as)
+                                            : range_of(a_s, 1, 1, 1, 4);
   Range rws = scale_mode == FP8_SCALE_BLOCK ? range_of(w_s, N / 128, KB, ld_ws, 4)
+              : scale_mode == FP8_SCALE_ROW ? row_scales(w_s, N, ld_ws)
                                             : range_of(w_s, 1, 1, 1, 4);
   if (overlap(ro, ra) || overlap(ro, rw) || overlap(ro, ras) || overlap(ro, rws)) return FP8_ERR_ALIAS;
   return FP8_OK;
@@ -103,8 +121,9 @@ fp8_status check_device() {
 fp8_status launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH; }
 
 // Workspace of the unfused fp8_linear path: activation codes [M, ld = K
-// rounded up to 16], then the scales (block: [M, K/128]; tensor: one float),
-// then the per-tensor partials.  Every piece starts 256-byte aligned.
+// rounded up to 16], then the scales (block: [M, K/128]; row: [M]; tensor:
+// one float), then the per-tensor partials.  Every piece starts 256-byte
+// aligned.
 struct LinearLayout {
   size_t codes, scales, partials, total;
   int64_t ld_q;
@@ -115,7 +134,9 @@ LinearLayout linear_layout(int64_t M, int64_t K, int scale_mode) {
   l.ld_q = (K + 15) / 16 * 16;
   l.codes = 0;
   l.scales = align256((size_t)M * (size_t)l.ld_q);
-  const size_t nscales = scale_mode == FP8_SCALE_BLOCK ? (size_t)M * (size_t)(K / 128) : 1;
+  const size_t nscales = scale_mode == FP8_SCALE_BLOCK ? (size_t)M * (size_t)(K / 128)
+                         : scale_mode == FP8_SCALE_ROW  ? (size_t)M
+                                                        : 1;
   l.partials = align256(l.scales + nscales * sizeof(float));
   l.total = scale_mode == FP8_SCALE_TENSOR
                 ? l.partials + (size_t)fp8k::kTensorPartials * sizeof(uint32_t)
@@ -193,6 +214,8 @@ fp8_status fp8_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, 
   hipStream_t s = (hipStream_t)stream;
   if (scale_mode == FP8_SCALE_BLOCK)
     return launched(fp8k::launch_quant_act_block(x, M, K, ld_x, q, ld_q, scales, ld_s, s));
+  if (scale_mode == FP8_SCALE_ROW)
+    return launched(fp8k::launch_quant_rows(x, M, K, ld_x, q, ld_q, scales, ld_s, s));
   return launched(fp8k::launch_quant_tensor(x, M, K, ld_x, q, ld_q, scales,
                                             (uint32_t*)workspace, s));
 }
@@ -208,6 +231,8 @@ fp8_status fp8_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64
   hipStream_t s = (hipStream_t)stream;
   if (scale_mode == FP8_SCALE_BLOCK)
     return launched(fp8k::launch_quant_weight_block(w, N, K, ld_w, q, ld_q, scales, ld_s, s));
+  if (scale_mode == FP8_SCALE_ROW)
+    return launched(fp8k::launch_quant_rows(w, N, K, ld_w, q, ld_q, scales, ld_s, s));
   return launched(fp8k::launch_quant_tensor(w, N, K, ld_w, q, ld_q, scales,
                                             (uint32_t*)workspace, s));
 }
@@ -221,15 +246,18 @@ fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, in
                                 K, scale_mode);
   if (st != FP8_OK || M == 0) return st;
   if ((st = check_device()) != FP8_OK) return st;
-  return launched(fp8k::launch_gemm(a_q, ld_a, a_s, ld_as, w_q, ld_w, w_s, ld_ws, out, ld_out, M,
-                                    N, K, scale_mode == FP8_SCALE_TENSOR, (hipStream_t)stream));
+  const bool kconst = scale_mode != FP8_SCALE_BLOCK;
+  const bool tensor = scale_mode == FP8_SCALE_TENSOR;
+  return launched(fp8k::launch_gemm(a_q, ld_a, a_s, tensor ? 0 : ld_as, w_q, ld_w, w_s,
+                                    tensor ? 0 : ld_ws, out, ld_out, M, N, K, kconst,
+                                    (hipStream_t)stream));
 }
 
 fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
                       const float* w_s, int64_t ld_ws, uint16_t* out, int64_t ld_out,
                       int64_t M, int64_t N, int64_t K, int scale_mode, void* workspace,
                       size_t ws_bytes, void* stream) {
-  if (scale_mode != FP8_SCALE_BLOCK && scale_mode != FP8_SCALE_TENSOR) return FP8_ERR_SCHEME;
+  if (!mode_ok(scale_mode)) return FP8_ERR_SCHEME;
   if (M < 0 || M >= kMaxDim || !shape_ok_kn(K) || !shape_ok_kn(N)) return FP8_ERR_SHAPE;
   if (M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems) return FP8_ERR_SHAPE;
   if (M == 0) return FP8_OK;
@@ -237,12 +265,14 @@ fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
   const int64_t KB = K / 128;
   if (ld_x < K || ld_w < K || ld_out < N) return FP8_ERR_STRIDE;
   if (scale_mode == FP8_SCALE_BLOCK && ld_ws < KB) return FP8_ERR_STRIDE;
+  if (scale_mode == FP8_SCALE_ROW && (ld_ws < 0 || ld_ws >= kMaxDim)) return FP8_ERR_STRIDE;
   if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(out, 16) || !aligned(w_s, 4))
     return FP8_ERR_ALIGN;
   if (ld_x % 8 != 0 || ld_w % 16 != 0 || ld_out % 8 != 0) return FP8_ERR_ALIGN;
   Range ro = range_of(out, M, N, ld_out, 2);
   Range rx = range_of(x, M, K, ld_x, 2), rw = range_of(w_q, N, K, ld_w, 1);
   Range rws = scale_mode == FP8_SCALE_BLOCK ? range_of(w_s, N / 128, KB, ld_ws, 4)
+              : scale_mode == FP8_SCALE_ROW ? row_scales(w_s, N, ld_ws)
                                             : range_of(w_s, 1, 1, 1, 4);
   if (overlap(ro, rx) || overlap(ro, rw) || overlap(ro, rws)) return FP8_ERR_ALIAS;
   const bool fused = scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, K);
@@ -265,12 +295,39 @@ fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
   hipError_t e;
   if (scale_mode == FP8_SCALE_BLOCK)
     e = fp8k::launch_quant_act_block(x, M, K, ld_x, q, lay.ld_q, sa, KB, s);
+  else if (scale_mode == FP8_SCALE_ROW)
+    e = fp8k::launch_quant_rows(x, M, K, ld_x, q, lay.ld_q, sa, 1, s);
   else
     e = fp8k::launch_quant_tensor(x, M, K, ld_x, q, lay.ld_q, sa, (uint32_t*)(ws8 + lay.partials),
                                   s);
   if (e != hipSuccess) return FP8_ERR_LAUNCH;
-  return launched(fp8k::launch_gemm(q, lay.ld_q, sa, KB, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N,
-                                    K, scale_mode == FP8_SCALE_TENSOR, s));
+  const int64_t lsa = scale_mode == FP8_SCALE_BLOCK ? KB : scale_mode == FP8_SCALE_ROW ? 1 : 0;
+  const int64_t lsw = scale_mode == FP8_SCALE_TENSOR ? 0 : ld_ws;
+  return launched(fp8k::launch_gemm(q, lay.ld_q, sa, lsa, w_q, ld_w, w_s, lsw, out, ld_out, M, N,
+                                    K, scale_mode != FP8_SCALE_BLOCK, s));
+}
+
+fp8_status fp8_validate_quant_act_static(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                         const uint8_t* q, int64_t ld_q, const float* scale) {
+  if (M < 0 || M >= kMaxDim || !shape_ok_kn(K)) return FP8_ERR_SHAPE;
+  if (M > 0 && M * K > kMaxElems) return FP8_ERR_SHAPE;
+  if (M == 0) return FP8_OK;
+  if (!x || !q || !scale) return FP8_ERR_NULL;
+  if (ld_x < K || ld_q < K) return FP8_ERR_STRIDE;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return FP8_ERR_ALIGN;
+  if (ld_x % 8 != 0 || ld_q % 16 != 0) return FP8_ERR_ALIGN;
+  Range rx = range_of(x, M, K, ld_x, 2), rq = range_of(q, M, K, ld_q, 1);
+  Range rs = range_of(scale, 1, 1, 1, 4);
+  if (overlap(rx, rq) || overlap(rq, rs)) return FP8_ERR_ALIAS;
+  return FP8_OK;
+}
+
+fp8_status fp8_quant_act_static(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* q,
+                                int64_t ld_q, const float* scale, void* stream) {
+  fp8_status st = fp8_validate_quant_act_static(x, M, K, ld_x, q, ld_q, scale);
+  if (st != FP8_OK || M == 0) return st;
+  if ((st = check_device()) != FP8_OK) return st;
+  return launched(fp8k::launch_quant_static(x, M, K, ld_x, q, ld_q, scale, (hipStream_t)stream));
 }
 
 fp8_status fp8_e4m3_encode_f32(const float* x, int64_t n, uint8_t* codes, void* stream) {

@@ -96,12 +96,12 @@ __device__ __forceinline__ v8i zero8() {
 constexpr int kFrag = 2048;                   // 16 rows x 128 bytes
 
 template <int KSPLIT, int KBW>
-constexpr size_t decode_lds_bytes(int KB, bool per_tensor) {
+constexpr size_t decode_lds_bytes(int KB, bool kconst) {
   return (size_t)KSPLIT * KBW * 2 * kFrag + (size_t)KSPLIT * 4 * 64 * sizeof(float) +
-         (per_tensor ? 0 : (size_t)16 * KB * sizeof(float));
+         (kconst ? 0 : (size_t)16 * KB * sizeof(float));
 }
 
-template <int KSPLIT, int KBW, bool PER_TENSOR>
+template <int KSPLIT, int KBW, bool KCONST>
 __global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
     const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
   };
 
   if (kb_lo < kb_hi) issue(kb_lo);
-  if (!PER_TENSOR) {
+  if (!KCONST) {
     // s_as[kb * 16 + m] = sa[m, kb] (rows >= M read 0); queued behind the
     // first batch's loads
     for (int i = threadIdx.x; i < KB * 16; i += 64 * KSPLIT) {
@@ -190,10 +190,10 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
     for (int u = 0; u < KBW; ++u) {
       const int kb = kb0 + u;
       const int kbc = min(kb, kb_hi - 1);
-      const float s_w = PER_TENSOR ? 0.f : sw[(int64_t)(n0 >> 7) * ld_sw + kbc];
+      const float s_w = KCONST ? 0.f : sw[(int64_t)(n0 >> 7) * ld_sw + kbc];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float s_a = PER_TENSOR ? 0.f : s_as[kbc * 16 + 4 * kg + i];
+        const float s_a = KCONST ? 0.f : s_as[kbc * 16 + 4 * kg + i];
         sc[u][i] = kb < kb_hi ? s_a * s_w : 0.f;
       }
     }
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
       const bool ok = arow && (kb0 + u < kb_hi);
 #pragma unroll
       for (int e = 0; e < 8; ++e) av[u][e] = ok ? av[u][e] : 0;
-      if (PER_TENSOR) {
+      if (KCONST) {
         acc = mfma_fp8(av[u], bw[u], acc);
       } else {
         v4f p = mfma_fp8(av[u], bw[u], v4f{0.f, 0.f, 0.f, 0.f});
@@ -217,15 +217,16 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
   for (int i = 0; i < 4; ++i) red[(wave * 4 + i) * 64 + lane] = acc[i];
   __syncthreads();
   if (wave == 0) {
-    const float st = PER_TENSOR ? sa[0] * sw[0] : 1.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float v = 0.f;
 #pragma unroll
       for (int s2 = 0; s2 < KSPLIT; ++s2) v += red[(s2 * 4 + i) * 64 + lane];
-      if (PER_TENSOR) v *= st;
       const int m = 4 * kg + i;
-      if (m < M) out[(int64_t)m * ld_out + n0 + r16] = (uint16_t)f32_to_bf16_rne(v);
+      if (m < M) {
+        if (KCONST) v *= sa[(int64_t)m * ld_sa] * sw[(n0 + r16) * ld_sw];
+        out[(int64_t)m * ld_out + n0 + r16] = (uint16_t)f32_to_bf16_rne(v);
+      }
     }
   }
 }
@@ -239,7 +240,7 @@ constexpr int kBM = 128;
 constexpr int kBN = 128;
 constexpr int kLdsRow = 144;
 
-template <bool PER_TENSOR>
+template <bool KCONST>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
     const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
       if (m0 + crow + 32 * p >= M) ra[p] = make_uint4(0, 0, 0, 0);
     }
     float s_a_ld = 0.f;
-    if (!PER_TENSOR && tid < kBM) {
+    if (!KCONST && tid < kBM) {
       const int64_t gm = m0 + tid;
       s_a_ld = gm < M ? sa[gm * ld_sa + kb] : 0.f;
     }
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
       *reinterpret_cast<uint4*>(lds_a + r * kLdsRow + cchunk * 16) = ra[p];
       *reinterpret_cast<uint4*>(lds_w + r * kLdsRow + cchunk * 16) = rw[p];
     }
-    if (!PER_TENSOR && tid < kBM) lds_sa[tid] = s_a_ld;
+    if (!KCONST && tid < kBM) lds_sa[tid] = s_a_ld;
     __syncthreads();
 
     v8i fa[4], fb[4];
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) fb[j] = load32(lds_w + (wn * 64 + j * 16 + r16) * kLdsRow + kg * 32);
 
-    if (PER_TENSOR) {
+    if (KCONST) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -332,7 +333,6 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
     }
   }
 
-  const float st = PER_TENSOR ? sa[0] * sw[0] : 1.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -341,9 +341,10 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
       if (gm < M) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          const int64_t gn = n0 + wn * 64 + j * 16 + r16;
           float v = acc[i][j][r];
-          if (PER_TENSOR) v *= st;
-          out[gm * ld_out + n0 + wn * 64 + j * 16 + r16] = (uint16_t)f32_to_bf16_rne(v);
+          if (KCONST) v *= sa[gm * ld_sa] * sw[gn * ld_sw];
+          out[gm * ld_out + gn] = (uint16_t)f32_to_bf16_rne(v);
         }
       }
     }
@@ -409,7 +410,7 @@ __device__ __forceinline__ int sc_index(int blk, int t) {
   return ((blk * kPWavesM + wm) * 16 + j) * kPMF + mf;
 }
 
-template <bool PER_TENSOR>
+template <bool KCONST>
 __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
     const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
     for (int t = 0; t < kCopies; ++t) issue_part(kb, t, adst, bdst);
   };
   // activation scale of tile row tid (threads 0 .. 255), 0 past M
-  const bool sa_thread = !PER_TENSOR && tid < kPM;
+  const bool sa_thread = !KCONST && tid < kPM;
   const float* sa_row = sa + min<int64_t>(m0 + tid, (int64_t)M - 1) * ld_sa;
   const bool sa_valid = m0 + tid < M;
   const int nb0 = (int)(n0 >> 7);
@@ -526,7 +527,7 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
     v8i fw[kPNF];
 #pragma unroll
     for (int i = 0; i < kPNF; ++i) fw[i] = frag(bt + i * 16 * 128);
-    if (PER_TENSOR) {
+    if (KCONST) {
       v8i fa = frag(at);
 #pragma unroll
       for (int j = 0; j < kPMF; ++j) {
@@ -574,7 +575,6 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
   }
 
   // epilogue: lane writes 4 adjacent bf16 of token row m per weight fragment
-  const float st = PER_TENSOR ? sa[0] * sw[0] : 1.0f;
 #pragma unroll
   for (int j = 0; j < kPMF; ++j) {
     const int64_t gm = m0 + wm * kPWM + j * 16 + r16;
@@ -585,7 +585,8 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
         if (gn < N) {
           float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = PER_TENSOR ? acc[i][j][r] * st : acc[i][j][r];
+          for (int r = 0; r < 4; ++r)
+            v[r] = KCONST ? acc[i][j][r] * (sa[gm * ld_sa] * sw[(gn + r) * ld_sw]) : acc[i][j][r];
           const uint2 packed = make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
                                           f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
           *reinterpret_cast<uint2*>(out + gm * ld_out + gn) = packed;
@@ -677,7 +678,7 @@ __device__ __forceinline__ v4i pf_desc(const void* base, int64_t bytes) {
 // NW = 8: 256 x 256 tiles, two waves per SIMD.  NW = 4: 256 x 128 tiles, one
 // wave per SIMD, for grids that would otherwise leave CUs idle (the same
 // 128 x 64 wave tile, so the K loop is the same schedule).
-template <bool PER_TENSOR, int NW>
+template <bool KCONST, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
     const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
@@ -756,7 +757,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   const v4i dOut = pf_desc(out + m0 * ld_out + n0, ((int64_t)M - m0) * ld_out * 2 - n0 * 2);
   const uint32_t ldo16 = pf_uni((uint32_t)(16 * ld_out * 2));
   const int colok = pf_uni((n0 + wn * kPWN < N) ? 1 : 0);
-  const int st = pf_uni(__builtin_bit_cast(int, PER_TENSOR ? sa[0] * sw[0] : 1.0f));
+  // scales constant along K: row scale sa[m * ld_sa], column scale
+  // sw[n * ld_sw] (strides 0: one scale each); the lane's rows are
+  // 128 wm + 16 j + r16, its columns 64 wn + 16 i + 4 kg + r
+  const v4i dSaR = pf_desc(sa + m0 * ld_sa, (((int64_t)M - m0 - 1) * ld_sa + 1) * 4);
+  const v4i dSwR = pf_desc(sw + n0 * ld_sw, (((int64_t)N - n0 - 1) * ld_sw + 1) * 4);
+  const uint32_t offSaR = (uint32_t)((wm * kPWM + r16) * ld_sa * 4);
+  const uint32_t offSwR = (uint32_t)((wn * kPWN + 4 * kg) * ld_sw * 4);
+  const uint32_t sjA = pf_uni((uint32_t)(16 * ld_sa * 4));
+  const uint32_t siW = pf_uni((uint32_t)(16 * ld_sw * 4));
+  const uint32_t srW = pf_uni((uint32_t)(ld_sw * 4));
   const int kb = pf_uni(KB);
   const int kbm1 = pf_uni(KB - 1);
   const int kbm4 = pf_uni(KB - kPfKbGroup);
@@ -768,20 +778,23 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
       [dW] "s"(dW), [rsA] "s"(rsA), [rsW] "s"(rsW), [dOut] "s"(dOut), [wave1k] "s"(wave1k),     \
       [kb] "s"(kb), [kbm1] "s"(kbm1), [ldo16] "s"(ldo16), [colok] "s"(colok),                  \
       [wave] "s"(wave_s), [ldsb] "s"(ldsb)
+#define FP8_PF_KCONST_OPERANDS                                                                  \
+  [offSaR] "v"(offSaR), [offSwR] "v"(offSwR), [dSaR] "s"(dSaR), [dSwR] "s"(dSwR),               \
+      [sjA] "s"(sjA), [siW] "s"(siW), [srW] "s"(srW)
 #define FP8_PF_BLOCK_OPERANDS                                                                   \
   [offSa] "v"(offSa), [scL0] "v"(scL0), [scH0] "v"(scH0), [scL1] "v"(scL1), [scH1] "v"(scH1),  \
       [offSw] "v"(offSw), [dSa] "s"(dSa), [dSw] "s"(dSw), [sam0] "s"(sam0), [wsa] "s"(wsa),     \
       [swm0] "s"(swm0), [kbm4] "s"(kbm4)
-  if (PER_TENSOR) {
+  if (KCONST) {
     if (NW == 8)
       asm volatile(FP8_PREFILL_ASM_TENSOR_W8
                    : [swrd] "+v"(swrd)
-                   : FP8_PF_COMMON_OPERANDS, [st] "s"(st)
+                   : FP8_PF_COMMON_OPERANDS, FP8_PF_KCONST_OPERANDS
                    : FP8_PREFILL_ASM_CLOBBERS);
     else
       asm volatile(FP8_PREFILL_ASM_TENSOR_W4
                    : [swrd] "+v"(swrd)
-                   : FP8_PF_COMMON_OPERANDS, [st] "s"(st)
+                   : FP8_PF_COMMON_OPERANDS, FP8_PF_KCONST_OPERANDS
                    : FP8_PREFILL_ASM_CLOBBERS);
   } else {
     if (NW == 8)
@@ -796,6 +809,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
                    : FP8_PREFILL_ASM_CLOBBERS);
   }
 #undef FP8_PF_COMMON_OPERANDS
+#undef FP8_PF_KCONST_OPERANDS
 #undef FP8_PF_BLOCK_OPERANDS
 }
 
@@ -803,11 +817,11 @@ template <int NW>
 hipError_t launch_prefill_asm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                               const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
                               uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int KB,
-                              bool per_tensor, hipStream_t st) {
+                              bool kconst, hipStream_t st) {
   const int tiles_m = (int)((M + kPM - 1) / kPM);
   const int tiles_n = (int)((N + 32 * NW - 1) / (32 * NW));
   dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n);
-  if (per_tensor)
+  if (kconst)
     hipLaunchKernelGGL((gemm_prefill_asm_kernel<true, NW>), grid, dim3(64 * NW), 0, st, a, ld_a,
                        sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, (int)N, KB, tiles_m,
                        tiles_n);
@@ -995,13 +1009,13 @@ bool linear_decode_supported(int64_t M, int64_t K) {
 hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                        const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
                        uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
-                       bool per_tensor, hipStream_t st) {
+                       bool kconst, hipStream_t st) {
   const int KB = (int)(K / 128);
   if (M <= 16 && KB <= kDecodeMaxKB) {
     constexpr int KSPLIT = FP8_DECODE_KSPLIT, KBW = FP8_DECODE_KBW;
     dim3 grid((uint32_t)(N / 16));
-    const size_t lds = decode_lds_bytes<KSPLIT, KBW>(KB, per_tensor);
-    if (per_tensor)
+    const size_t lds = decode_lds_bytes<KSPLIT, KBW>(KB, kconst);
+    if (kconst)
       hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, KBW, true>), grid, dim3(64 * KSPLIT), lds, st,
                          a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
     else
@@ -1010,7 +1024,7 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
     return hipGetLastError();
   }
   if (FP8_PREFILL_ASM && M > 64 && KB % kPfKbGroup == 0 && KB <= kPrefillMaxKB &&
-      ld_a < kPrefillMaxLd &&
+      (!kconst || ld_sw < kPrefillMaxLd / 4) && ld_a < kPrefillMaxLd &&
       ld_w < kPrefillMaxLd && ld_out < kPrefillMaxLd / 2 && ld_sa < kPrefillMaxLd / 4 &&
       ld_sw < kPrefillMaxLd) {
     // 256 x 256 tiles unless they would occupy at most half of the CUs: then
@@ -1018,15 +1032,15 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
     const int64_t tiles256 = ((M + kPM - 1) / kPM) * ((N + kPN - 1) / kPN);
     if (2 * tiles256 <= device_cus())
       return launch_prefill_asm<4>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N, KB,
-                                   per_tensor, st);
+                                   kconst, st);
     return launch_prefill_asm<8>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N, KB,
-                                 per_tensor, st);
+                                 kconst, st);
   }
   if (M > 64 && ld_a < kPrefillMaxLd && ld_w < kPrefillMaxLd) {
     const int tiles_m = (int)((M + kPM - 1) / kPM);
     const int tiles_n = (int)((N + kPN - 1) / kPN);
     dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n);
-    if (per_tensor)
+    if (kconst)
       hipLaunchKernelGGL(gemm_prefill_kernel<true>, grid, dim3(kPThreads), 0, st, a, ld_a, sa,
                          ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, (int)N, KB, tiles_m,
                          tiles_n);
@@ -1039,7 +1053,7 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
   const int tiles_m = (int)((M + kBM - 1) / kBM);
   const int tiles_n = (int)(N / kBN);
   dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n);
-  if (per_tensor)
+  if (kconst)
     hipLaunchKernelGGL(gemm_tile_kernel<true>, grid, dim3(256), 0, st, a, ld_a, sa, ld_sa, w, ld_w,
                        sw, ld_sw, out, ld_out, (int)M, KB, tiles_n);
   else

@@ -368,8 +368,36 @@ def gen_epilogue(block, tag, nw):
             for r in range(4):
                 L.append(f"v_fmac_f32_e32 v{acc(ii, jj, r)}, v{SPREV}, v{pslot(q) + r}")
     else:
-        for k in range(128):
-            L.append(f"v_mul_f32_e32 v{ACC0 + k}, %[st], v{ACC0 + k}")
+        # scales constant along K: out[m, n] = (sa[m] * sw[n]) * acc.  The
+        # lane's 8 row scales (rows 128 wm + 16 j + r16) and 16 column scales
+        # (columns 64 wn + 16 i + 4 kg + r) come through range-checked
+        # descriptors (strides 0 give the per-tensor case).
+        sa_r, sw_r, vt = P0, P0 + 8, (SC0, SC0 + 1)
+        n = 0
+        for j in range(8):
+            t = vt[n % 2]
+            n += 1
+            if j == 0:
+                L.append(f"v_mov_b32 v{t}, %[offSaR]")
+            else:
+                L += [f"s_mul_i32 {S_R}, %[sjA], {j}", f"v_add_u32 v{t}, {S_R}, %[offSaR]"]
+            L.append(f"buffer_load_dword v{sa_r + j}, v{t}, %[dSaR], 0 offen")
+        for i in range(4):
+            for r in range(4):
+                t = vt[n % 2]
+                n += 1
+                if i == 0 and r == 0:
+                    L.append(f"v_mov_b32 v{t}, %[offSwR]")
+                else:
+                    L += [f"s_mul_i32 {S_R}, %[siW], {i}", f"s_mul_i32 {S_T}, %[srW], {r}",
+                          f"s_add_u32 {S_R}, {S_R}, {S_T}", f"v_add_u32 v{t}, {S_R}, %[offSwR]"]
+                L.append(f"buffer_load_dword v{sw_r + 4 * i + r}, v{t}, %[dSwR], 0 offen")
+        L.append("s_waitcnt vmcnt(0)")
+        for i in range(4):
+            for j in range(8):
+                for r in range(4):
+                    L += [f"v_mul_f32_e32 v{vt[0]}, v{sa_r + j}, v{sw_r + 4 * i + r}",
+                          f"v_mul_f32_e32 v{acc(i, j, r)}, v{vt[0]}, v{acc(i, j, r)}"]
     # every wave's copies and fragment reads are done: the stages are free
     L += ["s_waitcnt vmcnt(0) lgkmcnt(0)", "s_barrier",
           "s_cmp_eq_u32 %[colok], 0", f"s_cbranch_scc1 fp8pf_done_{tag}"]

@@ -22,13 +22,20 @@ hipError_t launch_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, in
 hipError_t launch_quant_tensor(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
                                uint8_t* q, int64_t ld_q, float* s, uint32_t* partials,
                                hipStream_t st);
+hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t K, int64_t ld_x, uint8_t* q,
+                             int64_t ld_q, float* s, int64_t ld_s, hipStream_t st);
+hipError_t launch_quant_static(const uint16_t* x, int64_t R, int64_t K, int64_t ld_x, uint8_t* q,
+                               int64_t ld_q, const float* scale, hipStream_t st);
 hipError_t launch_encode_f32(const float* x, int64_t n, uint8_t* codes, hipStream_t st);
 
-// out = A . W^T, block scales (per_tensor = false) or one scale each.
+// out = A . W^T.  kconst = false: block scales sa[m * ld_sa + kb],
+// sw[(n / 128) * ld_sw + kb].  kconst = true: scales constant along K,
+// out[m, n] = (sa[m * ld_sa] * sw[n * ld_sw]) * acc; ld_sa = ld_sw = 0 is the
+// per-tensor case.
 hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                        const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
                        uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
-                       bool per_tensor, hipStream_t st);
+                       bool kconst, hipStream_t st);
 
 // Fused decode linear: dynamic 1x128 quantization of x inside the decode GEMM
 // (block scales).  Dispatched for 1 <= M <= 4 and K <= 16384; the result is

@@ -149,6 +149,61 @@ __global__ __launch_bounds__(256) void quant_tensor_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Dynamic per-row quantization: one scale per row -- per token for
+// activations, per output channel for weights ("[vLLM] FP8", scaling
+// strategies: dynamic per-token; "FP8 Quantization": channel-wise weight
+// scales).  One wave per row, four rows per workgroup: the wave reads the
+// row as 16-byte chunks (lane i takes chunks i, i + 64, ...; coalesced), folds
+// the amax with a wave reduction, then re-reads the row (from L1/L2) and
+// encodes it with the same divisor and encoder as the 1x128 quantizer.
+__global__ __launch_bounds__(256) void quant_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t ld_x, uint32_t chunks,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ s, int64_t ld_s) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;                                   // wave-uniform
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint16_t* xr = x + row * ld_x;
+  uint32_t m = 0;
+  for (uint32_t c = lane; c < chunks; c += 64u) {
+    const uint32_t t = absmax8_bits(*reinterpret_cast<const uint4*>(xr + c * 8u));
+    m = m > t ? m : t;
+  }
+  m = wave_max(m);
+  const GroupDivisor d = make_divisor(__uint_as_float(m));
+  if (lane == 0) s[row * ld_s] = d.s;
+  uint8_t* qr = q + row * ld_q;
+  for (uint32_t c = lane; c < chunks; c += 64u)
+    *reinterpret_cast<uint2*>(qr + c * 8u) = quant8(*reinterpret_cast<const uint4*>(xr + c * 8u), d);
+}
+
+// ---------------------------------------------------------------------------
+// Static quantization with a calibrated scale held in device memory
+// ("[vLLM] FP8", scaling strategies: static per-tensor): code = E4M3(x / s)
+// with the IEEE fp32 quotient (the compiler's correctly rounded division;
+// the scale is not derived from the data, so the bounded-quotient method of
+// the dynamic kernels does not apply) and the saturating, NaN-aware element
+// encoder.  Grid-stride over 16-byte chunks.
+__global__ __launch_bounds__(256) void quant_static_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
+    const float* __restrict__ scale, uint32_t chunks_per_row, uint64_t nchunks) {
+  const float sc = scale[0];
+  for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < nchunks;
+       i += (uint64_t)gridDim.x * 256u) {
+    const uint64_t row = i / chunks_per_row;
+    const uint64_t c = i - row * chunks_per_row;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + row * ld_x + c * 8u);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xe = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+      out[e >> 2] |= (uint32_t)e4m3_encode_one(xe / sc) << (8 * (e & 3));
+    }
+    *reinterpret_cast<uint2*>(q + row * ld_q + c * 8u) = make_uint2(out[0], out[1]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void encode_f32_kernel(const float* __restrict__ x, uint64_t n,
                                                          uint8_t* __restrict__ codes) {
   uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
@@ -196,6 +251,25 @@ hipError_t launch_quant_tensor(const uint16_t* x, int64_t R, int64_t C, int64_t 
   const uint32_t p2 = (uint32_t)(want2 < 8192 ? want2 : 8192);
   hipLaunchKernelGGL(quant_tensor_kernel, dim3(p2), dim3(256), 0, st, x, ld_x, q, ld_q, s, cpr,
                      nchunks, partials, p1);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t K, int64_t ld_x, uint8_t* q,
+                             int64_t ld_q, float* s, int64_t ld_s, hipStream_t st) {
+  const uint64_t grid = ((uint64_t)R + 3) / 4;
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((uint32_t)grid), dim3(256), 0, st, x, R, ld_x,
+                     (uint32_t)(K / 8), q, ld_q, s, ld_s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_static(const uint16_t* x, int64_t R, int64_t K, int64_t ld_x, uint8_t* q,
+                               int64_t ld_q, const float* scale, hipStream_t st) {
+  const uint32_t cpr = (uint32_t)(K / 8);
+  const uint64_t nchunks = (uint64_t)R * cpr;
+  const uint64_t want = (nchunks + 255) / 256;
+  const uint32_t grid = (uint32_t)(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(quant_static_kernel, dim3(grid), dim3(256), 0, st, x, ld_x, q, ld_q, scale,
+                     cpr, nchunks);
   return hipGetLastError();
 }
 

@@ -65,8 +65,16 @@ typedef enum {
  *                   (the dynamic 128-group and static 128-block schemes of
  *                   "[vLLM] FP8", scaling strategies).
  * FP8_SCALE_TENSOR: one scale for the whole tensor, computed dynamically from
- *                   the tensor's amax (the dynamic per-tensor scheme). */
-enum { FP8_SCALE_BLOCK = 0, FP8_SCALE_TENSOR = 1 };
+ *                   the tensor's amax (the dynamic per-tensor scheme).
+ * FP8_SCALE_ROW   : one scale per row -- per token for activations (the
+ *                   dynamic per-token scheme), per output channel for
+ *                   weights (channel-wise weight scales, "FP8 Quantization",
+ *                   the pre-quantized checkpoint path).  In the GEMM each
+ *                   scale vector may also be a single value (stride 0), so a
+ *                   static or dynamic per-tensor activation scale combines
+ *                   with per-channel weights, and per-token activations with
+ *                   a per-tensor weight. */
+enum { FP8_SCALE_BLOCK = 0, FP8_SCALE_TENSOR = 1, FP8_SCALE_ROW = 2 };
 
 /* Operation ids for fp8_workspace_bytes(). */
 enum { FP8_OP_QUANT_ACT = 0, FP8_OP_QUANT_WEIGHT = 1, FP8_OP_GEMM = 2, FP8_OP_LINEAR = 3 };
@@ -84,18 +92,19 @@ size_t fp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int scale_mo
  * Follows "FP8 Quantization" sections C and D.2 (activation scales computed
  * at run time per call) and "[vLLM] FP8", block quantization (the block path
  * takes only a dynamic activation scheme) and scaling strategies (dynamic
- * 128-group and dynamic per-tensor).
+ * 128-group, dynamic per-tensor, dynamic per-token).
  *   x      [M, K] bf16, ld_x elements per row                      (input)
  *   q      [M, K] E4M3 codes, ld_q bytes per row                    (output)
  *   scales FP8_SCALE_BLOCK : [M, K/128] fp32, ld_s >= K/128         (output)
  *          FP8_SCALE_TENSOR: scales[0], one fp32                    (output)
- *   For each group G (1x128 slice of a row, or the whole tensor):
+ *          FP8_SCALE_ROW   : scales[m * ld_s], M fp32, ld_s >= 1    (output)
+ *   For each group G (1x128 slice of a row, a whole row, or the tensor):
  *     amax = max |x|, s = fp32(amax) / 448 (IEEE round to nearest),
  *     code = E4M3_RNE_saturating(fp32(x) / s), the quotient correctly
  *     rounded; an all-zero group gets s = 0 and codes +-0 by x's sign.
  *   workspace: FP8_SCALE_TENSOR needs fp8_workspace_bytes(FP8_OP_QUANT_ACT,
  *     M, 0, K, FP8_SCALE_TENSOR) bytes of device memory (4-byte aligned,
- *     contents need not be initialized); FP8_SCALE_BLOCK needs none. */
+ *     contents need not be initialized); the other modes need none. */
 fp8_status fp8_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                          uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s,
                          int scale_mode, void* workspace, size_t ws_bytes, void* stream);
@@ -109,11 +118,12 @@ fp8_status fp8_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
  *   q      [N, K] E4M3 codes, ld_q bytes per row                    (output)
  *   scales FP8_SCALE_BLOCK : [N/128, K/128] fp32, ld_s >= K/128     (output)
  *          FP8_SCALE_TENSOR: scales[0]                               (output)
+ *          FP8_SCALE_ROW   : scales[n * ld_s], one per output channel (output)
  *   block_n, block_k: must both be 128 in FP8_SCALE_BLOCK mode (the block
- *   size has two dimensions; other sizes give FP8_ERR_BLOCK); ignored in
- *   FP8_SCALE_TENSOR mode.
- *   Same per-group rule as fp8_quant_act with G = one 128x128 block (or the
- *   tensor).  workspace as for fp8_quant_act with M = N. */
+ *   size has two dimensions; other sizes give FP8_ERR_BLOCK); ignored in the
+ *   other modes.
+ *   Same per-group rule as fp8_quant_act with G = one 128x128 block, one
+ *   weight row, or the tensor.  workspace as for fp8_quant_act with M = N. */
 fp8_status fp8_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
                                   uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s,
                                   int block_n, int block_k, int scale_mode,
@@ -131,6 +141,10 @@ fp8_status fp8_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64
  *                          sum_{k in kb} dec(a_q[m,k]) * dec(w_q[n,k]) )
  *     accumulated in fp32.
  *   FP8_SCALE_TENSOR: a_s[0], w_s[0]; out = bf16(a_s * w_s * sum_k ...).
+ *   FP8_SCALE_ROW   : a_s[m * ld_as] (per token), w_s[n * ld_ws] (per output
+ *     channel), ld_as, ld_ws >= 0 (0: one value for all rows / columns);
+ *     out[m,n] = bf16_RNE( (a_s[m] * w_s[n]) * sum_k dec(a_q) * dec(w_q) ),
+ *     the scale product in fp32, the sum accumulated in fp32.
  *   Mixing a per-tensor activation scale with block weights (or the reverse)
  *   is not a mode (FP8_ERR_SCHEME).  No workspace is used. */
 fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, int64_t ld_as,
@@ -147,7 +161,9 @@ fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, in
  *   x [M, K] bf16 (ld_x), w_q / w_s as for fp8_block_gemm, out [M, N] bf16.
  *   The result is bit-identical to fp8_quant_act (same scale_mode) followed
  *   by fp8_block_gemm.
- *   FP8_SCALE_BLOCK with 1 <= M <= 16 and K <= 16384 runs as one fused
+ *   FP8_SCALE_ROW quantizes x per token (dynamic) and takes per-channel
+ *   (or, with ld_ws = 0, per-tensor) weight scales w_s[n * ld_ws].
+ *   FP8_SCALE_BLOCK with 1 <= M <= 4 and K <= 16384 runs as one fused
  *   launch (quantization inside the decode GEMM) and needs no workspace.
  *   Any other call quantizes into the workspace and then multiplies; it
  *   needs fp8_workspace_bytes(FP8_OP_LINEAR, M, N, K, scale_mode) bytes of
@@ -157,7 +173,21 @@ fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
                       int64_t M, int64_t N, int64_t K, int scale_mode, void* workspace,
                       size_t ws_bytes, void* stream);
 
-/* Host-only validation: the argument checks of the three calls above, in the
+/* fp8_quant_act_static -- static activation quantization with a scale
+ * calibrated beforehand ("[vLLM] FP8", scaling strategies: static
+ * per-tensor; static scales come from calibration data, dynamic ones are
+ * computed at run time).
+ *   x      [M, K] bf16, ld_x elements per row                      (input)
+ *   q      [M, K] E4M3 codes, ld_q bytes per row                    (output)
+ *   scale  one fp32 in device memory, read by the kernel            (input)
+ *   code = E4M3_RNE_saturating(fp32(x) / scale), the quotient an IEEE fp32
+ *   division (a zero scale gives x / 0: saturated codes, NaN for 0 / 0).
+ *   The codes pair with a_s = scale in fp8_block_gemm (FP8_SCALE_TENSOR, or
+ *   FP8_SCALE_ROW with ld_as = 0 against per-channel weights).  No workspace. */
+fp8_status fp8_quant_act_static(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                uint8_t* q, int64_t ld_q, const float* scale, void* stream);
+
+/* Host-only validation: the argument checks of the calls above, in the
  * same order, without touching any device (no device check, no launch). */
 fp8_status fp8_validate_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                                   const uint8_t* q, int64_t ld_q, const float* scales,
@@ -173,6 +203,8 @@ fp8_status fp8_validate_block_gemm(const uint8_t* a_q, int64_t ld_a, const float
                                    const float* w_s, int64_t ld_ws, const uint16_t* out,
                                    int64_t ld_out, int64_t M, int64_t N, int64_t K,
                                    int scale_mode);
+fp8_status fp8_validate_quant_act_static(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                         const uint8_t* q, int64_t ld_q, const float* scale);
 
 /* fp8_e4m3_encode_f32 -- the device element encoder on its own.
  * codes[i] = E4M3 of x[i]: round to nearest even, magnitudes above 448 and

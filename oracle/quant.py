@@ -157,6 +157,6 @@ def quant_static_ref(bits, scale):
     """
     x = bf16_bits_to_f32(np.asarray(bits, dtype=np.uint16))
     s = np.float32(np.asarray(scale, dtype=np.float32).reshape(-1)[0])
-    with np.errstate(divide="ignore", invalid="ignore"):
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         q = (x / s).astype(np.float32)
     return e4m3.encode(q)

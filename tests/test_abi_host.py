@@ -32,7 +32,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -132,7 +132,7 @@ def test_validate_block_gemm():
     assert vg(N=100) == SHAPE
     assert vg(K=64) == SHAPE
     assert vg(N=0) == SHAPE
-    assert vg(mode=2) == SCHEME
+    assert vg(mode=7) == SCHEME
     assert vg(out=None) == NULL
     assert vg(sa=None) == NULL
     assert vg(ld_out=128) == STRIDE
@@ -141,6 +141,43 @@ def test_validate_block_gemm():
     assert vg(out=O + 4) == ALIGN
     assert vg(ld_out=260) == ALIGN
     assert vg(out=X + 16) == ALIAS
+
+
+def test_validate_row_mode():
+    # per token / per channel: one scale per row at stride ld_s >= 1
+    assert vq(mode=2, ld_s=1) == OK
+    assert vq(mode=2, ld_s=3) == OK
+    assert vq(mode=2, ld_s=0) == STRIDE
+    assert vq(mode=2, ld_s=1, s=Q + 64) == ALIAS
+    assert vw(mode=2, ld_s=1, bn=0, bk=0) == OK                 # block dims unused
+    assert vw(mode=2, ld_s=0) == STRIDE
+    # GEMM: per-row vectors, stride 0 = one value for all rows / columns
+    assert vg(mode=2, ld_as=1, ld_ws=1) == OK
+    assert vg(mode=2, ld_as=0, ld_ws=1) == OK
+    assert vg(mode=2, ld_as=0, ld_ws=0) == OK
+    assert vg(mode=2, ld_as=-1, ld_ws=1) == STRIDE
+    assert vg(mode=2, ld_as=1, ld_ws=-2) == STRIDE
+    assert vg(mode=2, ld_as=1, ld_ws=1, out=S + 16) == ALIAS     # out over the token scales
+    assert _lib.workspace_bytes(_lib.OP_QUANT_ACT, 16, 0, 4096, "row") == 0
+    assert _lib.workspace_bytes(_lib.OP_LINEAR, 16, 11008, 4096, "row") >= 16 * 4096 + 16 * 4
+
+
+def vs(x=X, M=16, K=512, ld_x=None, q=Q, ld_q=None, s=S):
+    ld_x = K if ld_x is None else ld_x
+    ld_q = K if ld_q is None else ld_q
+    return _lib.lib().fp8_validate_quant_act_static(x, M, K, ld_x, q, ld_q, s)
+
+
+def test_validate_quant_act_static():
+    assert vs() == OK
+    assert vs(M=0, x=None, q=None, s=None) == OK
+    assert vs(K=100) == SHAPE
+    assert vs(s=None) == NULL
+    assert vs(x=None) == NULL
+    assert vs(ld_q=256) == STRIDE
+    assert vs(s=S + 2) == ALIGN
+    assert vs(q=X + 64) == ALIAS
+    assert vs(s=Q + 16) == ALIAS                                # scale inside the codes
 
 
 def test_binding_rejects_host_tensors():
