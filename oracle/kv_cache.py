@@ -9,8 +9,8 @@ KV cache quantization and "why this design" item 4).  Each of K and V has a
 scale: the default is 1.0, which clips outliers, or a calibrated one baked
 into the checkpoint; one paged-attention block holds 16 tokens; outside an
 FP8 attention backend the stored codes are only a storage format, restored
-to 16 bits inside the attention kernel (the KV-cache section of the
-serving-format page).
+to 16 bits inside the attention kernel ("Quantization guide for serving:
+FP8, AWQ, GPTQ", KV-cache FP8 section).
 
 What is computed here:
     write:  cache[slot(t), h, d] = E4M3( fp32(x[t, h, d]) / scale )
@@ -24,8 +24,9 @@ Readings (the pages give no formula): the stored code is x / scale, the
 restored value code * scale (the dequantized value of oracle.quant); slot =
 block * block_size + offset in a cache laid out [blocks, block_size, heads,
 head_dim]; a negative slot marks a token that is not stored (padding); the
-restore multiplies in fp32 and rounds once to bf16; a NaN code restores to
-the quiet bf16 NaN with the code's sign.
+restore multiplies in fp32 and rounds once to bf16; a NaN product (a NaN
+code, or a NaN / infinite scale) restores to the quiet bf16 NaN carrying the
+sign of the stored code, so the sign never depends on how a NaN propagates.
 """
 
 import numpy as np
@@ -73,7 +74,11 @@ def kv_read_ref(cache, slots, scale):
     for t in range(T):
         s = int(slots[t])
         if 0 <= s < nb * bs:
-            v = e4m3.decode(cache[s // bs, s % bs]).astype(np.float32)
+            codes = cache[s // bs, s % bs]
+            v = e4m3.decode(codes).astype(np.float32)
             with np.errstate(over="ignore", invalid="ignore"):
-                out[t] = bf16_rne_bits((v * s32).astype(np.float32))
+                prod = (v * s32).astype(np.float32)
+            r = bf16_rne_bits(prod)
+            code_sign = (codes.astype(np.uint16) & np.uint16(0x80)) << np.uint16(8)
+            out[t] = np.where(np.isnan(prod), code_sign | np.uint16(0x7FC0), r)
     return out

@@ -71,3 +71,18 @@ def test_bf16_rounding_matches_torch():
     assert np.array_equal(kv_cache.bf16_rne_bits(f), want)
     nan = kv_cache.bf16_rne_bits(np.array([np.nan, -np.nan], dtype=np.float32))
     assert nan.tolist() == [0x7FC0, 0xFFC0]
+
+
+def test_nan_restores_with_the_code_sign():
+    # 0x7F / 0xFF are the E4M3 NaN codes; a zero code times an infinite scale
+    # and any code times a NaN scale are NaN products too: each restores to
+    # the quiet bf16 NaN carrying the stored code's sign bit
+    cache = np.array([0x7F, 0xFF, 0x00, 0x80, 0x01, 0x81, 0x38, 0xB8],
+                     dtype=np.uint8).reshape(1, 1, 1, 8)
+    one = kv_cache.kv_read_ref(cache, np.array([0]), np.float32(1.0))[0, 0]
+    assert one.tolist()[:2] == [0x7FC0, 0xFFC0]
+    assert one.tolist()[2:] == [0x0000, 0x8000, 0x3B00, 0xBB00, 0x3F80, 0xBF80]  # 2^-9, 1.0
+    inf = kv_cache.kv_read_ref(cache, np.array([0]), np.float32(np.inf))[0, 0]
+    assert inf.tolist() == [0x7FC0, 0xFFC0, 0x7FC0, 0xFFC0, 0x7F80, 0xFF80, 0x7F80, 0xFF80]
+    nan = kv_cache.kv_read_ref(cache, np.array([0]), np.float32(np.nan))[0, 0]
+    assert nan.tolist() == [0x7FC0, 0xFFC0] * 4
