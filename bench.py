@@ -1,6 +1,7 @@
 """Benchmark of the FP8 W8A8 linear hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|mlp_down|mlp_down_tensor|large|tiny]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload decode|prefill|mlp_down|mlp_down_tensor|large|tiny|kv_cache]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 dynamic activation quantization followed by the block-scaled GEMM (weights
@@ -16,6 +17,12 @@ graph per step pattern), bracketed by torch.cuda.synchronize() on both sides
 launch duration is measured with one HIP event pair on the launch stream
 around a run of back-to-back launches of that kernel, queued behind a
 bounded GPU-side delay so that no host gap falls inside the timed span.
+
+The kv_cache workload times the FP8 KV-cache codec instead: a step stores
+the keys and values of 65536 tokens (8 heads of 128) as E4M3 codes into two
+paged 1 GiB caches and restores to bf16 the tokens the previous step stored
+(two input batches alternate, so the codes read back have been pushed out of
+the Infinity Cache by a step's worth of other traffic).
 
 Prints ONE JSON line.
 """
@@ -39,19 +46,30 @@ CALIB_COPY_BYTES = 256 << 20   # plain device copy whose counters calibrate FETC
 KERNEL_SOURCES = ("fp8_w8a8_block_amd/csrc/gemm_kernels.hip",
                   "fp8_w8a8_block_amd/csrc/prefill_asm.inc",
                   "fp8_w8a8_block_amd/csrc/device_common.h")
+KV_SOURCES = ("fp8_w8a8_block_amd/csrc/kv_kernels.hip",
+              "fp8_w8a8_block_amd/csrc/device_common.h")
 TRAFFIC_FILE = os.path.join("profiles", "traffic.json")
 
 
-def kernel_source_hash():
+def kernel_source_hash(workload=None):
+    """Hash of the dominant kernel's sources with comments and blank lines
+    removed, so that counters stay attached to the code they measured."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for rel in (KV_SOURCES if workload == "kv_cache" else KERNEL_SOURCES):
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 
 def dominant_kernel(workload, decode):
+    if workload == "kv_cache":
+        return "kv_write_kernel"
     # the prefill-shaped workloads all have K % 512 == 0 and M > 64: the
     # hand-scheduled kernel
     return "gemm_decode_kernel" if decode or workload == "tiny" else "gemm_prefill_asm_kernel"
@@ -65,7 +83,7 @@ def measured_traffic(workload):
         return None
     with open(path) as f:
         rec = json.load(f).get(workload)
-    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return rec.get("bytes_per_launch")
 
@@ -92,7 +110,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "mlp_down", "mlp_down_tensor", "large", "tiny"])
+                   choices=["decode", "prefill", "mlp_down", "mlp_down_tensor", "large", "tiny",
+                            "kv_cache"])
     p.add_argument("--cpu-baseline-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample (0 disables it)")
     p.add_argument("--no-secondary", action="store_true",
@@ -288,6 +307,190 @@ def cpu_baseline(wl, target_s):
             "sample": sample, "seconds": round(el, 2)}
 
 
+def kv_write_bytes(T, HD):
+    """Algorithmic bytes of one cache write: bf16 keys and values in, E4M3
+    codes of both out, the slot of each token, the two scales."""
+    return T * (2 * 2 * HD + 2 * HD + 8) + 8
+
+
+def kv_read_bytes(T, HD):
+    """One restore: codes and slot of each token in, bf16 out, the scale."""
+    return T * (HD + 2 * HD + 8) + 4
+
+
+class KVWorkload:
+    """Two alternating batches of paged-cache traffic: step s stores batch
+    s % 2 and restores the keys and values of batch (s + 1) % 2."""
+
+    def __init__(self):
+        import torch
+        import fp8_w8a8_block_amd as fp8
+        from workloads import synth
+        self.fp8 = fp8
+        c = synth.KV_CONFIG
+        self.c = c
+        self.T, self.H, self.D = c["T"], c["H"], c["D"]
+        self.bs, self.nb = c["block_size"], c["num_blocks"]
+        self.batches = []
+        for b in range(2):
+            d = synth.make_kv(c["cfg"] + 100 * b, self.T, self.H, self.D, self.bs, self.nb,
+                              c["n_seqs"], c["key_outlier_dims"], c["key_outlier_mult"],
+                              c["pad_frac"])
+            self.batches.append({"key_bits": d["key"], "value_bits": d["value"],
+                                 "slots_host": d["slots"],
+                                 "key": dev_bf16(d["key"]), "value": dev_bf16(d["value"]),
+                                 "slots": torch.from_numpy(d["slots"]).cuda()})
+        f = synth.bf16_bits_to_f32_input(self.batches[0]["key_bits"][:4096])
+        self.k_scale = torch.tensor([float(np.abs(f).max()) / 448.0], dtype=torch.float32,
+                                    device="cuda")
+        self.v_scale = torch.ones(1, dtype=torch.float32, device="cuda")
+        shape = (self.nb, self.bs, self.H, self.D)
+        self.kc = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+        self.vc = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+        self.kout = torch.empty((self.T, self.H, self.D), dtype=torch.bfloat16, device="cuda")
+        self.vout = torch.empty_like(self.kout)
+        for b in range(2):
+            self.write(b)
+        torch.cuda.synchronize()
+
+    def write(self, b):
+        B = self.batches[b]
+        self.fp8.kv_cache_write(B["key"], B["value"], B["slots"], self.kc, self.vc,
+                                self.k_scale, self.v_scale)
+
+    def step(self, s):
+        self.write(s % 2)
+        r = self.batches[(s + 1) % 2]["slots"]
+        self.fp8.kv_cache_read(self.kc, r, self.k_scale, out=self.kout)
+        self.fp8.kv_cache_read(self.vc, r, self.v_scale, out=self.vout)
+
+    def bytes_per_step(self):
+        HD = self.H * self.D
+        return kv_write_bytes(self.T, HD) + 2 * kv_read_bytes(self.T, HD)
+
+
+def time_launches(fn, n_launches):
+    """Average duration of one kernel: an event pair on the launch stream
+    around n back-to-back launches queued behind a bounded GPU-side delay."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(5e7))
+    e0.record()
+    for i in range(n_launches):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n_launches
+
+
+def kv_cpu_baseline(wl, target_s):
+    """The KV-cache oracle timed on the host: store + restore of a token
+    sample of batch 0 into a cache sized for that sample."""
+    from oracle import kv_cache
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = os.cpu_count() or 1
+    n = 1024
+    B = wl.batches[0]
+    ks = np.float32(wl.k_scale.item())
+    HD = wl.H * wl.D
+    cache = np.zeros((n // wl.bs, wl.bs, wl.H, wl.D), dtype=np.uint8)
+    slots = np.arange(n, dtype=np.int64)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        lo = (reps * n) % wl.T
+        kc = kv_cache.kv_write_ref(B["key_bits"][lo:lo + n], slots, cache, ks)
+        vc = kv_cache.kv_write_ref(B["value_bits"][lo:lo + n], slots, cache, np.float32(1.0))
+        kv_cache.kv_read_ref(kc, slots, ks)
+        kv_cache.kv_read_ref(vc, slots, np.float32(1.0))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 64:
+            break
+    nbytes = reps * (kv_write_bytes(n, HD) + 2 * kv_read_bytes(n, HD))
+    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle store + restore of {n}-token slices of the same keys and values "
+                      f"(H={wl.H}, D={wl.D}) into a {n}-slot cache, repeated {reps}x",
+            "seconds": round(el, 2)}
+
+
+def main_kv(args):
+    import torch
+    calibration_copy()
+    wl = KVWorkload()
+    for s in range(args.warmup):
+        wl.step(s)
+    torch.cuda.synchronize()
+    graphs = []
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for p in range(2):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                wl.step(p)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(stream)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for s in range(K):
+        graphs[s % 2].replay()
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+
+    HD = wl.H * wl.D
+    n_l = 40
+    w_ms = time_launches(lambda i: wl.write(i % 2), n_l)
+    r_ms = time_launches(lambda i: wl.fp8.kv_cache_read(
+        wl.kc, wl.batches[i % 2]["slots"], wl.k_scale, out=wl.kout), n_l)
+    wb = kv_write_bytes(wl.T, HD)
+    rb = kv_read_bytes(wl.T, HD)
+    roof = {"bound": "hbm", "achieved": wb / (w_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic("kv_cache")
+    roof["kernel"] = "kv_write_kernel"
+    roof["avg_launch_us"] = w_ms * 1e3
+    roof["launches_timed"] = n_l
+    roof["algorithmic_bytes_per_launch"] = wb
+    roof["kernel_source_hash"] = kernel_source_hash("kv_cache")
+    read = {"kernel": "kv_read_kernel", "avg_launch_us": r_ms * 1e3,
+            "algorithmic_bytes_per_launch": rb, "GB/s": rb / (r_ms * 1e-3) / 1e9,
+            "frac_of_8000": rb / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    cpu = kv_cpu_baseline(wl, args.cpu_baseline_seconds) if args.cpu_baseline_seconds > 0 else None
+    total = wl.bytes_per_step()
+    line = {
+        "metric": "FP8 KV-cache codec GB/s (store + restore) as % of MI355X HBM roofline",
+        "value": total / (sec / K) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": sec / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 <-> fp8e4m3 (fp32 scale arithmetic)",
+        "data": "synthetic (seeded numpy, paged slot mapping)",
+        "config": {"workload": "kv_cache", "tokens": wl.T, "kv_heads": wl.H, "head_dim": wl.D,
+                   "block_size": wl.bs, "num_blocks": wl.nb,
+                   "cache_bytes_each": wl.nb * wl.bs * HD,
+                   "step": "store K and V of one batch, restore K and V of the other"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "secondary": read,
+        "step_bytes": {"total": total},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -296,6 +499,8 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload == "kv_cache":
+        return main_kv(args)
     calibration_copy()
     wl = Workload(args.workload)
     decode = len(wl.Ms) > 1

@@ -51,6 +51,13 @@ _SIGS = {
                           _sz, _vp]),
     "fp8_quant_act_static": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "fp8_validate_quant_act_static": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp]),
+    "fp8_kv_cache_write": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp, _i64,
+                                  _i64, _vp, _vp, _vp]),
+    "fp8_kv_cache_read": (_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp]),
+    "fp8_validate_kv_cache_write": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp,
+                                           _i64, _i64, _vp, _vp]),
+    "fp8_validate_kv_cache_read": (_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp,
+                                          _i64]),
 }
 
 _lib = None
@@ -243,6 +250,76 @@ def quant_act_static(x, scale, q=None):
         _check(lib().fp8_quant_act_static(x.data_ptr(), M, K, ld_x, q.data_ptr(), ld_q,
                                           scale.data_ptr(), _stream(x)))
     return q
+
+
+def _scalar_scale(t, name):
+    if t.dtype != torch.float32 or not t.is_cuda or t.numel() != 1:
+        raise TypeError(f"{name} must be a 1-element float32 device tensor")
+
+
+def _tokens(t, name):
+    """[T, H, D] bf16 with each token's H * D values contiguous -> (T, H, D, ld)."""
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name} must be [T, H, D] with contiguous heads")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    T, H, D = t.shape
+    return T, H, D, (t.stride(0) if T > 1 else H * D)
+
+
+def _cache(c, name):
+    if c.dtype != torch.uint8 or c.dim() != 4 or not c.is_contiguous() or not c.is_cuda:
+        raise ValueError(f"{name} must be a contiguous uint8 [blocks, block_size, H, D] device "
+                         "tensor")
+    return c.shape
+
+
+def _slots(s, T):
+    if s.dtype != torch.int64 or s.dim() != 1 or s.shape[0] != T or not s.is_cuda:
+        raise ValueError("slots must be a 1-D int64 device tensor with one entry per token")
+    return s.contiguous()
+
+
+def kv_cache_write(key, value, slot_mapping, key_cache, value_cache, k_scale, v_scale):
+    """Store bf16 key / value [T, H, D] as E4M3 codes into the paged caches
+    [blocks, block_size, H, D] at slot_mapping[t] (in place; negative or
+    out-of-range slots are skipped)."""
+    T, H, D, ld_k = _tokens(key, "key")
+    Tv, Hv, Dv, ld_v = _tokens(value, "value")
+    if (Tv, Hv, Dv) != (T, H, D):
+        raise ValueError("key and value shapes differ")
+    nb, bs, Hc, Dc = _cache(key_cache, "key_cache")
+    if tuple(value_cache.shape) != (nb, bs, Hc, Dc) or (Hc, Dc) != (H, D):
+        raise ValueError("cache shapes do not match the tokens")
+    _cache(value_cache, "value_cache")
+    _scalar_scale(k_scale, "k_scale")
+    _scalar_scale(v_scale, "v_scale")
+    slots = _slots(slot_mapping, T)
+    with torch.cuda.device(key.device):
+        _check(lib().fp8_kv_cache_write(key.data_ptr(), ld_k, value.data_ptr(), ld_v,
+                                        slots.data_ptr(), T, H, D, key_cache.data_ptr(),
+                                        value_cache.data_ptr(), nb, bs, k_scale.data_ptr(),
+                                        v_scale.data_ptr(), _stream(key)))
+
+
+def kv_cache_read(cache, slots, scale, out=None):
+    """Gather cache[slots] and restore to bf16 [T, H, D] (out-of-range slots
+    read zeros)."""
+    nb, bs, H, D = _cache(cache, "cache")
+    _scalar_scale(scale, "scale")
+    T = slots.shape[0] if slots.dim() == 1 else -1
+    slots = _slots(slots, T)
+    with torch.cuda.device(cache.device):
+        if out is None:
+            out = torch.empty((T, H, D), dtype=torch.bfloat16, device=cache.device)
+        To, Ho, Do, ld_o = _tokens(out, "out")
+        if (To, Ho, Do) != (T, H, D):
+            raise ValueError("out must be [T, H, D]")
+        _check(lib().fp8_kv_cache_read(cache.data_ptr(), nb, bs, H, D, slots.data_ptr(), T,
+                                       scale.data_ptr(), out.data_ptr(), ld_o, _stream(cache)))
+    return out
 
 
 def encode_f32(x):

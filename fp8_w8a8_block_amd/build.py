@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8w8a8.so")
-SOURCES = ["abi.hip", "quant_kernels.hip", "gemm_kernels.hip"]
+SOURCES = ["abi.hip", "quant_kernels.hip", "gemm_kernels.hip", "kv_kernels.hip"]
 ARCH = "gfx950"
 
 

@@ -330,6 +330,99 @@ fp8_status fp8_quant_act_static(const uint16_t* x, int64_t M, int64_t K, int64_t
   return launched(fp8k::launch_quant_static(x, M, K, ld_x, q, ld_q, scale, (hipStream_t)stream));
 }
 
+// ---- FP8 KV-cache codec --------------------------------------------------
+
+namespace {
+
+// Common shape checks: H * D values per token (a multiple of 8), a cache of
+// num_blocks * block_size slots.
+fp8_status kv_shape(int64_t T, int64_t H, int64_t D, int64_t num_blocks, int64_t block_size) {
+  if (T < 0 || T >= kMaxDim || H <= 0 || D <= 0 || H >= kMaxDim || D >= kMaxDim)
+    return FP8_ERR_SHAPE;
+  if (num_blocks < 0 || num_blocks >= kMaxDim || block_size <= 0 || block_size >= kMaxDim)
+    return FP8_ERR_SHAPE;
+  const int64_t hd = H * D;
+  if (hd >= kMaxDim || hd % 8 != 0) return FP8_ERR_SHAPE;
+  if (num_blocks * block_size > kMaxElems / hd || T > kMaxElems / hd) return FP8_ERR_SHAPE;
+  return FP8_OK;
+}
+
+}  // namespace
+
+fp8_status fp8_validate_kv_cache_write(const uint16_t* key, int64_t ld_key,
+                                       const uint16_t* value, int64_t ld_value,
+                                       const int64_t* slot_mapping, int64_t T, int64_t H,
+                                       int64_t D, const uint8_t* key_cache,
+                                       const uint8_t* value_cache, int64_t num_blocks,
+                                       int64_t block_size, const float* k_scale,
+                                       const float* v_scale) {
+  fp8_status st = kv_shape(T, H, D, num_blocks, block_size);
+  if (st != FP8_OK || T == 0) return st;
+  const int64_t hd = H * D, cap = num_blocks * block_size;
+  if (!key || !value || !slot_mapping || !k_scale || !v_scale) return FP8_ERR_NULL;
+  if (cap > 0 && (!key_cache || !value_cache)) return FP8_ERR_NULL;
+  if (ld_key < hd || ld_value < hd) return FP8_ERR_STRIDE;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(slot_mapping, 8) ||
+      !aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(k_scale, 4) ||
+      !aligned(v_scale, 4))
+    return FP8_ERR_ALIGN;
+  if (ld_key % 8 != 0 || ld_value % 8 != 0) return FP8_ERR_ALIGN;
+  const Range ins[] = {range_of(key, T, hd, ld_key, 2), range_of(value, T, hd, ld_value, 2),
+                       range_of(slot_mapping, 1, T, T, 8), range_of(k_scale, 1, 1, 1, 4),
+                       range_of(v_scale, 1, 1, 1, 4)};
+  const Range kc = range_of(key_cache, cap, hd, hd, 1), vc = range_of(value_cache, cap, hd, hd, 1);
+  if (overlap(kc, vc)) return FP8_ERR_ALIAS;
+  for (const Range& r : ins)
+    if (overlap(r, kc) || overlap(r, vc)) return FP8_ERR_ALIAS;
+  return FP8_OK;
+}
+
+fp8_status fp8_kv_cache_write(const uint16_t* key, int64_t ld_key, const uint16_t* value,
+                              int64_t ld_value, const int64_t* slot_mapping, int64_t T, int64_t H,
+                              int64_t D, uint8_t* key_cache, uint8_t* value_cache,
+                              int64_t num_blocks, int64_t block_size, const float* k_scale,
+                              const float* v_scale, void* stream) {
+  fp8_status st = fp8_validate_kv_cache_write(key, ld_key, value, ld_value, slot_mapping, T, H, D,
+                                              key_cache, value_cache, num_blocks, block_size,
+                                              k_scale, v_scale);
+  if (st != FP8_OK || T == 0) return st;
+  if ((st = check_device()) != FP8_OK) return st;
+  return launched(fp8k::launch_kv_write(key, ld_key, value, ld_value, slot_mapping, T, H * D,
+                                        key_cache, value_cache, num_blocks * block_size, k_scale,
+                                        v_scale, (hipStream_t)stream));
+}
+
+fp8_status fp8_validate_kv_cache_read(const uint8_t* cache, int64_t num_blocks,
+                                      int64_t block_size, int64_t H, int64_t D,
+                                      const int64_t* slots, int64_t T, const float* scale,
+                                      const uint16_t* out, int64_t ld_out) {
+  fp8_status st = kv_shape(T, H, D, num_blocks, block_size);
+  if (st != FP8_OK || T == 0) return st;
+  const int64_t hd = H * D, cap = num_blocks * block_size;
+  if (!slots || !scale || !out) return FP8_ERR_NULL;
+  if (cap > 0 && !cache) return FP8_ERR_NULL;
+  if (ld_out < hd) return FP8_ERR_STRIDE;
+  if (!aligned(cache, 16) || !aligned(slots, 8) || !aligned(scale, 4) || !aligned(out, 16))
+    return FP8_ERR_ALIGN;
+  if (ld_out % 8 != 0) return FP8_ERR_ALIGN;
+  const Range ro = range_of(out, T, hd, ld_out, 2);
+  if (overlap(ro, range_of(cache, cap, hd, hd, 1)) || overlap(ro, range_of(slots, 1, T, T, 8)) ||
+      overlap(ro, range_of(scale, 1, 1, 1, 4)))
+    return FP8_ERR_ALIAS;
+  return FP8_OK;
+}
+
+fp8_status fp8_kv_cache_read(const uint8_t* cache, int64_t num_blocks, int64_t block_size,
+                             int64_t H, int64_t D, const int64_t* slots, int64_t T,
+                             const float* scale, uint16_t* out, int64_t ld_out, void* stream) {
+  fp8_status st = fp8_validate_kv_cache_read(cache, num_blocks, block_size, H, D, slots, T, scale,
+                                             out, ld_out);
+  if (st != FP8_OK || T == 0) return st;
+  if ((st = check_device()) != FP8_OK) return st;
+  return launched(fp8k::launch_kv_read(cache, num_blocks * block_size, H * D, slots, T, scale, out,
+                                       ld_out, (hipStream_t)stream));
+}
+
 fp8_status fp8_e4m3_encode_f32(const float* x, int64_t n, uint8_t* codes, void* stream) {
   if (n < 0 || n > kMaxElems) return FP8_ERR_SHAPE;
   if (n == 0) return FP8_OK;

@@ -131,6 +131,87 @@ __device__ __forceinline__ uint2 quant8(const uint4 v, const GroupDivisor& d) {
   return make_uint2(c0, c1);
 }
 
+// ---- division by a static scale ------------------------------------------
+// A static scale s holds for a whole launch (calibrated activation scales,
+// KV-cache scales).  For a normal finite s the quotient x / s is formed with
+// the steps of the group divisor above: s' = |s| * 2^k in [1, 2),
+// r = fp32(1 / s') once, then per element x' = |x| * 2^k, q0 = x' r,
+// e = fma(-q0, s', x'), q = fma(e, r, q0).  An exhaustive host check in the
+// test suite (every fp32 mantissa of s' against every bf16 mantissa of x',
+// across the range where the E4M3 code depends on the quotient) shows q is
+// the IEEE quotient bit for bit.  Outside that range the code is the zero
+// code (x' underflows: the quotient is below 2^-126) or saturates (x'
+// overflows, or x is infinite: q turns NaN and is clamped to 448).  A zero,
+// subnormal, infinite or NaN scale divides directly, and so does any chunk
+// holding a NaN input (its code keeps the input's sign, as a division does).
+struct StaticDivisor {
+  float s;        // the scale (direct-division path)
+  float sp;       // s' in [1, 2)
+  float r;        // fp32(1 / s')
+  int k;          // exponent shift applied to |x|
+  uint32_t sign;  // sign of s at bit 7 of every byte
+  bool fast;      // s normal and finite
+};
+
+__device__ __forceinline__ StaticDivisor make_static_divisor(float s) {
+  StaticDivisor d;
+  d.s = s;
+  const float a = __builtin_fabsf(s);
+  d.fast = a >= 0x1p-126f && a <= 0x1.fffffep127f;    // false for NaN
+  d.sign = (__float_as_uint(s) >> 31) * 0x80808080u;
+  d.k = 0;
+  d.sp = 1.0f;
+  d.r = 1.0f;
+  if (d.fast) {
+    const int e = __builtin_amdgcn_frexp_expf(a);       // a = f * 2^e, f in [0.5, 1)
+    d.k = 1 - e;
+    d.sp = __builtin_ldexpf(a, d.k);
+    d.r = 1.0f / d.sp;
+  }
+  return d;
+}
+
+// |x| / |s| for the fast path, clamped to 448 (NaN from an overflowed x' too)
+__device__ __forceinline__ float static_quotient_abs(float x, const StaticDivisor& d) {
+  const float xa = __builtin_ldexpf(__builtin_fabsf(x), d.k);
+  const float q0 = xa * d.r;
+  const float e = __builtin_fmaf(-q0, d.sp, xa);
+  const float q = __builtin_fmaf(e, d.r, q0);
+  return q < kE4M3Max ? q : kE4M3Max;
+}
+
+// Nonzero iff one of the two bf16 halves of w is a NaN (|h| > 0x7f80).
+__device__ __forceinline__ uint32_t bf16x2_nan(uint32_t w) {
+  return ((w & 0x7fff7fffu) + 0x007f007fu) & 0x80008000u;
+}
+
+// E4M3 codes of 8 bf16 values divided by a static scale (byte i = element i),
+// equal to E4M3(fp32(x) / s) with an IEEE division.
+__device__ __forceinline__ uint2 quant8_static(const uint4 v, const StaticDivisor& d) {
+  const uint32_t nan = bf16x2_nan(v.x) | bf16x2_nan(v.y) | bf16x2_nan(v.z) | bf16x2_nan(v.w);
+  if (!d.fast || nan) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xe = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+      o[e >> 2] |= (uint32_t)e4m3_encode_one(xe / d.s) << (8 * (e & 3));
+    }
+    return make_uint2(o[0], o[1]);
+  }
+  uint32_t c0 = e4m3_pack4_mag(static_quotient_abs(bf16_lo(v.x), d),
+                               static_quotient_abs(bf16_hi(v.x), d),
+                               static_quotient_abs(bf16_lo(v.y), d),
+                               static_quotient_abs(bf16_hi(v.y), d));
+  uint32_t c1 = e4m3_pack4_mag(static_quotient_abs(bf16_lo(v.z), d),
+                               static_quotient_abs(bf16_hi(v.z), d),
+                               static_quotient_abs(bf16_lo(v.w), d),
+                               static_quotient_abs(bf16_hi(v.w), d));
+  c0 |= bf16x4_signs(v.x, v.y) ^ d.sign;
+  c1 |= bf16x4_signs(v.z, v.w) ^ d.sign;
+  return make_uint2(c0, c1);
+}
+
 // Largest |x| of 8 bf16 values, as fp32 bits.
 __device__ __forceinline__ uint32_t absmax8_bits(const uint4 v) {
   uint32_t a = bf16x2_absmax_bits(v.x);

@@ -45,4 +45,15 @@ hipError_t launch_linear_decode(const uint16_t* x, int64_t ld_x, const uint8_t* 
                                 const float* sw, int64_t ld_sw, uint16_t* out, int64_t ld_out,
                                 int64_t M, int64_t N, int64_t K, hipStream_t st);
 
+// FP8 KV-cache codec: HD = heads * head_dim values per token (multiple of 8),
+// capacity = blocks * block_size slots; out-of-range slots are skipped on
+// write and read as zeros.
+hipError_t launch_kv_write(const uint16_t* k, int64_t ld_k, const uint16_t* v, int64_t ld_v,
+                           const int64_t* slots, int64_t T, int64_t HD, uint8_t* kc, uint8_t* vc,
+                           int64_t capacity, const float* k_scale, const float* v_scale,
+                           hipStream_t st);
+hipError_t launch_kv_read(const uint8_t* cache, int64_t capacity, int64_t HD, const int64_t* slots,
+                          int64_t T, const float* scale, uint16_t* out, int64_t ld_out,
+                          hipStream_t st);
+
 }  // namespace fp8k

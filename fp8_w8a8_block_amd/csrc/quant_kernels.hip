@@ -179,27 +179,20 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 // ---------------------------------------------------------------------------
 // Static quantization with a calibrated scale held in device memory
 // ("[vLLM] FP8", scaling strategies: static per-tensor): code = E4M3(x / s)
-// with the IEEE fp32 quotient (the compiler's correctly rounded division;
-// the scale is not derived from the data, so the bounded-quotient method of
-// the dynamic kernels does not apply) and the saturating, NaN-aware element
-// encoder.  Grid-stride over 16-byte chunks.
+// with the IEEE fp32 quotient, formed by the static-divisor steps (one
+// reciprocal per thread and one FMA correction per element, exact for every
+// normal scale; other scales divide directly), saturating and NaN-aware.
+// Grid-stride over 16-byte chunks.
 __global__ __launch_bounds__(256) void quant_static_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
     const float* __restrict__ scale, uint32_t chunks_per_row, uint64_t nchunks) {
-  const float sc = scale[0];
+  const StaticDivisor d = make_static_divisor(scale[0]);
   for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < nchunks;
        i += (uint64_t)gridDim.x * 256u) {
     const uint64_t row = i / chunks_per_row;
     const uint64_t c = i - row * chunks_per_row;
     const uint4 v = *reinterpret_cast<const uint4*>(x + row * ld_x + c * 8u);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t out[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float xe = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-      out[e >> 2] |= (uint32_t)e4m3_encode_one(xe / sc) << (8 * (e & 3));
-    }
-    *reinterpret_cast<uint2*>(q + row * ld_q + c * 8u) = make_uint2(out[0], out[1]);
+    *reinterpret_cast<uint2*>(q + row * ld_q + c * 8u) = quant8_static(v, d);
   }
 }
 

@@ -49,7 +49,8 @@ extern "C" {
 typedef enum {
   FP8_OK = 0,
   FP8_ERR_NULL = 1,       /* a required pointer is NULL */
-  FP8_ERR_SHAPE = 2,      /* K or N not a positive multiple of 128, M < 0, or too large */
+  FP8_ERR_SHAPE = 2,      /* K or N not a positive multiple of 128, M < 0, a KV-cache
+                             shape out of range, or too large */
   FP8_ERR_STRIDE = 3,     /* a leading dimension is smaller than the row length */
   FP8_ERR_ALIGN = 4,      /* pointer or leading-dimension alignment */
   FP8_ERR_BLOCK = 5,      /* weight block size other than 128 x 128 */
@@ -187,6 +188,49 @@ fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
 fp8_status fp8_quant_act_static(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                                 uint8_t* q, int64_t ld_q, const float* scale, void* stream);
 
+/* fp8_kv_cache_write -- quantize one step's keys and values into a paged
+ * FP8 KV cache.  With an fp8 KV-cache dtype keys and values are stored as
+ * E4M3, halving the cache, each with its own scale: 1.0 by default (large
+ * values clip) or calibrated ("FP8 Quantization", D.4; "[vLLM] FP8", KV
+ * cache quantization; "Quantization guide for serving: FP8, AWQ, GPTQ",
+ * KV-cache FP8 section).
+ *   key, value    [T, H, D] bf16; the H * D values of a token are
+ *                 contiguous, tokens ld_key / ld_value elements apart  (input)
+ *   slot_mapping  [T] int64: the cache slot of each token,
+ *                 slot = block * block_size + offset                   (input)
+ *   key_cache, value_cache  [num_blocks, block_size, H, D] E4M3 codes,
+ *                 contiguous; only the slots named are written    (in/out)
+ *   k_scale, v_scale  one fp32 each in device memory                   (input)
+ *   cache[slot(t)][h][d] = E4M3_RNE_saturating(fp32(x[t][h][d]) / scale),
+ *   the quotient an IEEE fp32 division (as fp8_quant_act_static).  A token
+ *   whose slot is negative (padding) or >= num_blocks * block_size is not
+ *   stored; two tokens with one slot leave either token's codes.
+ *   H * D a multiple of 8; key, value and the caches 16-byte aligned, ld_key
+ *   and ld_value multiples of 8.  The caches may be NULL when
+ *   num_blocks == 0.  T == 0 does nothing.  No workspace. */
+fp8_status fp8_kv_cache_write(const uint16_t* key, int64_t ld_key, const uint16_t* value,
+                              int64_t ld_value, const int64_t* slot_mapping, int64_t T,
+                              int64_t H, int64_t D, uint8_t* key_cache, uint8_t* value_cache,
+                              int64_t num_blocks, int64_t block_size, const float* k_scale,
+                              const float* v_scale, void* stream);
+
+/* fp8_kv_cache_read -- gather tokens from a paged FP8 cache (either one)
+ * and restore them to bf16, as an attention backend without FP8 support
+ * does before it reads the cache ("Quantization guide for serving: FP8,
+ * AWQ, GPTQ", KV-cache FP8 section).
+ *   cache   [num_blocks, block_size, H, D] E4M3 codes, contiguous       (input)
+ *   slots   [T] int64 cache slots                                       (input)
+ *   scale   one fp32 in device memory: the scale the codes were written
+ *           with                                                        (input)
+ *   out     [T, H, D] bf16, tokens ld_out elements apart               (output)
+ *   out[t][h][d] = bf16_RNE(fp32(decode(code)) * scale), one fp32 multiply
+ *   and one rounding; a NaN result is the quiet bf16 NaN with the code's
+ *   sign.  A token whose slot is out of range reads zeros.  Alignment as for
+ *   fp8_kv_cache_write; no workspace. */
+fp8_status fp8_kv_cache_read(const uint8_t* cache, int64_t num_blocks, int64_t block_size,
+                             int64_t H, int64_t D, const int64_t* slots, int64_t T,
+                             const float* scale, uint16_t* out, int64_t ld_out, void* stream);
+
 /* Host-only validation: the argument checks of the calls above, in the
  * same order, without touching any device (no device check, no launch). */
 fp8_status fp8_validate_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
@@ -205,6 +249,17 @@ fp8_status fp8_validate_block_gemm(const uint8_t* a_q, int64_t ld_a, const float
                                    int scale_mode);
 fp8_status fp8_validate_quant_act_static(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                                          const uint8_t* q, int64_t ld_q, const float* scale);
+fp8_status fp8_validate_kv_cache_write(const uint16_t* key, int64_t ld_key,
+                                       const uint16_t* value, int64_t ld_value,
+                                       const int64_t* slot_mapping, int64_t T, int64_t H,
+                                       int64_t D, const uint8_t* key_cache,
+                                       const uint8_t* value_cache, int64_t num_blocks,
+                                       int64_t block_size, const float* k_scale,
+                                       const float* v_scale);
+fp8_status fp8_validate_kv_cache_read(const uint8_t* cache, int64_t num_blocks,
+                                      int64_t block_size, int64_t H, int64_t D,
+                                      const int64_t* slots, int64_t T, const float* scale,
+                                      const uint16_t* out, int64_t ld_out);
 
 /* fp8_e4m3_encode_f32 -- the device element encoder on its own.
  * codes[i] = E4M3 of x[i]: round to nearest even, magnitudes above 448 and

@@ -32,7 +32,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -178,6 +178,68 @@ def test_validate_quant_act_static():
     assert vs(s=S + 2) == ALIGN
     assert vs(q=X + 64) == ALIAS
     assert vs(s=Q + 16) == ALIAS                                # scale inside the codes
+
+
+KC = 0x60_0000_0000
+VC = 0x70_0000_0000
+SL = 0x80_0000_0000
+KS = 0x90_0000_0000
+VS = 0x90_0000_0010
+
+
+def vkw(k=X, ld_k=None, v=O, ld_v=None, sl=SL, T=37, H=8, D=128, kc=KC, vc=VC, nb=5, bs=16,
+        ks=KS, vs=VS):
+    ld_k = H * D if ld_k is None else ld_k
+    ld_v = H * D if ld_v is None else ld_v
+    return _lib.lib().fp8_validate_kv_cache_write(k, ld_k, v, ld_v, sl, T, H, D, kc, vc, nb, bs,
+                                                  ks, vs)
+
+
+def test_validate_kv_cache_write():
+    assert vkw() == OK
+    assert vkw(T=0, k=None, v=None, sl=None, kc=None, vc=None, ks=None, vs=None) == OK
+    assert vkw(nb=0, kc=None, vc=None) == OK                    # nothing can be stored
+    assert vkw(kc=None) == NULL
+    assert vkw(ks=None) == NULL
+    assert vkw(sl=None) == NULL
+    assert vkw(T=-1) == SHAPE
+    assert vkw(H=0) == SHAPE
+    assert vkw(H=1, D=12) == SHAPE                              # H * D not a multiple of 8
+    assert vkw(H=3, D=8) == OK
+    assert vkw(bs=0) == SHAPE
+    assert vkw(nb=-1) == SHAPE
+    assert vkw(ld_k=1000) == STRIDE
+    assert vkw(ld_k=1032) == OK                                 # tokens of a wider row
+    assert vkw(ld_v=1028) == ALIGN
+    assert vkw(k=X + 8) == ALIGN
+    assert vkw(kc=KC + 8) == ALIGN
+    assert vkw(sl=SL + 4) == ALIGN
+    assert vkw(ks=KS + 2) == ALIGN
+    assert vkw(vc=KC + 4096) == ALIAS                           # the two caches overlap
+    assert vkw(kc=X + 2048) == ALIAS                            # cache over the keys
+    assert vkw(sl=VC + 64) == ALIAS
+    assert vkw(k=X, v=X) == OK                                  # inputs may coincide
+    assert vkw(nb=1 << 31) == SHAPE
+
+
+def vkr(c=KC, nb=5, bs=16, H=8, D=128, sl=SL, T=37, s=KS, out=O, ld_out=None):
+    ld_out = H * D if ld_out is None else ld_out
+    return _lib.lib().fp8_validate_kv_cache_read(c, nb, bs, H, D, sl, T, s, out, ld_out)
+
+
+def test_validate_kv_cache_read():
+    assert vkr() == OK
+    assert vkr(T=0, c=None, sl=None, s=None, out=None) == OK
+    assert vkr(nb=0, c=None) == OK                              # every token reads zeros
+    assert vkr(out=None) == NULL
+    assert vkr(s=None) == NULL
+    assert vkr(D=4, H=1) == SHAPE
+    assert vkr(ld_out=512) == STRIDE
+    assert vkr(ld_out=1028) == ALIGN
+    assert vkr(out=O + 2) == ALIGN
+    assert vkr(c=KC + 8) == ALIGN
+    assert vkr(out=KC + 1024) == ALIAS                          # output over the cache
+    assert vkr(out=SL - 64) == ALIAS                            # output over the slots
 
 
 def test_binding_rejects_host_tensors():

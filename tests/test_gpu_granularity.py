@@ -143,6 +143,24 @@ def test_static_scales(scale):
     assert_equal_codes(got, quant.quant_static_ref(bits, np.float32(scale)), f"scale {scale}")
 
 
+# scales at the edges of the one-reciprocal quotient path: smallest and
+# largest normal, an all-ones mantissa, negative, and seeded mantissas
+# across the exponent range
+_EDGE_SCALES = [2.0 ** -126, 3.4028234663852886e38, 1.9999998807907104, -0.37, -2.0 ** -126,
+                448.0, 1.0 / 448.0] + [float(v) for v in np.float32(
+                    np.random.default_rng(41).uniform(1, 2, 8) *
+                    2.0 ** np.random.default_rng(42).integers(-120, 120, 8))]
+
+
+@pytest.mark.parametrize("scale", _EDGE_SCALES)
+def test_static_every_bf16_pattern(scale):
+    # all 65536 bf16 inputs, shuffled so NaN and infinite inputs share
+    # 8-value chunks with ordinary ones
+    allb = np.random.default_rng(43).permutation(65536).astype(np.uint16).reshape(64, 1024)
+    s = np.float32(scale)
+    assert_equal_codes(_static(allb, s), quant.quant_static_ref(allb, s), f"scale {scale!r}")
+
+
 def test_static_division_adversarial():
     # the adversarial (amax, x) pairs with s = fp32(amax) / 448 as the static scale
     pairs = json.load(open(os.path.join(GOLDEN, "div_adversarial.json")))["pairs_amax_bits_x_bits"]

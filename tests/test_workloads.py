@@ -44,3 +44,20 @@ def test_edge_cases_shapes():
     x = synth.bf16_bits_to_f32_input(e["all_amax"]).reshape(-1, 128)
     amax = np.abs(x).max(axis=1)
     assert len(np.unique(amax[amax > 0])) == 32639
+
+
+def test_kv_slots_are_paged_and_distinct():
+    d = synth.make_kv(6, 300, 2, 16, block_size=16, num_blocks=64, n_seqs=7, pad_frac=0.1)
+    assert d["key"].shape == d["value"].shape == (300, 2, 16)
+    s = d["slots"]
+    live = s[s >= 0]
+    assert 0 < (s < 0).sum() < 60
+    assert len(np.unique(live)) == len(live) and live.max() < 64 * 16
+    # without padding every token has a slot and consecutive tokens of a
+    # sequence sit at consecutive offsets of one block
+    d = synth.make_kv(6, 64, 1, 8, block_size=16, num_blocks=8, n_seqs=2)
+    s = d["slots"]
+    assert (s >= 0).all()
+    for seq in (s[:32], s[32:]):
+        assert (seq[:16] // 16 == seq[0] // 16).all() and (seq[:16] % 16 == np.arange(16)).all()
+    assert np.array_equal(synth.make_kv(6, 64, 1, 8, 16, 8, 2)["key"], d["key"])

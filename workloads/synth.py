@@ -15,13 +15,21 @@ Recipe (shapes and distributions of the workloads):
     M in {1, 4, 16} share the channels.
   * The MLP down-projection input is x * sigmoid(x), x ~ N(0, 2), computed in
     float64 before the bf16 rounding (a SiLU-like heavy right tail).
+  * KV cache (``make_kv``), seeded ``[cfg, 3, T]``: keys N(0, 1) with a few
+    head-dimension channels (the same ones in every head) multiplied by an
+    outlier factor, values N(0, 1), both [T, H, D] bf16; T tokens split
+    evenly over n_seqs sequences, each sequence's tokens filling its own
+    blocks in order, the blocks drawn without replacement from the whole
+    pool (a paged cache whose blocks are scattered); a seed-chosen fraction
+    of tokens gets slot -1 (padding).
 """
 
 import numpy as np
 
 __all__ = [
     "CONFIGS", "f32_to_bf16_bits", "bf16_bits_to_f32_input", "make_weight",
-    "make_activation", "make_config", "outlier_channels", "edge_activations",
+    "make_activation", "make_config", "outlier_channels", "edge_activations", "KV_CONFIG",
+    "make_kv",
 ]
 
 
@@ -51,6 +59,40 @@ CONFIGS = {
     "large":    dict(cfg=5, M=8192, K=8192,  N=28672, a_kind="normal", a_std=1.0, w_std=0.01,
                      n_outliers=None, outlier_mult=100.0),
 }
+
+
+# paged FP8 KV cache: 8 KV heads of 128 (a grouped-query 8B-class model),
+# 16-token blocks, a 1 GiB pool per cache, 64 sequences of 1024 tokens
+KV_CONFIG = dict(cfg=6, T=65536, H=8, D=128, block_size=16, num_blocks=65536, n_seqs=64,
+                 key_outlier_dims=4, key_outlier_mult=20.0, pad_frac=0.0)
+
+
+def make_kv(cfg, T, H, D, block_size, num_blocks, n_seqs, key_outlier_dims=4,
+            key_outlier_mult=20.0, pad_frac=0.0):
+    """Return dict(key=bits [T,H,D], value=bits [T,H,D], slots=int64 [T])."""
+    rng = np.random.default_rng([cfg, 3, T])
+    key = rng.standard_normal((T, H, D), dtype=np.float32)
+    if key_outlier_dims:
+        dims = rng.choice(D, size=min(key_outlier_dims, D), replace=False)
+        key[:, :, dims] *= np.float32(key_outlier_mult)
+    value = rng.standard_normal((T, H, D), dtype=np.float32)
+    lens = np.full(n_seqs, T // n_seqs, dtype=np.int64)
+    lens[: T % n_seqs] += 1
+    need = int(sum(-(-int(n) // block_size) for n in lens))
+    if need > num_blocks:
+        raise ValueError(f"{need} blocks needed, pool has {num_blocks}")
+    pool = rng.permutation(num_blocks)[:need]
+    slots = np.empty(T, dtype=np.int64)
+    t = b = 0
+    for n in lens:
+        i = np.arange(n)
+        blk = pool[b + i // block_size]
+        slots[t:t + n] = blk * block_size + i % block_size
+        t += int(n)
+        b += -(-int(n) // block_size)
+    if pad_frac > 0:
+        slots[rng.random(T) < pad_frac] = -1
+    return dict(key=f32_to_bf16_bits(key), value=f32_to_bf16_bits(value), slots=slots)
 
 
 def outlier_channels(cfg, K, n_outliers=None):
