@@ -1,7 +1,8 @@
 """Benchmark of the FP8 W8A8 linear hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload decode|prefill|mlp_down|mlp_down_tensor|large|tiny|kv_cache]
+                    [--workload decode|prefill|mlp_down|mlp_down_tensor|large|tiny|kv_cache|
+                                moe_decode|moe_prefill]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 dynamic activation quantization followed by the block-scaled GEMM (weights
@@ -23,6 +24,11 @@ the keys and values of 65536 tokens (8 heads of 128) as E4M3 codes into two
 paged 1 GiB caches and restores to bf16 the tokens the previous step stored
 (two input batches alternate, so the codes read back have been pushed out of
 the Infinity Cache by a step's worth of other traffic).
+
+The moe_decode and moe_prefill workloads time one GPU's expert shard of an
+FP8 MoE layer (32 of 256 experts, hidden 7168, fused gate and up projection
+N = 4096, top-8 routing): a step quantizes the routed rows of a 256-token
+decode batch or an 8192-token prefill chunk and runs the grouped GEMM.
 
 Prints ONE JSON line.
 """
@@ -70,6 +76,10 @@ def kernel_source_hash(workload=None):
 def dominant_kernel(workload, decode):
     if workload == "kv_cache":
         return "kv_write_kernel"
+    if workload == "moe_decode":
+        return "gemm_grouped_decode_kernel"
+    if workload == "moe_prefill":
+        return "gemm_prefill_asm_kernel"
     # the prefill-shaped workloads all have K % 512 == 0 and M > 64: the
     # hand-scheduled kernel
     return "gemm_decode_kernel" if decode or workload == "tiny" else "gemm_prefill_asm_kernel"
@@ -111,7 +121,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode",
                    choices=["decode", "prefill", "mlp_down", "mlp_down_tensor", "large", "tiny",
-                            "kv_cache"])
+                            "kv_cache", "moe_decode", "moe_prefill"])
     p.add_argument("--cpu-baseline-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample (0 disables it)")
     p.add_argument("--no-secondary", action="store_true",
@@ -491,6 +501,180 @@ def main_kv(args):
     print(json.dumps(line), flush=True)
 
 
+class MoEWorkload:
+    """One GPU's expert shard of an FP8 MoE layer: the routed rows of one
+    batch, grouped by expert, through dynamic 1x128 quantization and the
+    grouped block GEMM against 32 experts' 128x128-block FP8 weights."""
+
+    def __init__(self, name):
+        import torch
+        import fp8_w8a8_block_amd as fp8
+        from workloads import synth
+        self.fp8 = fp8
+        self.name = name
+        c = synth.MOE_CONFIGS[name]
+        self.c = c
+        self.E, self.N, self.K = c["experts_local"], c["N"], c["K"]
+        rows, offsets = synth.make_moe_routing(c["cfg"], c["tokens"], c["top_k"],
+                                               c["experts_total"], self.E)
+        self.offsets_host = offsets
+        self.M = len(rows)
+        tok = synth.make_moe_tokens(c["cfg"], c["tokens"], self.K, c["n_outliers"],
+                                    c["outlier_mult"])
+        self.a_bits = tok[rows]
+        self.x = dev_bf16(self.a_bits)
+        self.wq = torch.empty((self.E, self.N, self.K), dtype=torch.uint8, device="cuda")
+        self.ws = torch.empty((self.E, self.N // 128, self.K // 128), dtype=torch.float32,
+                              device="cuda")
+        for e in range(self.E):
+            q, sc = fp8.quant_weight_block(dev_bf16(synth.make_moe_weight(c["cfg"], e, self.N,
+                                                                          self.K, c["w_std"])))
+            self.wq[e].copy_(q)
+            self.ws[e].copy_(sc)
+        self.offsets = torch.from_numpy(offsets).cuda()
+        self.aq = torch.empty((self.M, self.K), dtype=torch.uint8, device="cuda")
+        self.as_ = torch.empty((self.M, self.K // 128), dtype=torch.float32, device="cuda")
+        self.out = torch.empty((self.M, self.N), dtype=torch.bfloat16, device="cuda")
+        fp8.quant_act(self.x, "block", q=self.aq, scales=self.as_)
+        torch.cuda.synchronize()
+        self.active = int((np.diff(offsets) > 0).sum())
+
+    def step(self, s):
+        self.fp8.quant_act(self.x, "block", q=self.aq, scales=self.as_)
+        self.gemm()
+
+    def gemm(self):
+        self.fp8.grouped_gemm(self.aq, self.as_, self.wq, self.ws, self.offsets, out=self.out)
+
+    def gemm_bytes(self):
+        """Each operand once: A codes and scales, the weights and weight
+        scales of the experts that have rows, the bf16 output."""
+        M, N, K = self.M, self.N, self.K
+        return (M * K + 4 * M * (K // 128) + self.active * (N * K + 4 * (N // 128) * (K // 128)) +
+                2 * M * N)
+
+    def flops(self):
+        return 2 * self.M * self.N * self.K
+
+
+def moe_cpu_baseline(wl, target_s):
+    """The oracle on the host: quantize and multiply up to 64 rows of each of
+    two experts against those experts' full weights (quantized beforehand)."""
+    from oracle import moe, quant
+    from workloads import synth
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = os.cpu_count() or 1
+    counts = np.diff(wl.offsets_host)
+    experts = [int(e) for e in np.argsort(-counts)[:2]]
+    wq, ws = zip(*[quant.quant_weight_block_ref(synth.make_moe_weight(wl.c["cfg"], e, wl.N, wl.K,
+                                                                      wl.c["w_std"]))
+                   for e in experts])
+    wq, ws = np.stack(wq), np.stack(ws)
+    rows = [np.arange(wl.offsets_host[e], wl.offsets_host[e] + min(64, counts[e])) for e in experts]
+    sub_off = np.array([0, len(rows[0]), len(rows[0]) + len(rows[1])])
+    a_bits = wl.a_bits[np.concatenate(rows)]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        aq, as_ = quant.quant_act_ref(a_bits)
+        moe.grouped_gemm_ref(aq, as_, wq, ws, sub_off)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    m = int(sub_off[-1])
+    sample = (f"oracle quant_act + grouped GEMM of {m} rows (up to 64 of each of the two busiest "
+              f"experts) against their full {wl.N}x{wl.K} weights, repeated {reps}x; weights "
+              "quantized beforehand")
+    if wl.name == "moe_decode":
+        nbytes = reps * (3 * m * wl.K + 2 * (wl.N * wl.K + 4 * (wl.N // 128) * (wl.K // 128)) +
+                         2 * m * wl.N)
+        return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": sample, "seconds": round(el, 2)}
+    return {"value": reps * 2 * m * wl.N * wl.K / el / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "sample": sample, "seconds": round(el, 2)}
+
+
+def main_moe(args):
+    import torch
+    calibration_copy()
+    wl = MoEWorkload(args.workload)
+    for s in range(args.warmup):
+        wl.step(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            wl.step(0)
+    torch.cuda.current_stream().wait_stream(stream)
+    g.replay()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for s in range(K):
+        g.replay()
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    n_l = 20
+    g_ms = time_launches(lambda i: wl.gemm(), n_l)
+    decode = wl.name == "moe_decode"
+    if decode:
+        step_bytes = quant_bytes(wl.M, wl.K) + wl.gemm_bytes()
+        value, unit = step_bytes / (sec / K) / 1e9, "GB/s"
+    else:
+        value, unit = wl.flops() / (sec / K) / 1e12, "TFLOP/s"
+    # the roof that binds: every expert's weight must come from HBM, so at
+    # these row counts (2 * rows / experts FLOP per weight byte, below the
+    # chip's 625 FLOP/B) the grouped GEMM is bound by HBM, not by the MFMA
+    if wl.gemm_bytes() / HBM_PEAK_GBS / 1e9 >= wl.flops() / FP8_PEAK_TFLOPS / 1e12:
+        roof = {"bound": "hbm", "achieved": wl.gemm_bytes() / (g_ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "algorithmic_bytes_per_launch": wl.gemm_bytes(),
+                "tflops": wl.flops() / (g_ms * 1e-3) / 1e12}
+    else:
+        roof = {"bound": "mfma", "achieved": wl.flops() / (g_ms * 1e-3) / 1e12,
+                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "flop_per_launch": wl.flops()}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(args.workload)
+    roof["kernel"] = dominant_kernel(args.workload, decode)
+    roof["avg_launch_us"] = g_ms * 1e3
+    roof["launches_timed"] = n_l
+    roof["kernel_source_hash"] = kernel_source_hash(args.workload)
+    cpu = moe_cpu_baseline(wl, args.cpu_baseline_seconds) if args.cpu_baseline_seconds > 0 else None
+    counts = np.diff(wl.offsets_host)
+    line = {
+        "metric": ("FP8 block-scaled MoE grouped GEMM " +
+                   ("GB/s (decode)" if decode else "TFLOPS (prefill)") +
+                   " as % of MI355X roofline"),
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": sec / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp8e4m3 -> fp32 accumulate -> bf16",
+        "data": "synthetic (seeded numpy, skewed top-k routing)",
+        "config": {"workload": args.workload, "tokens": wl.c["tokens"], "top_k": wl.c["top_k"],
+                   "experts_total": wl.c["experts_total"], "experts_local": wl.E,
+                   "rows": wl.M, "rows_per_expert_min_mean_max": [int(counts.min()),
+                                                                  float(counts.mean()),
+                                                                  int(counts.max())],
+                   "N": wl.N, "K": wl.K, "scales": "A 1x128, W 128x128 per expert",
+                   "step": "quant_act of the routed rows + grouped GEMM"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "step_flop": wl.flops(),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -501,6 +685,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.workload == "kv_cache":
         return main_kv(args)
+    if args.workload.startswith("moe_"):
+        return main_moe(args)
     calibration_copy()
     wl = Workload(args.workload)
     decode = len(wl.Ms) > 1

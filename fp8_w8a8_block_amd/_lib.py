@@ -51,6 +51,10 @@ _SIGS = {
                           _sz, _vp]),
     "fp8_quant_act_static": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "fp8_validate_quant_act_static": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp]),
+    "fp8_grouped_gemm": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                _i64, _i64, _i64, _vp]),
+    "fp8_validate_grouped_gemm": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                         _vp, _i64, _i64, _i64, _i64]),
     "fp8_kv_cache_write": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp, _i64,
                                   _i64, _vp, _vp, _vp]),
     "fp8_kv_cache_read": (_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp]),
@@ -250,6 +254,41 @@ def quant_act_static(x, scale, q=None):
         _check(lib().fp8_quant_act_static(x.data_ptr(), M, K, ld_x, q.data_ptr(), ld_q,
                                           scale.data_ptr(), _stream(x)))
     return q
+
+
+def grouped_gemm(a_q, a_s, w_q, w_s, expert_offsets, out=None):
+    """MoE grouped block-scaled GEMM: rows expert_offsets[e] .. [e+1] of the
+    codes a_q [M, K] (scales a_s [M, K/128]) against expert e of w_q
+    [E, N, K] (scales w_s [E, N/128, K/128]) -> bf16 [M, N].  Rows in no
+    expert's range are left as they were in ``out`` (uninitialized when
+    ``out`` is None)."""
+    M, K, ld_a = _rows(a_q, torch.uint8, "a_q")
+    if w_q.dtype != torch.uint8 or w_q.dim() != 3 or not w_q.is_cuda:
+        raise ValueError("w_q must be a uint8 [E, N, K] device tensor")
+    E, N, Kw = w_q.shape
+    if Kw != K:
+        raise ValueError("w_q and a_q disagree on K")
+    if w_q.stride(2) != 1 or w_q.stride(0) != N * w_q.stride(1):
+        raise ValueError("w_q experts must be stacked rows: strides (N * ld_w, ld_w, 1)")
+    ld_w = w_q.stride(1) if N > 1 else K
+    if (w_s.dtype != torch.float32 or w_s.dim() != 3 or not w_s.is_cuda or
+            tuple(w_s.shape[:2]) != (E, N // 128) or w_s.stride(2) != 1 or
+            w_s.stride(0) != (N // 128) * w_s.stride(1)):
+        raise ValueError("w_s must be a float32 [E, N/128, K/128] device tensor, experts stacked")
+    ld_ws = w_s.stride(1) if N // 128 > 1 else w_s.shape[2]
+    if (expert_offsets.dtype != torch.int64 or expert_offsets.dim() != 1 or
+            expert_offsets.shape[0] != E + 1 or not expert_offsets.is_cuda):
+        raise ValueError("expert_offsets must be a 1-D int64 device tensor of E + 1 entries")
+    offs = expert_offsets.contiguous()
+    with torch.cuda.device(a_q.device):
+        if out is None:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+        _check(lib().fp8_grouped_gemm(a_q.data_ptr(), ld_a, a_s.data_ptr(), _ld(a_s),
+                                      w_q.data_ptr(), ld_w, w_s.data_ptr(), ld_ws,
+                                      offs.data_ptr(), E, out.data_ptr(), _rows(out, torch.bfloat16,
+                                                                                "out")[2],
+                                      M, N, K, _stream(a_q)))
+    return out
 
 
 def _scalar_scale(t, name):

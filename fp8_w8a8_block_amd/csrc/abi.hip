@@ -330,6 +330,47 @@ fp8_status fp8_quant_act_static(const uint16_t* x, int64_t M, int64_t K, int64_t
   return launched(fp8k::launch_quant_static(x, M, K, ld_x, q, ld_q, scale, (hipStream_t)stream));
 }
 
+// ---- grouped (MoE) GEMM ---------------------------------------------------
+
+fp8_status fp8_validate_grouped_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s,
+                                     int64_t ld_as, const uint8_t* w_q, int64_t ld_w,
+                                     const float* w_s, int64_t ld_ws,
+                                     const int64_t* expert_offsets, int64_t E, const uint16_t* out,
+                                     int64_t ld_out, int64_t M, int64_t N, int64_t K) {
+  if (E < 0 || E > 65535) return FP8_ERR_SHAPE;
+  if (M < 0 || M >= kMaxDim || !shape_ok_kn(K) || !shape_ok_kn(N)) return FP8_ERR_SHAPE;
+  if (K / 128 > fp8k::kGroupedMaxKB) return FP8_ERR_SHAPE;
+  if (M * K > kMaxElems || M * N > kMaxElems || N * K > kMaxElems / (E > 0 ? E : 1))
+    return FP8_ERR_SHAPE;
+  if (M == 0 || E == 0) return FP8_OK;
+  if (!a_q || !a_s || !w_q || !w_s || !out || !expert_offsets) return FP8_ERR_NULL;
+  const int64_t KB = K / 128;
+  if (ld_a < K || ld_w < K || ld_out < N || ld_as < KB || ld_ws < KB) return FP8_ERR_STRIDE;
+  if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(out, 16)) return FP8_ERR_ALIGN;
+  if (!aligned(a_s, 4) || !aligned(w_s, 4) || !aligned(expert_offsets, 8)) return FP8_ERR_ALIGN;
+  if (ld_a % 16 != 0 || ld_w % 16 != 0 || ld_out % 8 != 0) return FP8_ERR_ALIGN;
+  const Range ro = range_of(out, M, N, ld_out, 2);
+  const Range ins[] = {range_of(a_q, M, K, ld_a, 1), range_of(a_s, M, KB, ld_as, 4),
+                       range_of(w_q, E * N, K, ld_w, 1), range_of(w_s, E * (N / 128), KB, ld_ws, 4),
+                       range_of(expert_offsets, 1, E + 1, E + 1, 8)};
+  for (const Range& r : ins)
+    if (overlap(ro, r)) return FP8_ERR_ALIAS;
+  return FP8_OK;
+}
+
+fp8_status fp8_grouped_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, int64_t ld_as,
+                            const uint8_t* w_q, int64_t ld_w, const float* w_s, int64_t ld_ws,
+                            const int64_t* expert_offsets, int64_t E, uint16_t* out,
+                            int64_t ld_out, int64_t M, int64_t N, int64_t K, void* stream) {
+  fp8_status st = fp8_validate_grouped_gemm(a_q, ld_a, a_s, ld_as, w_q, ld_w, w_s, ld_ws,
+                                            expert_offsets, E, out, ld_out, M, N, K);
+  if (st != FP8_OK || M == 0 || E == 0) return st;
+  if ((st = check_device()) != FP8_OK) return st;
+  return launched(fp8k::launch_grouped_gemm(a_q, ld_a, a_s, ld_as, w_q, ld_w, w_s, ld_ws, out,
+                                            ld_out, expert_offsets, E, M, N, K,
+                                            (hipStream_t)stream));
+}
+
 // ---- FP8 KV-cache codec --------------------------------------------------
 
 namespace {

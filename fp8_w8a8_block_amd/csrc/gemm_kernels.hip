@@ -101,17 +101,17 @@ constexpr size_t decode_lds_bytes(int KB, bool kconst) {
          (kconst ? 0 : (size_t)16 * KB * sizeof(float));
 }
 
+// One 16-column output tile of at most 16 rows (1 <= M <= 16), columns
+// n0 .. n0 + 15; the whole workgroup takes part (it holds barriers).
 template <int KSPLIT, int KBW, bool KCONST>
-__global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
-    const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
-    const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
-    uint16_t* __restrict__ out, int64_t ld_out, int M, int KB) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+__device__ __forceinline__ void decode_tile(
+    uint8_t* lds, const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa,
+    int64_t ld_sa, const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw,
+    int64_t ld_sw, uint16_t* __restrict__ out, int64_t ld_out, int M, int KB, int64_t n0) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int kg = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
   const bool arow = r16 < M;
 
   uint8_t* wbuf = lds + (size_t)wave * (KBW * 2 * kFrag);     // this wave's W fragments
@@ -228,6 +228,51 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
         out[(int64_t)m * ld_out + n0 + r16] = (uint16_t)f32_to_bf16_rne(v);
       }
     }
+  }
+}
+
+template <int KSPLIT, int KBW, bool KCONST>
+__global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
+    const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
+    const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
+    uint16_t* __restrict__ out, int64_t ld_out, int M, int KB) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  decode_tile<KSPLIT, KBW, KCONST>(lds, a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, KB,
+                                   (int64_t)blockIdx.x * 16);
+}
+
+// Clamped row range of expert e in a grouped call: offsets are read as
+// given, then clamped to 0 <= lo <= hi <= M, so no offsets can send an
+// access outside the M rows.
+__device__ __forceinline__ void expert_rows(const int64_t* __restrict__ offsets, int e, int64_t M,
+                                            int64_t& lo, int64_t& hi) {
+  int64_t a = offsets[e], b = offsets[e + 1];
+  lo = a < 0 ? 0 : (a > M ? M : a);
+  hi = b < lo ? lo : (b > M ? M : b);
+}
+
+// Grouped (MoE) GEMM for few rows per expert: workgroup (x, e) computes
+// columns 16 x .. 16 x + 15 of expert e's rows, 16 rows at a time with the
+// decode tile, weight W + e * w_es, scales sw + e * sw_es.  An expert with no
+// rows costs one offsets read.
+template <int KSPLIT, int KBW>
+__global__ __launch_bounds__(64 * KSPLIT) void gemm_grouped_decode_kernel(
+    const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
+    const uint8_t* __restrict__ w, int64_t ld_w, int64_t w_es, const float* __restrict__ sw,
+    int64_t ld_sw, int64_t sw_es, uint16_t* __restrict__ out, int64_t ld_out,
+    const int64_t* __restrict__ offsets, int64_t M, int KB) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int e = blockIdx.y;
+  int64_t lo, hi;
+  expert_rows(offsets, e, M, lo, hi);
+  const uint8_t* we = w + (int64_t)e * w_es;
+  const float* swe = sw + (int64_t)e * sw_es;
+  for (int64_t r = lo; r < hi; r += 16) {
+    if (r > lo) __syncthreads();                      // LDS reuse across row chunks
+    const int m = (int)(hi - r < 16 ? hi - r : 16);
+    decode_tile<KSPLIT, KBW, false>(lds, a + r * ld_a, ld_a, sa + r * ld_sa, ld_sa, we, ld_w, swe,
+                                    ld_sw, out + r * ld_out, ld_out, m, KB,
+                                    (int64_t)blockIdx.x * 16);
   }
 }
 
@@ -675,14 +720,74 @@ __device__ __forceinline__ v4i pf_desc(const void* base, int64_t bytes) {
   return d;
 }
 
+// Grouped (MoE) tile lookup.  Tile numbers run expert by expert; within
+// expert e (t_e = ceil(rows_e / 256) M tiles) the M tile varies fastest, so
+// the t_e tiles that read one weight slab (same expert, same N tile) are
+// neighbours: they land on one XCD together and share the slab in its L2.
+// Every wave runs the same scan (64 experts per step, a wave prefix sum of
+// t_e * tiles_n), so the result is uniform over the workgroup.  Returns
+// false when the tile lies past the last expert's tiles.
+__device__ __forceinline__ bool grouped_tile(const int64_t* __restrict__ offsets, int E,
+                                             int64_t M, int tile, int tiles_n, int& e_out,
+                                             int& tm_out, int& tn_out, int64_t& lo_out,
+                                             int64_t& hi_out) {
+  const int lane = threadIdx.x & 63;
+  // 64-bit counts: even offsets that overlap cannot wrap them
+  long long base = 0;                            // tiles of the experts before this chunk
+  for (int c = 0; c < E; c += 64) {
+    const int e = c + lane;
+    long long t = 0;
+    if (e < E) {
+      int64_t lo, hi;
+      expert_rows(offsets, e, M, lo, hi);
+      t = (hi - lo + kPM - 1) / kPM * tiles_n;
+    }
+    long long incl = t;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const long long v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    const long long excl = incl - t;
+    const unsigned long long own = __ballot(t > 0 && tile >= base + excl && tile < base + incl);
+    if (own) {
+      const int l = __ffsll((long long)own) - 1;
+      const int e_own = __builtin_amdgcn_readfirstlane(c + l);
+      const long long local = (long long)tile - base - __shfl(excl, l, 64);
+      int64_t lo, hi;
+      expert_rows(offsets, e_own, M, lo, hi);
+      const long long te = (hi - lo + kPM - 1) / kPM;
+      // 0 <= local < te * tiles_n by construction; checked anyway
+      if (te <= 0 || local < 0 || local >= te * tiles_n) return false;
+      e_out = e_own;
+      tm_out = __builtin_amdgcn_readfirstlane((int)(local % te));
+      tn_out = __builtin_amdgcn_readfirstlane((int)(local / te));
+      lo_out = lo;
+      hi_out = hi;
+      return true;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  return false;
+}
+
 // NW = 8: 256 x 256 tiles, two waves per SIMD.  NW = 4: 256 x 128 tiles, one
 // wave per SIMD, for grids that would otherwise leave CUs idle (the same
 // 128 x 64 wave tile, so the K loop is the same schedule).
+// E > 0: the grouped (MoE) form, chosen at run time so the K loop exists
+// once per variant (its labels are fixed names).  The grid enumerates the
+// tiles of all experts (rounded up to a multiple of 8; workgroups past the
+// last tile exit at once), consecutive numbers on one XCD; each workgroup
+// finds its expert and tile and then runs the plain kernel on that expert's rows (A, scales and output rebased to the
+// expert's first row, M = its row count) and weight (w + e * w_es, sw +
+// e * sw_es).  The range-checked descriptors end at the expert's last row,
+// so the next expert's rows are neither read nor written.
 template <bool KCONST, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
     const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
-    uint16_t* __restrict__ out, int64_t ld_out, int M, int N, int KB, int tiles_m, int tiles_n) {
+    uint16_t* __restrict__ out, int64_t ld_out, int64_t M_all, int N, int KB, int tiles_m,
+    int tiles_n, const int64_t* __restrict__ offsets, int E, int64_t w_es, int64_t sw_es) {
   constexpr int kTN = 32 * NW;                 // tile width (weight rows)
   constexpr int kWN = NW / 2;                  // waves along N
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kPfLdsBytes];
@@ -695,15 +800,32 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   const int r16 = lane & 15;
   const int kg = lane >> 4;
 
-  // workgroup id -> tile, as gemm_prefill_kernel
-  const int tiles = tiles_m * tiles_n;
-  int lin = blockIdx.x;
-  if (tiles % 8 == 0) lin = (lin % 8) * (tiles / 8) + lin / 8;
-  const int group = lin / (kGroupM * tiles_n);
-  const int first_m = group * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int tm = first_m + (lin % (kGroupM * tiles_n)) % gsize;
-  const int tn = (lin % (kGroupM * tiles_n)) / gsize;
+  int tm, tn;
+  int M = (int)M_all;
+  if (E > 0) {
+    // gridDim.x is a multiple of 8: consecutive tiles share an XCD
+    const int G = (int)gridDim.x;
+    const int lin = (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8);
+    int e;
+    int64_t lo, hi;
+    if (!grouped_tile(offsets, E, M_all, lin, tiles_n, e, tm, tn, lo, hi)) return;
+    a += lo * ld_a;
+    sa += lo * ld_sa;
+    out += lo * ld_out;
+    w += (int64_t)e * w_es;
+    sw += (int64_t)e * sw_es;
+    M = (int)(hi - lo);
+  } else {
+    // workgroup id -> tile, as gemm_prefill_kernel
+    const int tiles = tiles_m * tiles_n;
+    int lin = blockIdx.x;
+    if (tiles % 8 == 0) lin = (lin % 8) * (tiles / 8) + lin / 8;
+    const int group = lin / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gsize = min(tiles_m - first_m, kGroupM);
+    tm = first_m + (lin % (kGroupM * tiles_n)) % gsize;
+    tn = (lin % (kGroupM * tiles_n)) / gsize;
+  }
   const int64_t m0 = (int64_t)tm * kPM;
   const int64_t n0 = (int64_t)tn * kTN;
 
@@ -822,13 +944,32 @@ hipError_t launch_prefill_asm(const uint8_t* a, int64_t ld_a, const float* sa, i
   const int tiles_n = (int)((N + 32 * NW - 1) / (32 * NW));
   dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n);
   if (kconst)
-    hipLaunchKernelGGL((gemm_prefill_asm_kernel<true, NW>), grid, dim3(64 * NW), 0, st, a, ld_a,
-                       sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, (int)N, KB, tiles_m,
-                       tiles_n);
+    hipLaunchKernelGGL((gemm_prefill_asm_kernel<true, NW>), grid, dim3(64 * NW), 0, st, a,
+                       ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, (int)N, KB, tiles_m,
+                       tiles_n, nullptr, 0, (int64_t)0, (int64_t)0);
   else
-    hipLaunchKernelGGL((gemm_prefill_asm_kernel<false, NW>), grid, dim3(64 * NW), 0, st, a, ld_a,
-                       sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, (int)N, KB, tiles_m,
-                       tiles_n);
+    hipLaunchKernelGGL((gemm_prefill_asm_kernel<false, NW>), grid, dim3(64 * NW), 0, st, a,
+                       ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, (int)N, KB, tiles_m,
+                       tiles_n, nullptr, 0, (int64_t)0, (int64_t)0);
+  return hipGetLastError();
+}
+
+// Grouped launch: at most floor((M + 255 E) / 256) M tiles over all experts
+// (each expert's last tile may be partial), times the N tiles, rounded up to
+// a multiple of 8.
+template <int NW>
+hipError_t launch_prefill_asm_grouped(const uint8_t* a, int64_t ld_a, const float* sa,
+                                      int64_t ld_sa, const uint8_t* w, int64_t ld_w, int64_t w_es,
+                                      const float* sw, int64_t ld_sw, int64_t sw_es,
+                                      uint16_t* out, int64_t ld_out, const int64_t* offsets,
+                                      int64_t E, int64_t M, int64_t N, int KB, hipStream_t st) {
+  const int64_t tiles_m = (M + (kPM - 1) * E) / kPM;
+  const int64_t tiles_n = (N + 32 * NW - 1) / (32 * NW);
+  const int64_t g = (tiles_m * tiles_n + 7) / 8 * 8;
+  if (g == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_prefill_asm_kernel<false, NW>), dim3((uint32_t)g), dim3(64 * NW),
+                     0, st, a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, (int)N, KB,
+                     (int)tiles_m, (int)tiles_n, offsets, (int)E, w_es, sw_es);
   return hipGetLastError();
 }
 
@@ -1059,6 +1200,48 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
   else
     hipLaunchKernelGGL(gemm_tile_kernel<false>, grid, dim3(256), 0, st, a, ld_a, sa, ld_sa, w, ld_w,
                        sw, ld_sw, out, ld_out, (int)M, KB, tiles_n);
+  return hipGetLastError();
+}
+
+// Grouped (MoE) block-scaled GEMM.  A few rows per expert on average: the
+// decode tile per (16 columns, expert); otherwise the grouped form of the
+// hand-scheduled prefill kernel.
+#ifndef FP8_GROUPED_DECODE_MAX_AVG
+#define FP8_GROUPED_DECODE_MAX_AVG 32
+#endif
+
+static_assert(kGroupedMaxKB <= kDecodeMaxKB, "grouped calls must fit the decode tile");
+
+bool grouped_prefill_ok(int64_t M, int64_t E, int64_t N, int64_t K, int64_t ld_a, int64_t ld_w,
+                        int64_t ld_sa, int64_t ld_sw, int64_t ld_out) {
+  const int64_t KB = K / 128;
+  return FP8_PREFILL_ASM && M > FP8_GROUPED_DECODE_MAX_AVG * E && KB % kPfKbGroup == 0 &&
+         KB <= kPrefillMaxKB && ld_a < kPrefillMaxLd && ld_w < kPrefillMaxLd &&
+         ld_out < kPrefillMaxLd / 2 && ld_sa < kPrefillMaxLd / 4 && ld_sw < kPrefillMaxLd &&
+         (M + (kPM - 1) * E) / kPM * (N / 128) < ((int64_t)1 << 31);
+}
+
+hipError_t launch_grouped_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
+                               const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
+                               uint16_t* out, int64_t ld_out, const int64_t* offsets, int64_t E,
+                               int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int KB = (int)(K / 128);
+  const int64_t w_es = N * ld_w;                   // expert strides
+  const int64_t sw_es = (N / 128) * ld_sw;
+  if (grouped_prefill_ok(M, E, N, K, ld_a, ld_w, ld_sa, ld_sw, ld_out)) {
+    const int64_t tiles256 = ((M + (kPM - 1) * E) / kPM) * ((N + kPN - 1) / kPN);
+    if (2 * tiles256 <= device_cus())
+      return launch_prefill_asm_grouped<4>(a, ld_a, sa, ld_sa, w, ld_w, w_es, sw, ld_sw, sw_es,
+                                           out, ld_out, offsets, E, M, N, KB, st);
+    return launch_prefill_asm_grouped<8>(a, ld_a, sa, ld_sa, w, ld_w, w_es, sw, ld_sw, sw_es, out,
+                                         ld_out, offsets, E, M, N, KB, st);
+  }
+  constexpr int KSPLIT = FP8_DECODE_KSPLIT, KBW = FP8_DECODE_KBW;
+  dim3 grid((uint32_t)(N / 16), (uint32_t)E);
+  const size_t lds = decode_lds_bytes<KSPLIT, KBW>(KB, false);
+  hipLaunchKernelGGL((gemm_grouped_decode_kernel<KSPLIT, KBW>), grid, dim3(64 * KSPLIT), lds, st,
+                     a, ld_a, sa, ld_sa, w, ld_w, w_es, sw, ld_sw, sw_es, out, ld_out, offsets, M,
+                     KB);
   return hipGetLastError();
 }
 

@@ -45,6 +45,18 @@ hipError_t launch_linear_decode(const uint16_t* x, int64_t ld_x, const uint8_t* 
                                 const float* sw, int64_t ld_sw, uint16_t* out, int64_t ld_out,
                                 int64_t M, int64_t N, int64_t K, hipStream_t st);
 
+// largest K / 128 of a grouped call (its decode-tile path stages the
+// activation scales of a row chunk in LDS)
+constexpr int kGroupedMaxKB = 128;
+
+// Grouped (MoE) block-scaled GEMM: rows offsets[e] .. offsets[e + 1] of A
+// (clamped to [0, M]) against expert e's weight w + e * N * ld_w with scales
+// sw + e * (N / 128) * ld_sw.  E >= 1; K <= 16384 (decode-tile path).
+hipError_t launch_grouped_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
+                               const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
+                               uint16_t* out, int64_t ld_out, const int64_t* offsets, int64_t E,
+                               int64_t M, int64_t N, int64_t K, hipStream_t st);
+
 // FP8 KV-cache codec: HD = heads * head_dim values per token (multiple of 8),
 // capacity = blocks * block_size slots; out-of-range slots are skipped on
 // write and read as zeros.

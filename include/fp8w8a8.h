@@ -188,6 +188,36 @@ fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
 fp8_status fp8_quant_act_static(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                                 uint8_t* q, int64_t ld_q, const float* scale, void* stream);
 
+/* fp8_grouped_gemm -- block-scaled FP8 grouped GEMM for a mixture-of-experts
+ * layer: each expert's rows of A against that expert's FP8 weight.  A fused
+ * MoE layer gets its own FP8 method, with expert weights quantized offline
+ * or at load ("[vLLM] FP8", the config's dispatch and its table of methods);
+ * the experts are small matrices ("Quantization guide for serving: FP8,
+ * AWQ, GPTQ", closing section).
+ *   a_q, a_s       [M, K] codes (ld_a) and [M, K/128] scales (ld_as) of the
+ *                  activations, rows grouped by expert (as fp8_quant_act
+ *                  makes them, block mode)                             (input)
+ *   w_q, w_s       E experts stacked: codes [E, N, K] (row stride ld_w,
+ *                  expert e at w_q + e * N * ld_w) and 128 x 128 block scales
+ *                  [E, N/128, K/128] (row stride ld_ws, expert e at
+ *                  w_s + e * (N/128) * ld_ws)                          (input)
+ *   expert_offsets [E + 1] int64 in device memory: expert e owns rows
+ *                  expert_offsets[e] .. expert_offsets[e + 1] - 1      (input)
+ *   out            [M, N] bf16 (ld_out)                                (output)
+ *   out[r, n] = bf16_RNE( sum_kb a_s[r, kb] * w_s[e][n/128, kb] *
+ *                         sum_{k in kb} dec(a_q[r, k]) * dec(w_q[e][n, k]) )
+ *   for every row r of expert e, the same arithmetic as fp8_block_gemm.
+ *   The offsets should be nondecreasing with expert_offsets[0] >= 0 and
+ *   expert_offsets[E] <= M; the device clamps each range to [0, M], so other
+ *   offsets give unspecified rows but no access outside the tensors.  Rows
+ *   in no expert's range are not written.  1 <= E <= 65535, K <= 16384;
+ *   alignment as for fp8_block_gemm.  E == 0 or M == 0 does nothing.  No
+ *   workspace; the routing that groups the rows is the caller's. */
+fp8_status fp8_grouped_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, int64_t ld_as,
+                            const uint8_t* w_q, int64_t ld_w, const float* w_s, int64_t ld_ws,
+                            const int64_t* expert_offsets, int64_t E, uint16_t* out,
+                            int64_t ld_out, int64_t M, int64_t N, int64_t K, void* stream);
+
 /* fp8_kv_cache_write -- quantize one step's keys and values into a paged
  * FP8 KV cache.  With an fp8 KV-cache dtype keys and values are stored as
  * E4M3, halving the cache, each with its own scale: 1.0 by default (large
@@ -249,6 +279,11 @@ fp8_status fp8_validate_block_gemm(const uint8_t* a_q, int64_t ld_a, const float
                                    int scale_mode);
 fp8_status fp8_validate_quant_act_static(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                                          const uint8_t* q, int64_t ld_q, const float* scale);
+fp8_status fp8_validate_grouped_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s,
+                                     int64_t ld_as, const uint8_t* w_q, int64_t ld_w,
+                                     const float* w_s, int64_t ld_ws,
+                                     const int64_t* expert_offsets, int64_t E, const uint16_t* out,
+                                     int64_t ld_out, int64_t M, int64_t N, int64_t K);
 fp8_status fp8_validate_kv_cache_write(const uint16_t* key, int64_t ld_key,
                                        const uint16_t* value, int64_t ld_value,
                                        const int64_t* slot_mapping, int64_t T, int64_t H,

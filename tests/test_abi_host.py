@@ -32,7 +32,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -178,6 +178,38 @@ def test_validate_quant_act_static():
     assert vs(s=S + 2) == ALIGN
     assert vs(q=X + 64) == ALIAS
     assert vs(s=Q + 16) == ALIAS                                # scale inside the codes
+
+
+OFFS = 0xA0_0000_0000
+
+
+def vgg(a=X, ld_a=None, sa=S, ld_as=None, w=Q, ld_w=None, sw=WS, ld_ws=None, off=OFFS, E=4,
+        out=O, ld_out=None, M=40, N=256, K=512):
+    ld_a = K if ld_a is None else ld_a
+    ld_w = K if ld_w is None else ld_w
+    ld_as = K // 128 if ld_as is None else ld_as
+    ld_ws = K // 128 if ld_ws is None else ld_ws
+    ld_out = N if ld_out is None else ld_out
+    return _lib.lib().fp8_validate_grouped_gemm(a, ld_a, sa, ld_as, w, ld_w, sw, ld_ws, off, E,
+                                                out, ld_out, M, N, K)
+
+
+def test_validate_grouped_gemm():
+    assert vgg() == OK
+    assert vgg(M=0, a=None, sa=None) == OK                    # nothing to do
+    assert vgg(E=0, w=None, sw=None, off=None) == OK
+    assert vgg(E=-1) == SHAPE
+    assert vgg(E=65536) == SHAPE
+    assert vgg(K=128 * 129) == SHAPE                          # K <= 16384
+    assert vgg(N=200) == SHAPE
+    assert vgg(off=None) == NULL
+    assert vgg(off=OFFS + 4) == ALIGN
+    assert vgg(ld_ws=3) == STRIDE
+    assert vgg(ld_out=128) == STRIDE
+    assert vgg(ld_a=520) == ALIGN
+    assert vgg(out=Q + 4 * 256 * 512 - 64) == ALIAS           # over the last expert's codes
+    assert vgg(out=Q + 4 * 256 * 512) == OK                   # just past them
+    assert vgg(out=OFFS - 16) == ALIAS                        # over the offsets
 
 
 KC = 0x60_0000_0000

@@ -22,6 +22,14 @@ Recipe (shapes and distributions of the workloads):
     blocks in order, the blocks drawn without replacement from the whole
     pool (a paged cache whose blocks are scattered); a seed-chosen fraction
     of tokens gets slot -1 (padding).
+  * MoE (``make_moe``), seeded ``[cfg, 4]`` for routing, ``[cfg, 5]`` for the
+    token activations (N(0, 1) with outlier channels as above) and
+    ``[cfg, 6, e]`` for expert e's weight (N(0, w_std)): every token picks
+    top_k distinct experts of experts_total, without replacement, with
+    probabilities proportional to a lognormal popularity (sigma 0.6, drawn
+    once: some experts hot, some cold); the experts 0 .. experts_local - 1
+    are this GPU's shard, and their (token, expert) pairs, grouped by expert
+    and ordered by token within an expert, are the rows of the grouped GEMM.
 """
 
 import numpy as np
@@ -29,7 +37,7 @@ import numpy as np
 __all__ = [
     "CONFIGS", "f32_to_bf16_bits", "bf16_bits_to_f32_input", "make_weight",
     "make_activation", "make_config", "outlier_channels", "edge_activations", "KV_CONFIG",
-    "make_kv",
+    "make_kv", "MOE_CONFIGS", "make_moe_routing", "make_moe_tokens", "make_moe_weight",
 ]
 
 
@@ -93,6 +101,49 @@ def make_kv(cfg, T, H, D, block_size, num_blocks, n_seqs, key_outlier_dims=4,
     if pad_frac > 0:
         slots[rng.random(T) < pad_frac] = -1
     return dict(key=f32_to_bf16_bits(key), value=f32_to_bf16_bits(value), slots=slots)
+
+
+# MoE layer, one GPU's expert shard: 256 experts of hidden 7168, the gate and
+# up projections fused (N = 2 * 2048), top-8 routing, 32 experts per GPU
+# (expert parallelism over 8 GPUs); a decode batch and a prefill chunk
+MOE_CONFIGS = {
+    "moe_decode":  dict(cfg=7, tokens=256,  top_k=8, experts_total=256, experts_local=32,
+                        K=7168, N=4096, w_std=0.02, n_outliers=None, outlier_mult=20.0),
+    "moe_prefill": dict(cfg=8, tokens=8192, top_k=8, experts_total=256, experts_local=32,
+                        K=7168, N=4096, w_std=0.02, n_outliers=None, outlier_mult=20.0),
+}
+
+
+def make_moe_routing(cfg, tokens, top_k, experts_total, experts_local):
+    """Routing of one batch: (token index of each row [M], offsets [E_local + 1])."""
+    rng = np.random.default_rng([cfg, 4])
+    logp = rng.standard_normal(experts_total) * 0.6
+    # Gumbel-top-k: top_k distinct experts per token, P(e) proportional to exp(logp[e])
+    g = logp[None, :] - np.log(-np.log(rng.random((tokens, experts_total))))
+    choice = np.argpartition(-g, top_k - 1, axis=1)[:, :top_k]
+    rows, counts = [], []
+    for e in range(experts_local):
+        tok = np.flatnonzero((choice == e).any(axis=1))
+        rows.append(tok)
+        counts.append(len(tok))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return np.concatenate(rows).astype(np.int64), offsets
+
+
+def make_moe_tokens(cfg, tokens, K, n_outliers=None, mult=20.0):
+    """Token activations bf16 bits [tokens, K] ~ N(0, 1), outlier channels times mult."""
+    rng = np.random.default_rng([cfg, 5])
+    x = rng.standard_normal((tokens, K), dtype=np.float32)
+    ch = outlier_channels(cfg, K, n_outliers)
+    if len(ch):
+        x[:, ch] *= np.float32(mult)
+    return f32_to_bf16_bits(x)
+
+
+def make_moe_weight(cfg, e, N, K, std):
+    """Expert e's weight, bf16 bits [N, K] ~ N(0, std)."""
+    rng = np.random.default_rng([cfg, 6, e])
+    return f32_to_bf16_bits(rng.standard_normal((N, K), dtype=np.float32) * np.float32(std))
 
 
 def outlier_channels(cfg, K, n_outliers=None):
