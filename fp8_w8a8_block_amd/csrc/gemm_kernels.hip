@@ -88,8 +88,10 @@ __device__ __forceinline__ v8i zero8() {
 // touch 16 rows x 64 bytes, which streams far below the HBM rate.)  Within
 // a row the eight 16-byte chunks are stored XOR-swizzled by swz(row), so the
 // fragment reads hit distinct banks.  While the MFMAs of batch b run, the loads of batch b+1
-// are in flight.  Activation rows >= M repeat row M - 1 in LDS and are
-// zeroed in registers.  The waves' 16x16 partial sums are reduced in LDS.
+// are in flight.  Activation rows >= M are not copied (the lanes that would
+// copy them are switched off; M = 1 moves 128 bytes per K block instead of
+// 2 KiB) and are zeroed in registers.  The waves' 16x16 partial sums are
+// reduced in LDS.
 //
 // Dynamic LDS: KSPLIT * KBW * 4 KiB operand buffers, then the reduction
 // buffer (KSPLIT * 1 KiB), then the activation scales (16 * KB floats).
@@ -148,8 +150,10 @@ __device__ __forceinline__ void decode_tile(
         const int64_t off = (int64_t)kb * 128;
         dma(wsrc0 + off, wbuf + u * kFrag);
         dma(wsrc1 + off, wbuf + u * kFrag + 1024);
-        dma(asrc0 + off, abuf + u * kFrag);
-        dma(asrc1 + off, abuf + u * kFrag + 1024);
+        // activation rows >= M are never copied: their fragment lanes are
+        // zeroed in registers, whatever the LDS holds
+        if (drow < M) dma(asrc0 + off, abuf + u * kFrag);
+        if (8 + drow < M) dma(asrc1 + off, abuf + u * kFrag + 1024);
       }
     }
   };
