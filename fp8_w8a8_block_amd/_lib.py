@@ -122,9 +122,49 @@ def _ld(t):
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
-def _vec_ld(t):
-    """Element stride of a row-mode scale vector; a single value is stride 0."""
-    return 0 if t.numel() == 1 else t.stride(0)
+def _vec_ld(t, n, name):
+    """Element stride of a row-mode scale vector of n entries (1-D, or 2-D
+    with one dimension of size 1), or 0 for a single value shared by all."""
+    if t.numel() == 1:
+        return 0
+    if t.numel() != n:
+        raise ValueError(f"{name} must hold {n} scales or one, got {t.numel()}")
+    if t.dim() == 1:
+        return t.stride(0)
+    if t.dim() == 2 and 1 in t.shape:
+        return t.stride(0) if t.shape[1] == 1 else t.stride(1)
+    raise ValueError(f"{name} must be a vector")
+
+
+def _device_tensor(t, name, dtype, device, shape=None):
+    """Check a caller-supplied tensor before its pointer goes to a kernel:
+    type, dtype, device and (if given) exact shape."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _scale_matrix(t, name, rows, cols, device):
+    """Block-scale matrix [rows, cols] with unit column stride -> its leading dimension."""
+    _device_tensor(t, name, torch.float32, device, (rows, cols))
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return _ld(t)
+
+
+def _workspace(ws, device):
+    if ws is None:
+        return None, 0
+    _device_tensor(ws, "workspace", torch.uint8, device)
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws.data_ptr(), ws.numel()
 
 
 def workspace_bytes(op, M, N, K, scale_mode):
@@ -142,16 +182,20 @@ def quant_act(x, scale_mode="block", workspace=None, q=None, scales=None):
     with torch.cuda.device(x.device):
         if q is None:
             q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        _device_tensor(q, "q", torch.uint8, x.device, (M, K))
+        ld_q = _rows(q, torch.uint8, "q")[2]
+        shape = (M, K // 128) if mode == SCALE_BLOCK else (M,) if mode == SCALE_ROW else (1,)
         if scales is None:
-            shape = (M, K // 128) if mode == SCALE_BLOCK else (M,) if mode == SCALE_ROW else (1,)
             scales = torch.empty(shape, dtype=torch.float32, device=x.device)
-        ld_s = scales.stride(0) if mode == SCALE_ROW and scales.dim() == 1 else _ld(scales)
-        ld_q = q.stride(0) if q.shape[0] > 1 else q.shape[1]
+        if mode == SCALE_BLOCK:
+            ld_s = _scale_matrix(scales, "scales", M, K // 128, x.device)
+        else:
+            _device_tensor(scales, "scales", torch.float32, x.device, shape)
+            ld_s = scales.stride(0) if mode == SCALE_ROW else 1
         nws = workspace_bytes(OP_QUANT_ACT, M, 0, K, mode)
         if nws and workspace is None:
             workspace = torch.empty(nws, dtype=torch.uint8, device=x.device)
-        ws_ptr = workspace.data_ptr() if workspace is not None else None
-        ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        ws_ptr, ws_len = _workspace(workspace, x.device)
         _check(lib().fp8_quant_act(x.data_ptr(), M, K, ld_x, q.data_ptr(), ld_q,
                                    scales.data_ptr(), ld_s, mode, ws_ptr, ws_len, _stream(x)))
     return q, scales
@@ -179,8 +223,7 @@ def quant_weight_block(w, scale_mode="block", block_n=128, block_k=128, workspac
         nws = workspace_bytes(OP_QUANT_WEIGHT, N, 0, K, mode)
         if nws and workspace is None:
             workspace = torch.empty(nws, dtype=torch.uint8, device=w.device)
-        ws_ptr = workspace.data_ptr() if workspace is not None else None
-        ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        ws_ptr, ws_len = _workspace(workspace, w.device)
         _check(lib().fp8_quant_weight_block(w.data_ptr(), N, K, ld_w, q.data_ptr(), K,
                                             scales.data_ptr(), ld_s, int(block_n), int(block_k),
                                             mode, ws_ptr, ws_len, _stream(w)))
@@ -194,17 +237,23 @@ def block_gemm(a_q, a_s, w_q, w_s, scale_mode="block", out=None):
     N, K2, ld_w = _rows(w_q, torch.uint8, "w_q")
     if K2 != K:
         raise ValueError(f"K mismatch: a_q has {K}, w_q has {K2}")
+    _device_tensor(w_q, "w_q", torch.uint8, a_q.device)
     for t, nm in ((a_s, "a_s"), (w_s, "w_s")):
-        if t.dtype != torch.float32 or not t.is_cuda:
-            raise TypeError(f"{nm} must be a float32 device tensor")
+        _device_tensor(t, nm, torch.float32, a_q.device)
     if mode == SCALE_ROW:
-        ld_as, ld_ws = _vec_ld(a_s.reshape(-1)), _vec_ld(w_s.reshape(-1))
+        ld_as, ld_ws = _vec_ld(a_s, M, "a_s"), _vec_ld(w_s, N, "w_s")
+    elif mode == SCALE_BLOCK:
+        ld_as = _scale_matrix(a_s, "a_s", M, K // 128, a_q.device)
+        ld_ws = _scale_matrix(w_s, "w_s", N // 128, K // 128, a_q.device)
     else:
-        ld_as, ld_ws = _ld(a_s), _ld(w_s)
+        if a_s.numel() != 1 or w_s.numel() != 1:
+            raise ValueError("per-tensor scales are one value each")
+        ld_as, ld_ws = 1, 1
     with torch.cuda.device(a_q.device):
         if out is None:
             out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
-        ld_out = out.stride(0) if out.shape[0] > 1 else out.shape[1]
+        _device_tensor(out, "out", torch.bfloat16, a_q.device, (M, N))
+        ld_out = _rows(out, torch.bfloat16, "out")[2]
         _check(lib().fp8_block_gemm(a_q.data_ptr(), ld_a, a_s.data_ptr(), ld_as, w_q.data_ptr(),
                                     ld_w, w_s.data_ptr(), ld_ws, out.data_ptr(), ld_out,
                                     M, N, K, mode, None, 0, _stream(a_q)))
@@ -224,18 +273,25 @@ def linear(x, w_q, w_s, scale_mode="block", out=None, workspace=None):
     N, K2, ld_w = _rows(w_q, torch.uint8, "w_q")
     if K2 != K:
         raise ValueError(f"K mismatch: x has {K}, w_q has {K2}")
-    if w_s.dtype != torch.float32 or not w_s.is_cuda:
-        raise TypeError("w_s must be a float32 device tensor")
+    _device_tensor(w_q, "w_q", torch.uint8, x.device)
+    _device_tensor(w_s, "w_s", torch.float32, x.device)
+    if mode == SCALE_ROW:
+        ld_ws = _vec_ld(w_s, N, "w_s")
+    elif mode == SCALE_BLOCK:
+        ld_ws = _scale_matrix(w_s, "w_s", N // 128, K // 128, x.device)
+    else:
+        if w_s.numel() != 1:
+            raise ValueError("a per-tensor weight scale is one value")
+        ld_ws = 1
     with torch.cuda.device(x.device):
         if out is None:
             out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-        ld_out = out.stride(0) if out.shape[0] > 1 else out.shape[1]
+        _device_tensor(out, "out", torch.bfloat16, x.device, (M, N))
+        ld_out = _rows(out, torch.bfloat16, "out")[2]
         nws = workspace_bytes(OP_LINEAR, M, N, K, mode)
         if nws and workspace is None:
             workspace = torch.empty(nws, dtype=torch.uint8, device=x.device)
-        ws_ptr = workspace.data_ptr() if workspace is not None else None
-        ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        ld_ws = _vec_ld(w_s.reshape(-1)) if mode == SCALE_ROW else _ld(w_s)
+        ws_ptr, ws_len = _workspace(workspace, x.device)
         _check(lib().fp8_linear(x.data_ptr(), ld_x, w_q.data_ptr(), ld_w, w_s.data_ptr(), ld_ws,
                                 out.data_ptr(), ld_out, M, N, K, mode, ws_ptr, ws_len, _stream(x)))
     return out
@@ -245,12 +301,13 @@ def quant_act_static(x, scale, q=None):
     """Static activation quantization of bf16 x [M, K] with a calibrated
     scale (a 1-element float32 device tensor) -> codes uint8 [M, K]."""
     M, K, ld_x = _rows(x, torch.bfloat16, "x")
-    if scale.dtype != torch.float32 or not scale.is_cuda or scale.numel() != 1:
-        raise TypeError("scale must be a 1-element float32 device tensor")
+    _scalar_scale(scale, "scale")
+    _device_tensor(scale, "scale", torch.float32, x.device)
     with torch.cuda.device(x.device):
         if q is None:
             q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-        ld_q = q.stride(0) if q.shape[0] > 1 else q.shape[1]
+        _device_tensor(q, "q", torch.uint8, x.device, (M, K))
+        ld_q = _rows(q, torch.uint8, "q")[2]
         _check(lib().fp8_quant_act_static(x.data_ptr(), M, K, ld_x, q.data_ptr(), ld_q,
                                           scale.data_ptr(), _stream(x)))
     return q
@@ -271,22 +328,22 @@ def grouped_gemm(a_q, a_s, w_q, w_s, expert_offsets, out=None):
     if w_q.stride(2) != 1 or w_q.stride(0) != N * w_q.stride(1):
         raise ValueError("w_q experts must be stacked rows: strides (N * ld_w, ld_w, 1)")
     ld_w = w_q.stride(1) if N > 1 else K
-    if (w_s.dtype != torch.float32 or w_s.dim() != 3 or not w_s.is_cuda or
-            tuple(w_s.shape[:2]) != (E, N // 128) or w_s.stride(2) != 1 or
-            w_s.stride(0) != (N // 128) * w_s.stride(1)):
+    _device_tensor(w_q, "w_q", torch.uint8, a_q.device)
+    _device_tensor(w_s, "w_s", torch.float32, a_q.device, (E, N // 128, K // 128))
+    if w_s.stride(2) != 1 or w_s.stride(0) != (N // 128) * w_s.stride(1):
         raise ValueError("w_s must be a float32 [E, N/128, K/128] device tensor, experts stacked")
+    ld_as = _scale_matrix(a_s, "a_s", M, K // 128, a_q.device)
     ld_ws = w_s.stride(1) if N // 128 > 1 else w_s.shape[2]
-    if (expert_offsets.dtype != torch.int64 or expert_offsets.dim() != 1 or
-            expert_offsets.shape[0] != E + 1 or not expert_offsets.is_cuda):
-        raise ValueError("expert_offsets must be a 1-D int64 device tensor of E + 1 entries")
+    _device_tensor(expert_offsets, "expert_offsets", torch.int64, a_q.device, (E + 1,))
     offs = expert_offsets.contiguous()
     with torch.cuda.device(a_q.device):
         if out is None:
             out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
-        _check(lib().fp8_grouped_gemm(a_q.data_ptr(), ld_a, a_s.data_ptr(), _ld(a_s),
+        _device_tensor(out, "out", torch.bfloat16, a_q.device, (M, N))
+        ld_out = _rows(out, torch.bfloat16, "out")[2]
+        _check(lib().fp8_grouped_gemm(a_q.data_ptr(), ld_a, a_s.data_ptr(), ld_as,
                                       w_q.data_ptr(), ld_w, w_s.data_ptr(), ld_ws,
-                                      offs.data_ptr(), E, out.data_ptr(), _rows(out, torch.bfloat16,
-                                                                                "out")[2],
+                                      offs.data_ptr(), E, out.data_ptr(), ld_out,
                                       M, N, K, _stream(a_q)))
     return out
 

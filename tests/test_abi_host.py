@@ -279,3 +279,30 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros((16, 512), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         _lib.quant_act(x)
+
+
+def test_binding_scale_vector_strides():
+    torch = pytest.importorskip("torch")
+    v = torch.zeros(12)
+    assert _lib._vec_ld(v[:1], 5, "s") == 0                  # one value for all rows
+    assert _lib._vec_ld(v[:5], 5, "s") == 1
+    assert _lib._vec_ld(v[::2][:5], 5, "s") == 2
+    m = torch.zeros((5, 3))
+    assert _lib._vec_ld(m[:, 0], 5, "s") == 3                # a column of a matrix
+    assert _lib._vec_ld(m[:, :1], 5, "s") == 3               # the same as [5, 1]
+    assert _lib._vec_ld(torch.zeros((1, 5)), 5, "s") == 1
+    with pytest.raises(ValueError):
+        _lib._vec_ld(v[:4], 5, "s")                           # wrong count
+    with pytest.raises(ValueError):
+        _lib._vec_ld(torch.zeros((5, 2)), 10, "s")            # not a vector
+
+
+def test_binding_rejects_host_scales_and_outputs():
+    torch = pytest.importorskip("torch")
+    dev = torch.device("cuda", 0)
+    with pytest.raises(ValueError):
+        _lib._device_tensor(torch.zeros(4), "s", torch.float32, dev)
+    with pytest.raises(TypeError):
+        _lib._device_tensor(torch.zeros(4, dtype=torch.float64), "s", torch.float32, dev)
+    with pytest.raises(TypeError):
+        _lib._device_tensor(None, "s", torch.float32, dev)

@@ -446,6 +446,34 @@ def test_linear_workspace_path(M, mode):
     check_out(got, oracle_gemm(a, w, mode), f"linear {mode} M={M}")
 
 
+def test_binding_checks_caller_tensors():
+    # outputs and scales handed in by the caller are checked before any launch
+    x = torch.zeros((16, 512), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        fp8.quant_act(x, q=torch.empty((8, 512), dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        fp8.quant_act(x, scales=torch.empty((16, 3), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        fp8.quant_act(x, scales=torch.empty((16, 4), dtype=torch.float32))     # host memory
+    aq, as_ = fp8.quant_act(x)
+    wq = torch.zeros((256, 512), dtype=torch.uint8, device="cuda")
+    ws = torch.ones((2, 4), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        fp8.block_gemm(aq, as_, wq, ws, out=torch.empty((16, 128), dtype=torch.bfloat16,
+                                                        device="cuda"))
+    with pytest.raises(ValueError):
+        fp8.block_gemm(aq, as_[:8], wq, ws)
+    with pytest.raises(ValueError):
+        fp8.block_gemm(aq, as_, wq, ws[:1])
+    with pytest.raises(ValueError):
+        fp8.linear(x, wq, ws.cpu())
+    with pytest.raises(ValueError):
+        fp8.grouped_gemm(aq, as_, wq[None], ws[None],
+                         torch.tensor([0, 16], device="cuda"), out=torch.empty(
+                             (16, 256), dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+
+
 def test_linear_errors():
     x = torch.zeros((100, 512), dtype=torch.bfloat16, device="cuda")
     wq = torch.zeros((256, 512), dtype=torch.uint8, device="cuda")
