@@ -241,6 +241,34 @@ def time_gemm_launches(wl, n_launches):
     return float(ms), n_launches
 
 
+def time_quantizer(wl):
+    """The dynamic activation quantizer on its own: average duration of
+    back-to-back launches on the workload's largest activation (the kernel
+    the two-launch path runs), against its algorithmic bytes.  The launches
+    rotate over enough copies of the input and outputs (more than 600 MB in
+    all, up to 16) that they come from HBM, not from the 256 MB Infinity
+    Cache."""
+    import torch
+    j = max(range(len(wl.Ms)), key=lambda i: wl.Ms[i])
+    M, K = wl.Ms[j], wl.K
+    # block: bf16 in, codes and 1x128 scales out; tensor: the bf16 read twice
+    # (global amax, then encode), codes and one scale out
+    b = quant_bytes(M, K) if wl.mode == "block" else 5 * M * K + 4
+    n_c = int(min(16, max(1, -(-600_000_000 // quant_bytes(M, K)))))
+    xs = [wl.x[j]] + [wl.x[j].clone() for _ in range(n_c - 1)]
+    qs = [wl.aq[j]] + [torch.empty_like(wl.aq[j]) for _ in range(n_c - 1)]
+    ss = [wl.as_[j]] + [torch.empty_like(wl.as_[j]) for _ in range(n_c - 1)]
+    n_l = 96 if M <= 64 else 24
+    ms = time_launches(lambda i: wl.fp8.quant_act(xs[i % n_c], wl.mode, workspace=wl.ws_buf,
+                                                  q=qs[i % n_c], scales=ss[i % n_c]), n_l)
+    del xs, qs, ss
+    name = "quant_act_block_kernel" if wl.mode == "block" else "absmax_partial_kernel + quant_tensor_kernel"
+    return {"kernel": name, "M": M, "K": K, "avg_launch_us": ms * 1e3, "launches_timed": n_l,
+            "input_copies": n_c,
+            "algorithmic_bytes_per_launch": b, "GB/s": b / (ms * 1e-3) / 1e9,
+            "frac_of_8000": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def calibration_copy():
     """One plain device-to-device copy of known size; under rocprofv3 --pmc its
     FETCH_SIZE / WRITE_SIZE give the scale factor for the kernels' counters."""
@@ -747,6 +775,7 @@ def main():
         gemm_bytes_per_launch if decode else flops_per_launch)
     roof["kernel_source_hash"] = kernel_source_hash()
 
+    quantizer = time_quantizer(wl)
     cpu = None
     if args.cpu_baseline_seconds > 0:
         cpu = cpu_baseline(wl, args.cpu_baseline_seconds)
@@ -782,6 +811,7 @@ def main():
         "step_flop": flops,
         "tflops_per_step": flops / (sec / K) / 1e12,
         "secondary": secondary,
+        "quantizer": quantizer,
     }
     print(json.dumps(line), flush=True)
 
