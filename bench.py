@@ -12,9 +12,10 @@ sizes M = 1, 4 and 16 back to back.  Each GEMM of a decode step reads a
 different copy of the weight codes (8 copies, 360 MB, more than the 256 MB
 Infinity Cache) so the weight really comes from HBM.
 
-Timing: W warm-up steps, then exactly K steps replayed from HIP graphs (one
-graph per step pattern), bracketed by torch.cuda.synchronize() on both sides
-(one process, one GPU: no barrier needed).  The dominant kernel's average
+Timing: W warm-up steps, then exactly K steps replayed from HIP graphs (a
+graph of 8 consecutive steps replayed K // 8 times, single-step graphs for
+the rest), bracketed by torch.cuda.synchronize() on both sides (one process,
+one GPU: no barrier needed).  The dominant kernel's average
 launch duration is measured with one HIP event pair on the launch stream
 around a run of back-to-back launches of that kernel, queued behind a
 bounded GPU-side delay so that no host gap falls inside the timed span.
@@ -407,6 +408,42 @@ class KVWorkload:
         return kv_write_bytes(self.T, HD) + 2 * kv_read_bytes(self.T, HD)
 
 
+def timed_steps(step, n_patterns, K):
+    """Wall time of exactly K steps replayed from HIP graphs: one graph of
+    S >= 8 consecutive steps (S a multiple of the number of step patterns)
+    replayed K // S times, then single-step graphs for the K % S left, so the
+    host's per-replay cost is paid once per S steps.  Step s runs pattern
+    s % n_patterns.  Returns seconds between two device synchronizations."""
+    import torch
+    S = n_patterns * -(-8 // n_patterns)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    singles = []
+    with torch.cuda.stream(stream):
+        for p in range(n_patterns):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(p)
+            singles.append(g)
+        block = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(block, stream=stream):
+            for s in range(S):
+                step(s % n_patterns)
+    torch.cuda.current_stream().wait_stream(stream)
+    block.replay()                     # warm-up replays
+    for g in singles:
+        g.replay()
+    torch.cuda.synchronize()
+    full, rem = divmod(K, S)
+    t0 = time.perf_counter()
+    for _ in range(full):
+        block.replay()
+    for r in range(rem):
+        singles[(full * S + r) % n_patterns].replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
 def time_launches(fn, n_launches):
     """Average duration of one kernel: an event pair on the launch stream
     around n back-to-back launches queued behind a bounded GPU-side delay."""
@@ -463,25 +500,8 @@ def main_kv(args):
     for s in range(args.warmup):
         wl.step(s)
     torch.cuda.synchronize()
-    graphs = []
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
-        for p in range(2):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                wl.step(p)
-            graphs.append(g)
-    torch.cuda.current_stream().wait_stream(stream)
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
     K = args.steps
-    t0 = time.perf_counter()
-    for s in range(K):
-        graphs[s % 2].replay()
-    torch.cuda.synchronize()
-    sec = time.perf_counter() - t0
+    sec = timed_steps(wl.step, 2, K)
 
     HD = wl.H * wl.D
     n_l = 40
@@ -632,21 +652,8 @@ def main_moe(args):
     for s in range(args.warmup):
         wl.step(s)
     torch.cuda.synchronize()
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            wl.step(0)
-    torch.cuda.current_stream().wait_stream(stream)
-    g.replay()
-    torch.cuda.synchronize()
     K = args.steps
-    t0 = time.perf_counter()
-    for s in range(K):
-        g.replay()
-    torch.cuda.synchronize()
-    sec = time.perf_counter() - t0
+    sec = timed_steps(wl.step, 1, K)
     n_l = 20
     g_ms = time_launches(lambda i: wl.gemm(), n_l)
     decode = wl.name == "moe_decode"
@@ -719,32 +726,12 @@ def main():
     wl = Workload(args.workload)
     decode = len(wl.Ms) > 1
 
-    # warm-up (eager), then capture one HIP graph per step pattern
+    # warm-up (eager), then the timed steps from HIP graphs
     for s in range(args.warmup):
         wl.step(s)
     torch.cuda.synchronize()
-    graphs = []
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
-        for p in range(wl.n_patterns()):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                wl.step(p)
-            graphs.append(g)
-    torch.cuda.current_stream().wait_stream(stream)
-    for p in range(len(graphs)):       # graph warm-up replays
-        graphs[p].replay()
-    torch.cuda.synchronize()
-
     K = args.steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(K):
-        graphs[s % len(graphs)].replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    sec = t1 - t0
+    sec = timed_steps(wl.step, wl.n_patterns(), K)
     ms_per_step = sec / K * 1e3
 
     total_b, q_b, g_b = wl.bytes_per_step()
