@@ -38,6 +38,10 @@ constexpr int kDecodeMaxKB = 128;             // K <= 16384
 #ifndef FP8_DECODE_KBW
 #define FP8_DECODE_KBW 1
 #endif
+// largest M the decode tile serves (16-row chunks above 16)
+#ifndef FP8_DECODE_MAX_M
+#define FP8_DECODE_MAX_M 64
+#endif
 // prefill: the hand-scheduled K loop (prefill_asm.inc) instead of the C++ one
 #ifndef FP8_PREFILL_ASM
 #define FP8_PREFILL_ASM 1
@@ -235,14 +239,22 @@ __device__ __forceinline__ void decode_tile(
   }
 }
 
+// Rows beyond 16 go through the tile 16 at a time (each chunk streams the
+// workgroup's weight strip again), which keeps every CU busy for the
+// mid-size batches the 256-row prefill tiles would leave mostly empty.
 template <int KSPLIT, int KBW, bool KCONST>
 __global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
     const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
     uint16_t* __restrict__ out, int64_t ld_out, int M, int KB) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  decode_tile<KSPLIT, KBW, KCONST>(lds, a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, KB,
-                                   (int64_t)blockIdx.x * 16);
+  for (int r = 0; r < M; r += 16) {
+    if (r > 0) __syncthreads();                       // LDS reuse across row chunks
+    decode_tile<KSPLIT, KBW, KCONST>(lds, a + (int64_t)r * ld_a, ld_a,
+                                     sa + (int64_t)r * ld_sa, ld_sa,
+                                     w, ld_w, sw, ld_sw, out + (int64_t)r * ld_out, ld_out,
+                                     M - r < 16 ? M - r : 16, KB, (int64_t)blockIdx.x * 16);
+  }
 }
 
 // Clamped row range of expert e in a grouped call: offsets are read as
@@ -1156,7 +1168,7 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
                        uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
                        bool kconst, hipStream_t st) {
   const int KB = (int)(K / 128);
-  if (M <= 16 && KB <= kDecodeMaxKB) {
+  if (M <= FP8_DECODE_MAX_M && KB <= kDecodeMaxKB) {
     constexpr int KSPLIT = FP8_DECODE_KSPLIT, KBW = FP8_DECODE_KBW;
     dim3 grid((uint32_t)(N / 16));
     const size_t lds = decode_lds_bytes<KSPLIT, KBW>(KB, kconst);

@@ -292,8 +292,11 @@ def test_gemm_tiny_full():
     check_out(out, oracle_gemm(d["A"], d["W"]), "tiny")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (3, 256, 384), (17, 384, 640), (100, 256, 1024),
-                                   (129, 512, 512), (300, 384, 640), (256, 256, 2304)])
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (3, 256, 384), (17, 384, 640), (40, 256, 512),
+                                   (64, 512, 1024), (100, 256, 1024), (129, 512, 512),
+                                   (300, 384, 640), (256, 256, 2304),
+                                   # K / 128 > 128: the 128 x 128 tile kernel
+                                   (10, 256, 16512), (40, 256, 16512)])
 def test_gemm_ragged_full(M, N, K):
     rng = np.random.default_rng([M, N, K])
     a = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
