@@ -239,15 +239,25 @@ __device__ __forceinline__ void decode_tile(
   }
 }
 
-// Rows beyond 16 go through the tile 16 at a time (each chunk streams the
-// workgroup's weight strip again), which keeps every CU busy for the
-// mid-size batches the 256-row prefill tiles would leave mostly empty.
-template <int KSPLIT, int KBW, bool KCONST>
-__global__ __launch_bounds__(64 * KSPLIT) void gemm_decode_kernel(
+// CHUNKED (16 < M): rows go through the tile 16 at a time, each chunk
+// streaming the workgroup's weight strip again, which keeps every CU busy
+// for the mid-size batches the 256-row prefill tiles would leave mostly
+// empty.  M <= 16 uses the loop-free form: the loop raised the register
+// count to 86 (two workgroups per CU instead of three; 9.9 -> 12.3 us at
+// M = 1).  Six waves per SIMD are requested for both forms, so that three
+// 8-wave workgroups fit on a CU.
+template <int KSPLIT, int KBW, bool KCONST, bool CHUNKED>
+__global__ __launch_bounds__(64 * KSPLIT) __attribute__((amdgpu_waves_per_eu(6, 8)))
+void gemm_decode_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
     const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
     uint16_t* __restrict__ out, int64_t ld_out, int M, int KB) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  if (!CHUNKED) {
+    decode_tile<KSPLIT, KBW, KCONST>(lds, a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M,
+                                     KB, (int64_t)blockIdx.x * 16);
+    return;
+  }
   for (int r = 0; r < M; r += 16) {
     if (r > 0) __syncthreads();                       // LDS reuse across row chunks
     decode_tile<KSPLIT, KBW, KCONST>(lds, a + (int64_t)r * ld_a, ld_a,
@@ -1172,12 +1182,22 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
     constexpr int KSPLIT = FP8_DECODE_KSPLIT, KBW = FP8_DECODE_KBW;
     dim3 grid((uint32_t)(N / 16));
     const size_t lds = decode_lds_bytes<KSPLIT, KBW>(KB, kconst);
-    if (kconst)
-      hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, KBW, true>), grid, dim3(64 * KSPLIT), lds, st,
-                         a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
-    else
-      hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, KBW, false>), grid, dim3(64 * KSPLIT), lds, st,
-                         a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
+    const dim3 block(64 * KSPLIT);
+    if (M <= 16) {
+      if (kconst)
+        hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, KBW, true, false>), grid, block, lds, st,
+                           a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
+      else
+        hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, KBW, false, false>), grid, block, lds, st,
+                           a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
+    } else {
+      if (kconst)
+        hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, KBW, true, true>), grid, block, lds, st,
+                           a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
+      else
+        hipLaunchKernelGGL((gemm_decode_kernel<KSPLIT, KBW, false, true>), grid, block, lds, st,
+                           a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, (int)M, KB);
+    }
     return hipGetLastError();
   }
   if (FP8_PREFILL_ASM && M > 64 && KB % kPfKbGroup == 0 && KB <= kPrefillMaxKB &&
