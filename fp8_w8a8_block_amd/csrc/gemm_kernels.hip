@@ -280,9 +280,11 @@ __device__ __forceinline__ void expert_rows(const int64_t* __restrict__ offsets,
 // Grouped (MoE) GEMM for few rows per expert: workgroup (x, e) computes
 // columns 16 x .. 16 x + 15 of expert e's rows, 16 rows at a time with the
 // decode tile, weight W + e * w_es, scales sw + e * sw_es.  An expert with no
-// rows costs one offsets read.
+// rows costs one offsets read.  Six waves per SIMD keep three workgroups on a
+// CU, as for the chunked decode kernel.
 template <int KSPLIT, int KBW>
-__global__ __launch_bounds__(64 * KSPLIT) void gemm_grouped_decode_kernel(
+__global__ __launch_bounds__(64 * KSPLIT) __attribute__((amdgpu_waves_per_eu(6, 8)))
+void gemm_grouped_decode_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
     const uint8_t* __restrict__ w, int64_t ld_w, int64_t w_es, const float* __restrict__ sw,
     int64_t ld_sw, int64_t sw_es, uint16_t* __restrict__ out, int64_t ld_out,
