@@ -13,6 +13,13 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;        // any single extent
 constexpr int64_t kMaxElems = (int64_t)1 << 40;      // rows * cols of one tensor
+constexpr int64_t kMaxSpan = (int64_t)1 << 56;       // rows * ld of one tensor (elements)
+
+// rows rows at leading dimension ld span at most kMaxSpan elements, so every
+// byte range below is computed without overflow
+bool span_ok(int64_t rows, int64_t ld) {
+  return ld >= 0 && ld <= kMaxSpan && (rows <= 1 || ld <= kMaxSpan / rows);
+}
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -48,10 +55,13 @@ fp8_status validate_quant(const uint16_t* x, int64_t R, int64_t K, int64_t ld_x,
   if (ld_x < K || ld_q < K) return FP8_ERR_STRIDE;
   if (scale_mode == FP8_SCALE_BLOCK && ld_s < groups) return FP8_ERR_STRIDE;
   if (scale_mode == FP8_SCALE_ROW && ld_s < 1) return FP8_ERR_STRIDE;
-  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4)) return FP8_ERR_ALIGN;
-  if (ld_x % 8 != 0 || ld_q % 16 != 0) return FP8_ERR_ALIGN;
   const int64_t srows = scale_mode == FP8_SCALE_BLOCK ? (rows_blocked ? R / 128 : R)
                         : scale_mode == FP8_SCALE_ROW ? R : 1;
+  if (!span_ok(R, ld_x) || !span_ok(R, ld_q) ||
+      (scale_mode != FP8_SCALE_TENSOR && !span_ok(srows, ld_s)))
+    return FP8_ERR_STRIDE;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4)) return FP8_ERR_ALIGN;
+  if (ld_x % 8 != 0 || ld_q % 16 != 0) return FP8_ERR_ALIGN;
   const int64_t scols = scale_mode == FP8_SCALE_BLOCK ? groups : 1;
   const int64_t sld = scale_mode == FP8_SCALE_TENSOR ? 1 : ld_s;
   Range rx = range_of(x, R, K, ld_x, 2), rq = range_of(q, R, K, ld_q, 1);
@@ -85,6 +95,11 @@ fp8_status validate_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, int
   if (scale_mode == FP8_SCALE_BLOCK && (ld_as < KB || ld_ws < KB)) return FP8_ERR_STRIDE;
   if (scale_mode == FP8_SCALE_ROW && (ld_as < 0 || ld_ws < 0 || ld_as >= kMaxDim ||
                                       ld_ws >= kMaxDim))
+    return FP8_ERR_STRIDE;
+  if (!span_ok(M, ld_a) || !span_ok(N, ld_w) || !span_ok(M, ld_out)) return FP8_ERR_STRIDE;
+  if (scale_mode == FP8_SCALE_BLOCK && (!span_ok(M, ld_as) || !span_ok(N / 128, ld_ws)))
+    return FP8_ERR_STRIDE;
+  if (scale_mode == FP8_SCALE_ROW && (!span_ok(M, ld_as) || !span_ok(N, ld_ws)))
     return FP8_ERR_STRIDE;
   if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(out, 16)) return FP8_ERR_ALIGN;
   if (!aligned(a_s, 4) || !aligned(w_s, 4)) return FP8_ERR_ALIGN;
@@ -153,7 +168,7 @@ const char* fp8_status_str(fp8_status s) {
     case FP8_OK: return "ok";
     case FP8_ERR_NULL: return "a required pointer is NULL";
     case FP8_ERR_SHAPE: return "bad shape: K and N must be positive multiples of 128, M >= 0";
-    case FP8_ERR_STRIDE: return "leading dimension smaller than the row length";
+    case FP8_ERR_STRIDE: return "leading dimension smaller than the row length, or too large";
     case FP8_ERR_ALIGN: return "misaligned pointer or leading dimension";
     case FP8_ERR_BLOCK: return "the weight block size must have two dimensions, 128 x 128";
     case FP8_ERR_SCHEME: return "unsupported scale mode: block mode supports only dynamic activation scales";
@@ -266,6 +281,9 @@ fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
   if (ld_x < K || ld_w < K || ld_out < N) return FP8_ERR_STRIDE;
   if (scale_mode == FP8_SCALE_BLOCK && ld_ws < KB) return FP8_ERR_STRIDE;
   if (scale_mode == FP8_SCALE_ROW && (ld_ws < 0 || ld_ws >= kMaxDim)) return FP8_ERR_STRIDE;
+  if (!span_ok(M, ld_x) || !span_ok(N, ld_w) || !span_ok(M, ld_out)) return FP8_ERR_STRIDE;
+  if (scale_mode == FP8_SCALE_BLOCK && !span_ok(N / 128, ld_ws)) return FP8_ERR_STRIDE;
+  if (scale_mode == FP8_SCALE_ROW && !span_ok(N, ld_ws)) return FP8_ERR_STRIDE;
   if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(out, 16) || !aligned(w_s, 4))
     return FP8_ERR_ALIGN;
   if (ld_x % 8 != 0 || ld_w % 16 != 0 || ld_out % 8 != 0) return FP8_ERR_ALIGN;
@@ -314,6 +332,7 @@ fp8_status fp8_validate_quant_act_static(const uint16_t* x, int64_t M, int64_t K
   if (M == 0) return FP8_OK;
   if (!x || !q || !scale) return FP8_ERR_NULL;
   if (ld_x < K || ld_q < K) return FP8_ERR_STRIDE;
+  if (!span_ok(M, ld_x) || !span_ok(M, ld_q)) return FP8_ERR_STRIDE;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return FP8_ERR_ALIGN;
   if (ld_x % 8 != 0 || ld_q % 16 != 0) return FP8_ERR_ALIGN;
   Range rx = range_of(x, M, K, ld_x, 2), rq = range_of(q, M, K, ld_q, 1);
@@ -346,6 +365,9 @@ fp8_status fp8_validate_grouped_gemm(const uint8_t* a_q, int64_t ld_a, const flo
   if (!a_q || !a_s || !w_q || !w_s || !out || !expert_offsets) return FP8_ERR_NULL;
   const int64_t KB = K / 128;
   if (ld_a < K || ld_w < K || ld_out < N || ld_as < KB || ld_ws < KB) return FP8_ERR_STRIDE;
+  if (!span_ok(M, ld_a) || !span_ok(M, ld_as) || !span_ok(M, ld_out) || !span_ok(E * N, ld_w) ||
+      !span_ok(E * (N / 128), ld_ws))
+    return FP8_ERR_STRIDE;
   if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(out, 16)) return FP8_ERR_ALIGN;
   if (!aligned(a_s, 4) || !aligned(w_s, 4) || !aligned(expert_offsets, 8)) return FP8_ERR_ALIGN;
   if (ld_a % 16 != 0 || ld_w % 16 != 0 || ld_out % 8 != 0) return FP8_ERR_ALIGN;
@@ -403,6 +425,7 @@ fp8_status fp8_validate_kv_cache_write(const uint16_t* key, int64_t ld_key,
   if (!key || !value || !slot_mapping || !k_scale || !v_scale) return FP8_ERR_NULL;
   if (cap > 0 && (!key_cache || !value_cache)) return FP8_ERR_NULL;
   if (ld_key < hd || ld_value < hd) return FP8_ERR_STRIDE;
+  if (!span_ok(T, ld_key) || !span_ok(T, ld_value)) return FP8_ERR_STRIDE;
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(slot_mapping, 8) ||
       !aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(k_scale, 4) ||
       !aligned(v_scale, 4))
@@ -442,7 +465,7 @@ fp8_status fp8_validate_kv_cache_read(const uint8_t* cache, int64_t num_blocks,
   const int64_t hd = H * D, cap = num_blocks * block_size;
   if (!slots || !scale || !out) return FP8_ERR_NULL;
   if (cap > 0 && !cache) return FP8_ERR_NULL;
-  if (ld_out < hd) return FP8_ERR_STRIDE;
+  if (ld_out < hd || !span_ok(T, ld_out)) return FP8_ERR_STRIDE;
   if (!aligned(cache, 16) || !aligned(slots, 8) || !aligned(scale, 4) || !aligned(out, 16))
     return FP8_ERR_ALIGN;
   if (ld_out % 8 != 0) return FP8_ERR_ALIGN;

@@ -51,7 +51,8 @@ typedef enum {
   FP8_ERR_NULL = 1,       /* a required pointer is NULL */
   FP8_ERR_SHAPE = 2,      /* K or N not a positive multiple of 128, M < 0, a KV-cache
                              shape out of range, or too large */
-  FP8_ERR_STRIDE = 3,     /* a leading dimension is smaller than the row length */
+  FP8_ERR_STRIDE = 3,     /* a leading dimension is smaller than the row length, or
+                             rows x leading dimension exceeds 2^56 elements */
   FP8_ERR_ALIGN = 4,      /* pointer or leading-dimension alignment */
   FP8_ERR_BLOCK = 5,      /* weight block size other than 128 x 128 */
   FP8_ERR_SCHEME = 6,     /* unsupported scale mode / scheme combination */

@@ -306,3 +306,27 @@ def test_binding_rejects_host_scales_and_outputs():
         _lib._device_tensor(torch.zeros(4, dtype=torch.float64), "s", torch.float32, dev)
     with pytest.raises(TypeError):
         _lib._device_tensor(None, "s", torch.float32, dev)
+
+
+def test_leading_dimensions_are_bounded():
+    # rows x ld beyond 2^56 elements is refused before any byte range is
+    # formed (such a tensor cannot exist, and its range would overflow)
+    huge = 1 << 62
+    assert vq(ld_x=huge) == STRIDE
+    assert vq(ld_q=huge) == STRIDE
+    assert vq(ld_s=huge) == STRIDE
+    assert vq(mode=2, ld_s=huge) == STRIDE
+    assert vq(M=1 << 20, ld_x=1 << 37) == STRIDE          # 2^57 elements
+    assert vq(M=2, ld_x=1 << 30) == OK                    # large but within bounds
+    assert vg(ld_a=huge) == STRIDE
+    assert vg(ld_w=huge) == STRIDE
+    assert vg(ld_out=huge) == STRIDE
+    assert vg(ld_as=huge) == STRIDE
+    assert vg(ld_ws=huge) == STRIDE
+    assert vg(ld_as=huge, mode=1) == OK                    # per-tensor scales have no ld
+    assert vg(mode=2, ld_as=(1 << 31) - 1, ld_ws=1, M=(1 << 30)) == STRIDE
+    assert vgg(ld_a=huge) == STRIDE
+    assert vgg(ld_w=huge) == STRIDE
+    assert vgg(ld_ws=huge) == STRIDE
+    assert vkw(ld_k=huge) == STRIDE
+    assert vkr(ld_out=huge) == STRIDE
