@@ -295,6 +295,9 @@ def test_gemm_tiny_full():
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (3, 256, 384), (17, 384, 640), (40, 256, 512),
                                    (64, 512, 1024), (100, 256, 1024), (129, 512, 512),
                                    (300, 384, 640), (256, 256, 2304),
+                                   # one K block past 64 rows; one 128-wide N tile on both
+                                   # large-M kernels
+                                   (65, 128, 128), (300, 128, 512), (70, 128, 2176),
                                    # K / 128 > 128: the 128 x 128 tile kernel
                                    (10, 256, 16512), (40, 256, 16512)])
 def test_gemm_ragged_full(M, N, K):
