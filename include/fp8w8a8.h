@@ -30,7 +30,10 @@
  *   - Calls are thread-safe; the only global state is a per-device cache of
  *     the architecture check.  Calls on one stream are ordered; calls on
  *     different streams that write the same buffers race (caller's duty).
- *   - Inputs are assumed finite (no NaN/Inf in bf16 inputs).
+ *   - The dynamic quantizers (scales derived from the data) assume finite
+ *     bf16 inputs: a NaN or infinity in a group makes its scale non-finite.
+ *     The static-scale calls (fp8_quant_act_static, fp8_kv_cache_write)
+ *     define NaN and infinity per element.
  *
  * Page references: "[vLLM] FP8" = blog.secrett2633.cloud/opensource/vllm/fp8;
  * "FP8 Quantization" = zzong2006.github.io fp8-quantization;
