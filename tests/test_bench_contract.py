@@ -1,6 +1,7 @@
 """bench.py's output contract: one JSON line with the fields the driver reads,
 a roofline object for the dominant kernel and the oracle's CPU baseline; more
-than one GPU is refused with a message."""
+than one GPU is refused with a message; the committed HBM-traffic record is
+reported only while the kernel source it was taken on is unchanged."""
 
 import json
 import os
@@ -16,6 +17,38 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def run_bench(*args, timeout=600):
     return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT,
                           capture_output=True, text=True, timeout=timeout)
+
+
+def _kernel_tree(tmp_path):
+    """A copy of the files the traffic record is keyed on, and the record."""
+    import shutil
+    import bench
+    for rel in set(bench.KERNEL_SOURCES) | set(bench.KV_SOURCES) | {bench.TRAFFIC_FILE}:
+        dst = tmp_path / rel
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(ROOT, rel), dst)
+    return bench
+
+
+def test_traffic_stays_attached_to_its_kernel_source(tmp_path, monkeypatch):
+    # the committed HBM-traffic record is used only while the kernel source it
+    # was taken on is unchanged; comments and blank lines do not count
+    bench = _kernel_tree(tmp_path)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    with open(tmp_path / bench.TRAFFIC_FILE) as f:
+        workloads = sorted(json.load(f))
+    assert "decode" in workloads and "kv_cache" in workloads
+    attached = {w: bench.measured_traffic(w) is not None for w in workloads}
+    src = tmp_path / bench.KERNEL_SOURCES[0]
+    text = src.read_text()
+    src.write_text(text + "\n// a note\n\n/* another\n   note */\n")
+    assert {w: bench.measured_traffic(w) is not None for w in workloads} == attached
+    src.write_text(text + "\nstatic int fp8_changed_token = 0;\n")
+    for w in workloads:
+        if w == "kv_cache":               # keyed on the KV sources only
+            assert (bench.measured_traffic(w) is not None) == attached[w]
+        else:
+            assert bench.measured_traffic(w) is None, w
 
 
 def test_more_than_one_gpu_is_refused():
