@@ -98,7 +98,8 @@ __device__ __forceinline__ v8i zero8() {
 // reduced in LDS.
 //
 // Dynamic LDS: KSPLIT * KBW * 4 KiB operand buffers, then the reduction
-// buffer (KSPLIT * 1 KiB), then the activation scales (16 * KB floats).
+// buffer (KSPLIT * 1 KiB), then the activation scales (16 * KB floats; in
+// the loop-free form already multiplied by the tile's weight scales).
 constexpr int kFrag = 2048;                   // 16 rows x 128 bytes
 
 template <int KSPLIT, int KBW>
@@ -109,7 +110,11 @@ constexpr size_t decode_lds_bytes(int KB, bool kconst) {
 
 // One 16-column output tile of at most 16 rows (1 <= M <= 16), columns
 // n0 .. n0 + 15; the whole workgroup takes part (it holds barriers).
-template <int KSPLIT, int KBW, bool KCONST>
+// WSTAGE: the weight scales are folded into the staged activation scales up
+// front, so the K loop reads no scale from memory (the same fp32 product,
+// bit for bit); the chunked and grouped forms, which sit at their register
+// limit, read the weight scale in the loop.
+template <int KSPLIT, int KBW, bool KCONST, bool WSTAGE = false>
 __device__ __forceinline__ void decode_tile(
     uint8_t* lds, const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa,
     int64_t ld_sa, const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw,
@@ -172,12 +177,16 @@ __device__ __forceinline__ void decode_tile(
 
   if (kb_lo < kb_hi) issue(kb_lo);
   if (!KCONST) {
-    // s_as[kb * 16 + m] = sa[m, kb] (rows >= M read 0); queued behind the
-    // first batch's loads
+    // s_as[kb * 16 + m] = sa[m, kb] (rows >= M read 0), times sw[n0 / 128, kb]
+    // when WSTAGE; queued behind the first batch's loads
+    const float* __restrict__ swr = sw + (int64_t)(n0 >> 7) * ld_sw;
     for (int i = threadIdx.x; i < KB * 16; i += 64 * KSPLIT) {
       const int m = i & 15;
       const int kb = i >> 4;
-      s_as[i] = m < M ? sa[(int64_t)m * ld_sa + kb] : 0.f;
+      if (WSTAGE)
+        s_as[i] = m < M ? sa[(int64_t)m * ld_sa + kb] * swr[kb] : 0.f;
+      else
+        s_as[i] = m < M ? sa[(int64_t)m * ld_sa + kb] : 0.f;
     }
   }
   __syncthreads();
@@ -198,11 +207,11 @@ __device__ __forceinline__ void decode_tile(
     for (int u = 0; u < KBW; ++u) {
       const int kb = kb0 + u;
       const int kbc = min(kb, kb_hi - 1);
-      const float s_w = KCONST ? 0.f : sw[(int64_t)(n0 >> 7) * ld_sw + kbc];
+      const float s_w = KCONST || WSTAGE ? 0.f : sw[(int64_t)(n0 >> 7) * ld_sw + kbc];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float s_a = KCONST ? 0.f : s_as[kbc * 16 + 4 * kg + i];
-        sc[u][i] = kb < kb_hi ? s_a * s_w : 0.f;
+        sc[u][i] = kb < kb_hi ? (WSTAGE ? s_a : s_a * s_w) : 0.f;
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -254,8 +263,8 @@ void gemm_decode_kernel(
     uint16_t* __restrict__ out, int64_t ld_out, int M, int KB) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   if (!CHUNKED) {
-    decode_tile<KSPLIT, KBW, KCONST>(lds, a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M,
-                                     KB, (int64_t)blockIdx.x * 16);
+    decode_tile<KSPLIT, KBW, KCONST, true>(lds, a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out,
+                                           ld_out, M, KB, (int64_t)blockIdx.x * 16);
     return;
   }
   for (int r = 0; r < M; r += 16) {
