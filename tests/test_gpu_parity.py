@@ -278,6 +278,35 @@ def check_out(out_bits, ref, what):
     return r
 
 
+@pytest.mark.parametrize("which", ["wide_a", "wide_out"])
+def test_gemm_strides_beyond_32bit_offsets(which):
+    # leading dimensions past the hand-scheduled kernel's 32-bit buffer
+    # offsets: an activation stride of 2^23 + 16 codes sends M > 64 to the
+    # 128 x 128 tile kernel, an output stride of 2^22 + 64 to the C++ prefill
+    # kernel; both against the oracle
+    M, N, K = 100, 256, 512
+    rng = np.random.default_rng(71)
+    a_bits = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    w_bits = synth.f32_to_bf16_bits(rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02))
+    aq, as_ = quant.quant_act_ref(a_bits)
+    wq, ws = quant.quant_weight_block_ref(w_bits)
+    ld_a = (1 << 23) + 16 if which == "wide_a" else K
+    ld_o = (1 << 22) + 64 if which == "wide_out" else N
+    log("gemm wide strides", which, dict(ld_a=ld_a, ld_out=ld_o))
+    a_big = torch.zeros((M, ld_a), dtype=torch.uint8, device="cuda")
+    a_big[:, :K] = torch.from_numpy(aq).cuda()
+    o_big = torch.full((M, ld_o), 0x7E00, dtype=torch.int16, device="cuda")
+    out = o_big.view(torch.bfloat16)[:, :N]
+    fp8.block_gemm(a_big[:, :K], torch.from_numpy(as_).cuda(), torch.from_numpy(wq).cuda(),
+                   torch.from_numpy(ws).cuda(), out=out)
+    torch.cuda.synchronize()
+    check_out(host_u16(out), gemm.gemm_block_ref(aq, as_, wq, ws), f"wide strides {which}")
+    if which == "wide_out":
+        assert (o_big[:, N:N + 64] == 0x7E00).all().item()      # nothing past the row written
+    del a_big, o_big
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_gemm_decode_full(M):
     d = synth.make_config("decode", M=M)
