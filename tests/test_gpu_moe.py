@@ -6,7 +6,7 @@ tolerance gate of the block GEMM: both kernel paths (the decode tile for a
 few rows per expert, including its 16-row chunk loop, and the grouped
 hand-scheduled kernel in both tile shapes), empty experts, rows in no
 expert's range left untouched, ragged segments crossing 256-row tiles,
-clamped offsets, bit-identity with fp8_block_gemm for a single expert, and
+clamped offsets, an activation stride past 32-bit buffer offsets, bit-identity with fp8_block_gemm for a single expert, and
 sampled rows of the two full MoE workloads.
 """
 
@@ -138,6 +138,25 @@ def test_single_expert_bit_identical_to_block_gemm():
     plain16 = fp8.block_gemm(dev(aq[5:13]), dev(as_[5:13]), dev(wq[0]), dev(ws[0]))
     torch.cuda.synchronize()
     assert np.array_equal(got16[5:13], host_u16(plain16))
+
+
+def test_wide_activation_stride_uses_the_decode_tile():
+    # 200 rows over 2 experts would take the grouped hand-scheduled kernel;
+    # an activation stride past its 32-bit buffer offsets sends the call to
+    # the grouped decode tile, which has no such limit
+    E, N, K, M = 2, 256, 512, 200
+    aq, as_, wq, ws = operands(67, E, N, K, M)
+    offsets = [0, 120, 200]
+    ld_a = (1 << 23) + 16
+    a_big = torch.zeros((M, ld_a), dtype=torch.uint8, device="cuda")
+    a_big[:, :K] = torch.from_numpy(aq).cuda()
+    out = torch.full((M, N), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    fp8.grouped_gemm(a_big[:, :K], dev(as_), dev(wq), dev(ws), dev(np.asarray(offsets, np.int64)),
+                     out=out)
+    torch.cuda.synchronize()
+    check(host_u16(out), aq, as_, wq, ws, offsets, "wide activation stride")
+    del a_big
+    torch.cuda.empty_cache()
 
 
 def test_offsets_are_clamped():
