@@ -278,6 +278,37 @@ def check_out(out_bits, ref, what):
     return r
 
 
+@pytest.mark.parametrize("K", [32768, 33280])
+def test_gemm_longest_k(K):
+    # K = 32768 fills the hand-scheduled kernel's weight-scale table (256 K
+    # blocks); one more 512 goes to the C++ prefill kernel
+    M, N = 300, 256
+    rng = np.random.default_rng(K)
+    a_bits = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    w_bits = synth.f32_to_bf16_bits(rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02))
+    log("gemm longest K", (M, N, K))
+    check_out(run_gemm(a_bits, w_bits), oracle_gemm(a_bits, w_bits), f"K={K}")
+
+
+def test_gemm_longest_k_256_tiles_sampled():
+    # the 256 x 256 tile shape at K = 32768 (both rows of the weight-scale
+    # table): the device quantizes for the call, the oracle re-quantizes the
+    # sampled activation rows and weight blocks for the check
+    M, N, K = 2304, 4096, 32768
+    rng = np.random.default_rng(72)
+    a_bits = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    w_bits = synth.f32_to_bf16_bits(rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02))
+    log("gemm longest K, 256x256 tiles", (M, N, K))
+    out = run_gemm(a_bits, w_bits)
+    rows = np.array([0, 1, 255, 256, 1000, 2047, 2048, M - 1])
+    blocks = [0, 17, 31]                               # weight blocks of 128 rows
+    cols = np.concatenate([np.arange(b * 128, b * 128 + 128) for b in blocks])
+    aq, as_ = quant.quant_act_ref(a_bits[rows])
+    wq, ws = quant.quant_weight_block_ref(w_bits[cols])
+    check_out(np.ascontiguousarray(out[rows][:, cols]), gemm.gemm_block_ref(aq, as_, wq, ws),
+              "K=32768 256x256 sampled")
+
+
 @pytest.mark.parametrize("which", ["wide_a", "wide_out"])
 def test_gemm_strides_beyond_32bit_offsets(which):
     # leading dimensions past the hand-scheduled kernel's 32-bit buffer
