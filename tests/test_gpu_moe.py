@@ -80,6 +80,9 @@ CASES = {
     "decode_k640": (2, 256, 640, [150, 90], 1, 0),
     "asm_w4": (3, 512, 1024, [300, 0, 530], 5, 7),
     "asm_k512_edges": (4, 384, 512, [255, 256, 257, 1], 0, 2),
+    # the longest K of a grouped call (128 K blocks) on both paths
+    "decode_k16384": (3, 256, 16384, [5, 20, 0], 1, 0),
+    "asm_k16384": (2, 256, 16384, [300, 100], 0, 0),
 }
 
 

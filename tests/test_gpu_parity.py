@@ -358,7 +358,9 @@ def test_gemm_tiny_full():
                                    # one K block past 64 rows; one 128-wide N tile on both
                                    # large-M kernels
                                    (65, 128, 128), (300, 128, 512), (70, 128, 2176),
+                                   # K / 128 = 128: the decode tile's longest K (both forms);
                                    # K / 128 > 128: the 128 x 128 tile kernel
+                                   (5, 256, 16384), (40, 256, 16384),
                                    (10, 256, 16512), (40, 256, 16512)])
 def test_gemm_ragged_full(M, N, K):
     rng = np.random.default_rng([M, N, K])
@@ -474,7 +476,7 @@ def _two_call(x, wq, ws, mode):
     return host_u16(fp8.block_gemm(aq, as_, wq, ws, mode))
 
 
-@pytest.mark.parametrize("K", [512, 4096])
+@pytest.mark.parametrize("K", [512, 4096, 16384])
 def test_linear_fused_matches_two_calls(K):
     """The fused decode path is bit-identical to quant_act + block_gemm."""
     rng = np.random.default_rng([K, 7])
