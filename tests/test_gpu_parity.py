@@ -175,6 +175,19 @@ def test_quant_act_strided_and_ragged():
     assert np.all(sbuf[:, 8:].cpu().numpy() == 0)
 
 
+@pytest.mark.parametrize("M,K", [(3, 1 << 20), (100003, 128)])
+def test_quant_act_extreme_shapes(M, K):
+    # a 2^20-element row (256 workgroups per row) and 100003 one-group rows
+    # (groups numbered across rows); codes and scales bit-exact
+    rng = np.random.default_rng([M, K])
+    bits = synth.f32_to_bf16_bits((rng.standard_normal((M, K)) * 3).astype(np.float32))
+    log("quant extreme", (M, K))
+    q, s = gpu_quant_act(bits)
+    wq, ws = quant.quant_act_ref(bits)
+    assert_codes_equal(q, wq, f"codes {M}x{K}")
+    assert_scales_equal(s, ws, f"scales {M}x{K}")
+
+
 def test_quant_act_empty():
     x = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
     q, s = fp8.quant_act(x)
