@@ -59,9 +59,8 @@ def assert_equal_scales(got, want, what):
         raise AssertionError(f"{what}: scale mismatch at {i}: got {got[i]!r} want {want[i]!r}")
 
 
-def check_out(out_bits, refb, what):
-    ref, bound = refb
-    r = tolerance.check(out_bits, ref, bound)
+def check_out(out_bits, refd, what):
+    r = oracle_refs.check(out_bits, refd)
     log(what, {k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
     assert r["ok"], (what, r)
 

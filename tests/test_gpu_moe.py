@@ -66,9 +66,9 @@ def run_grouped(aq, as_, wq, ws, offsets):
 
 
 def check(got, aq, as_, wq, ws, offsets, what):
-    ref, bound = oracle_refs.grouped(aq, as_, wq, ws, offsets)
-    covered = ~np.isnan(ref[:, 0])
-    r = tolerance.check(got[covered], ref[covered], bound[covered])
+    d = oracle_refs.grouped(aq, as_, wq, ws, offsets)
+    covered = ~np.isnan(d["ref"][:, 0])
+    r = oracle_refs.check(got[covered], oracle_refs.select(d, np.flatnonzero(covered)))
     log(what, {k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
     assert r["ok"], (what, r)
     assert (got[~covered] == SENTINEL).all(), f"{what}: rows in no segment were written"
@@ -123,8 +123,7 @@ def test_grouped_w8_sampled():
     inside = (rows >= offsets[0]) & (rows < offsets[-1])
     sub_off = np.concatenate([[0], np.cumsum([np.sum(inside & (expert == e)) for e in range(E)])])
     order = rows[inside]
-    ref_rows, bound = oracle_refs.grouped(aq[order], as_[order], wq, ws, sub_off)
-    r = tolerance.check(got[order], ref_rows, bound)
+    r = oracle_refs.check(got[order], oracle_refs.grouped(aq[order], as_[order], wq, ws, sub_off))
     log("grouped w8 sampled", r)
     assert r["ok"], r
     assert (got[rows[~inside]] == SENTINEL).all()
@@ -204,9 +203,8 @@ def test_full_workload_sampled(name):
     for e in picks:
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         sample = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 6)]))
-        ref, bound = oracle_refs.grouped(aq[sample], as_[sample], ref_w[e][0][None],
-                                         ref_w[e][1][None], [0, len(sample)])
-        r = tolerance.check(got[sample], ref, bound)
+        r = oracle_refs.check(got[sample], oracle_refs.grouped(
+            aq[sample], as_[sample], ref_w[e][0][None], ref_w[e][1][None], [0, len(sample)]))
         log(name, "expert", e, "rows", hi - lo, r)
         assert r["ok"], (name, e, r)
     assert not (got == SENTINEL).any(), "every row belongs to an expert here"

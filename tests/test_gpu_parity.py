@@ -4,9 +4,10 @@ Every call goes through the C ABI (libfp8w8a8.so via the ctypes binding).
 Inputs are the seeded workloads; expected values come from oracle/ only.
 Codes and scales must be bit-exact; the GEMM must pass the oracle's
 tolerance gate (elementwise 1e-2 * rms(ref) + half a bf16 ulp, Frobenius
-<= 4e-3).  Full-size workloads are compared on every code and scale where the
-oracle is fast enough, otherwise on sampled rows / block rows and on sampled
-output rows and columns computed by the oracle from the bf16 inputs.
+<= 4e-3, the accumulation bound and the bf16-neighbour clause).
+Codes and scales are compared in full on every workload.  GEMM outputs are
+compared in full on every workload except the 8192 x 28672 x 8192 one, where
+stratified full rows and full columns cover every output tile of the launch.
 """
 
 import sys
@@ -147,17 +148,13 @@ def test_quant_act_configs_full(name, M):
     assert_codes_equal(q, wq, f"codes[{name}]")
 
 
-def test_quant_act_large_sampled_rows():
-    c = synth.CONFIGS["large"]
-    ch = synth.outlier_channels(c["cfg"], c["K"], c["n_outliers"])
-    bits = synth.make_activation(c["cfg"], c["M"], c["K"], c["a_kind"], c["a_std"], ch,
-                                 c["outlier_mult"])
-    log("quant_act large", bits.shape)
-    q, s = gpu_quant_act(bits)
-    rows = np.random.default_rng(42).choice(c["M"], 256, replace=False)
-    wq, ws = quant.quant_act_ref(bits[rows])
-    assert_scales_equal(s[rows], ws, "scales[large]")
-    assert_codes_equal(q[rows], wq, "codes[large]")
+def test_quant_act_large_full():
+    # every code and scale of the 8192 x 8192 activation (oracle in row chunks)
+    d, wq, ws, _, _ = oracle_refs.workload("large")
+    log("quant_act large", d["A"].shape)
+    q, s = gpu_quant_act(d["A"])
+    assert_scales_equal(s, ws, "scales[large]")
+    assert_codes_equal(q, wq, "codes[large]")
 
 
 def test_quant_act_strided_and_ragged():
@@ -210,16 +207,13 @@ def test_quant_weight_configs_full(name):
     assert_codes_equal(q, wq, f"wcodes[{name}]")
 
 
-def test_quant_weight_large_sampled_blocks():
-    c = synth.CONFIGS["large"]
-    bits = synth.make_weight(c["cfg"], c["N"], c["K"], c["w_std"])
-    log("quant_weight large", bits.shape)
-    q, s = gpu_quant_weight(bits)
-    for nb in (0, 77, 223):
-        sl = slice(nb * 128, (nb + 1) * 128)
-        wq, ws = quant.quant_weight_block_ref(bits[sl])
-        assert_scales_equal(s[nb:nb + 1], ws, f"wscales[large:{nb}]")
-        assert_codes_equal(q[sl], wq, f"wcodes[large:{nb}]")
+def test_quant_weight_large_full():
+    # all 224 block rows of the 28672 x 8192 weight
+    d, _, _, wq, ws = oracle_refs.workload("large")
+    log("quant_weight large", d["W"].shape)
+    q, s = gpu_quant_weight(d["W"])
+    assert_scales_equal(s, ws, "wscales[large]")
+    assert_codes_equal(q, wq, "wcodes[large]")
 
 
 def test_quant_weight_edge_blocks():
@@ -277,7 +271,7 @@ def run_gemm(a_bits, w_bits, mode="block"):
 
 
 def oracle_gemm(a_bits, w_bits, mode="block"):
-    """(ref, accumulation bound) of the oracle on the oracle's own codes."""
+    """The oracle's reference dict (oracle_refs) on the oracle's own codes."""
     if mode == "block":
         aq, as_ = quant.quant_act_ref(a_bits)
         wq, ws = quant.quant_weight_block_ref(w_bits)
@@ -287,9 +281,8 @@ def oracle_gemm(a_bits, w_bits, mode="block"):
     return oracle_refs.tensor(aq, as_, wq, ws)
 
 
-def check_out(out_bits, refb, what):
-    ref, bound = refb
-    r = tolerance.check(out_bits, ref, bound)
+def check_out(out_bits, refd, what):
+    r = oracle_refs.check(out_bits, refd)
     log(what, {k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
     assert r["ok"], (what, r)
     return r
@@ -390,48 +383,73 @@ def test_gemm_ragged_full(M, N, K):
     check_out(out_t, oracle_gemm(a, w, "tensor"), f"ragged tensor {M}x{N}x{K}")
 
 
-def _sampled(name, rows_n, cols_n, mode="block"):
-    c = synth.CONFIGS[name]
-    d = synth.make_config(name)
-    log("gemm sampled", name, mode, (d["M"], d["N"], d["K"]))
-    out = run_gemm(d["A"], d["W"], mode)
-    rng = np.random.default_rng(44)
-    rows = np.sort(rng.choice(d["M"], rows_n, replace=False))
-    cols = np.sort(rng.choice(d["N"], cols_n, replace=False))
-    if mode == "block":
-        aq, as_ = quant.quant_act_ref(d["A"][rows])
-        wq_rows = np.empty((cols_n, d["K"]), dtype=np.uint8)
-        ws_rows = np.empty((cols_n, d["K"] // 128), dtype=np.float32)
-        for nb in np.unique(cols // 128):
-            sl = slice(nb * 128, (nb + 1) * 128)
-            bq, bs = quant.quant_weight_block_ref(d["W"][sl])
-            sel = np.nonzero(cols // 128 == nb)[0]
-            wq_rows[sel] = bq[cols[sel] - nb * 128]
-            ws_rows[sel] = bs[0]
-        ref = oracle_refs.block_rows(aq, as_, wq_rows, ws_rows)
-    else:
-        a_amax = quant.tensor_amax_ref(d["A"])
-        w_amax = quant.tensor_amax_ref(d["W"])
-        aq, as_ = quant.quant_tensor_with_amax_ref(d["A"][rows], a_amax)
-        wq, ws = quant.quant_tensor_with_amax_ref(d["W"][cols], w_amax)
-        ref = oracle_refs.tensor(aq, as_, wq, ws)
-    return check_out(out[np.ix_(rows, cols)], ref, f"{name} {mode} sampled")
+def test_gemm_prefill_full():
+    # every output of the 4096^3 GEMM in the launch configuration the bench
+    # times, against the oracle on its own codes
+    d, aq, as_, wq, ws = oracle_refs.workload("prefill")
+    log("gemm prefill full", (d["M"], d["N"], d["K"]))
+    out = run_gemm(d["A"], d["W"])
+    check_out(out, oracle_refs.block(aq, as_, wq, ws), "prefill full")
 
 
-def test_gemm_prefill_sampled():
-    _sampled("prefill", 96, 1024)
+def test_gemm_mlp_down_full():
+    d, aq, as_, wq, ws = oracle_refs.workload("mlp_down")
+    log("gemm mlp_down full", (d["M"], d["N"], d["K"]))
+    out = run_gemm(d["A"], d["W"])
+    check_out(out, oracle_refs.block(aq, as_, wq, ws), "mlp_down full")
 
 
-def test_gemm_mlp_down_sampled():
-    _sampled("mlp_down", 64, 1024)
+def test_gemm_mlp_down_tensor_full():
+    d = oracle_refs.workload("mlp_down")[0]
+    log("gemm mlp_down tensor full", (d["M"], d["N"], d["K"]))
+    out = run_gemm(d["A"], d["W"], "tensor")
+    a_amax = quant.tensor_amax_ref(d["A"])
+    w_amax = quant.tensor_amax_ref(d["W"])
+    aq, as_ = oracle_refs.parallel_rows(lambda b: quant.quant_tensor_with_amax_ref(b, a_amax),
+                                        d["A"], 256)
+    wq, ws = oracle_refs.parallel_rows(lambda b: quant.quant_tensor_with_amax_ref(b, w_amax),
+                                       d["W"], 512)
+    check_out(out, oracle_refs.tensor(aq, as_[:1], wq, ws[:1]), "mlp_down tensor full")
 
 
-def test_gemm_mlp_down_tensor_sampled():
-    _sampled("mlp_down", 64, 1024, "tensor")
+def stratified(extent, tile, per_tile, seed):
+    """``per_tile`` indices in every ``tile``-wide tile of [0, extent): the
+    offsets within the tile cycle through every residue mod 16 and through
+    both halves of the tile, so every fragment row position and wave row of
+    the launch is sampled."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for t in range(-(-extent // tile)):
+        for j in range(per_tile):
+            k = t * per_tile + j
+            off = (k % 16) + 16 * int(rng.integers(0, tile // 16))
+            off = (off % (tile // 2)) + (tile // 2) * (k % 2)
+            if t * tile + off < extent:
+                out.append(t * tile + off)
+    return np.unique(np.array(out))
 
 
-def test_gemm_large_sampled():
-    _sampled("large", 48, 768)
+def test_gemm_large_stratified():
+    # 8192 x 28672 x 8192: two rows in every 256-row M tile compared on all
+    # 28672 columns, and two columns in every 256-wide N tile compared on all
+    # 8192 rows, so every output tile of the full launch is checked
+    d, aq, as_, wq, ws = oracle_refs.workload("large")
+    log("gemm large", (d["M"], d["N"], d["K"]))
+    out = run_gemm(d["A"], d["W"])
+    rows = stratified(d["M"], 256, 2, 45)
+    cols = stratified(d["N"], 256, 2, 46)
+    assert len(rows) == 64 and len(cols) == 224
+    assert sorted(set(rows % 16)) == list(range(16)) and sorted(set(cols % 16)) == list(range(16))
+    for lo in range(0, d["N"], 4096):                  # full rows, in column chunks
+        sl = np.arange(lo, min(lo + 4096, d["N"]))
+        check_out(np.ascontiguousarray(out[np.ix_(rows, sl)]),
+                  oracle_refs.block_cols(aq[rows], as_[rows], wq, ws, sl, 1 << 28),
+                  f"large rows x cols {lo}..")
+    for lo in range(0, d["M"], 2048):                  # full columns, in row chunks
+        rs = np.arange(lo, lo + 2048)
+        check_out(np.ascontiguousarray(out[np.ix_(rs, cols)]),
+                  oracle_refs.block_cols(aq[rs], as_[rs], wq, ws, cols, 1 << 28),
+                  f"large rows {lo}.. x cols")
 
 
 def test_gemm_small_integers_exact():
