@@ -221,25 +221,49 @@ class Workload:
         return sum(gemm_flops(M, self.N, self.K) for M in self.Ms)
 
 
-def time_gemm_launches(wl, n_launches):
-    """Average duration of the GEMM kernel: one HIP event pair on the launch
-    stream around n back-to-back GEMM launches (cycling through the batch
-    sizes and weight copies of the step), all queued behind a bounded
-    GPU-side delay so that no host gap falls inside the timed span."""
-    import torch
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(5e7))          # a bounded GPU-side delay while the host queues work
-    e0.record()
-    for i in range(n_launches):
-        j = i % len(wl.Ms)
-        wl.fp8.block_gemm(wl.aq[j], wl.as_[j], wl.wq[i % wl.ncopy], wl.ws, wl.mode,
-                          out=wl.out[j])
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n_launches
-    return float(ms), n_launches
+def gemm_kernel_name(M, K):
+    """The kernel fp8_block_gemm dispatches for an M x K activation (the
+    library's dispatch rule: the decode tile up to 64 rows and K <= 16384,
+    the hand-scheduled prefill kernel above 64 rows when K % 512 == 0)."""
+    if M <= 64 and K // 128 <= 128:
+        return "gemm_decode_kernel"
+    return "gemm_prefill_asm_kernel" if (K // 128) % 4 == 0 else "gemm_prefill_kernel"
+
+
+def fused_bytes(M, N, K):
+    """Algorithmic bytes of one fused linear launch: bf16 input, weight codes
+    and scales, bf16 output (the activation codes never leave the chip)."""
+    return 2 * M * K + N * K + 4 * (N // 128) * (K // 128) + 2 * M * N
+
+
+def time_step_kernels(wl, n_per):
+    """For each batch size of the step, the launch that carries its GEMM:
+    the fused linear kernel where the step's fp8_linear call is one launch,
+    otherwise the GEMM kernel alone (on codes quantized beforehand).  Each is
+    timed as n_per back-to-back launches (rotating over the weight copies)
+    with one HIP event pair on the launch stream, behind a bounded GPU-side
+    delay so that no host gap falls inside the timed span."""
+    pt = wl.mode == "tensor"
+    res = []
+    for j, M in enumerate(wl.Ms):
+        fused = wl.lin_ws[j] is None
+        if fused:
+            def fn(i, j=j):
+                wl.fp8.linear(wl.x[j], wl.wq[i % wl.ncopy], wl.ws, wl.mode, out=wl.out[j])
+            b, kernel = fused_bytes(M, wl.N, wl.K), "linear_decode_kernel"
+        else:
+            def fn(i, j=j):
+                wl.fp8.block_gemm(wl.aq[j], wl.as_[j], wl.wq[i % wl.ncopy], wl.ws, wl.mode,
+                                  out=wl.out[j])
+            b, kernel = gemm_bytes(M, wl.N, wl.K, pt), gemm_kernel_name(M, wl.K)
+        ms = time_launches(fn, n_per)
+        f = gemm_flops(M, wl.N, wl.K)
+        res.append({"M": M, "kernel": kernel, "avg_launch_us": ms * 1e3, "launches_timed": n_per,
+                    "algorithmic_bytes": b, "GB/s": b / (ms * 1e-3) / 1e9,
+                    "frac_of_8000": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "flop": f, "TFLOP/s": f / (ms * 1e-3) / 1e12,
+                    "frac_of_5000": f / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS})
+    return res
 
 
 def time_quantizer(wl):
@@ -283,67 +307,152 @@ def calibration_copy():
     del src, dst
 
 
-def secondary_prefill(steps=20):
-    """GEMM-only TFLOP/s of the 4096^3 prefill shape, as context in the decode line."""
+SECONDARY = ("prefill", "mlp_down", "mlp_down_tensor", "large")
+
+
+def secondary_gemm(name, n_launches=None):
+    """GEMM-only TFLOP/s of a prefill-shaped workload (codes quantized
+    beforehand), as context in the decode line."""
     import torch
-    wl = Workload("prefill")
-    for s in range(3):
+    wl = Workload(name)
+    for s in range(2):
         wl.step(s)
     torch.cuda.synchronize()
-    ms, n = time_gemm_launches(wl, steps)
-    tf = wl.flops_per_step() / (ms * 1e-3) / 1e12
+    n = n_launches or (8 if wl.Ms[0] * wl.N * wl.K > 1e12 else 24)
+    r = dict(time_step_kernels(wl, n)[0])
+    r.update({"workload": name, "N": wl.N, "K": wl.K,
+              "scales": "per-tensor" if wl.mode == "tensor" else "A 1x128, W 128x128"})
     del wl
     torch.cuda.empty_cache()
-    return {"workload": "prefill M=N=K=4096", "kernel": "gemm_prefill_asm_kernel",
-            "gemm_us": ms * 1e3, "TFLOP/s": tf, "frac_of_5000": tf / FP8_PEAK_TFLOPS}
+    return r
+
+
+def hbm_reference(nbytes=1 << 30, n=10):
+    """Timed HBM reference beside the kernels: torch's device copy of
+    a 1 GiB buffer (2 GiB moved per launch) and torch's sum over it (a pure
+    1 GiB read), each n back-to-back launches timed like the kernels."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    acc = torch.empty((), dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    c_ms = time_launches(lambda i: dst.copy_(src), n)
+    r_ms = time_launches(lambda i: torch.sum(src.view(torch.int32), dim=0, out=acc), n)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy": {"bytes_moved": 2 * nbytes, "avg_launch_us": c_ms * 1e3,
+                     "GB/s": 2 * nbytes / (c_ms * 1e-3) / 1e9},
+            "read_sum": {"bytes_read": nbytes, "avg_launch_us": r_ms * 1e3,
+                         "GB/s": nbytes / (r_ms * 1e-3) / 1e9},
+            "note": "torch.Tensor.copy_ and torch.sum over a 1 GiB device buffer"}
+
+
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def blas_threads():
+    try:
+        import threadpoolctl
+        return max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def oracle_linear_sample(A_bits, W_bits, a_rows, w_rows, mode, target_s, max_reps=1000):
+    """Repeat the oracle's quantization of a_rows rows of A and its GEMM
+    against w_rows rows of W (quantized once beforehand, as offline weight
+    quantization is) for about target_s seconds.  Returns (reps, seconds,
+    bytes moved per the algorithmic count, flop)."""
+    from oracle import gemm, quant
+    K = A_bits.shape[1]
+    if mode == "block":
+        rwq, rws = quant.quant_weight_block_ref(W_bits[:w_rows])
+    else:
+        rwq, rws = quant.quant_tensor_with_amax_ref(W_bits[:w_rows], quant.tensor_amax_ref(W_bits))
+    ab = A_bits[:a_rows]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        if mode == "block":
+            aq, as_ = quant.quant_act_ref(ab)
+            gemm.gemm_block_ref(aq, as_, rwq, rws)
+        else:
+            aq, as_ = quant.quant_tensor_ref(ab)
+            gemm.gemm_tensor_ref(aq, as_, rwq, rws)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= max_reps:
+            break
+    nbytes = quant_bytes(a_rows, K) + gemm_bytes(a_rows, w_rows, K, mode != "block")
+    return reps, el, reps * nbytes, reps * gemm_flops(a_rows, w_rows, K)
+
+
+def single_thread_baselines(target_s):
+    """The oracle on one BLAS thread, on bounded samples of the tiny, decode
+    (M = 16) and prefill workloads: quantize the activation rows and multiply
+    them against weight rows quantized beforehand."""
+    from workloads import synth
+    try:
+        import threadpoolctl
+        limit = threadpoolctl.threadpool_limits(1)
+    except Exception:
+        limit = None
+    out = []
+    try:
+        for name, M, a_rows, w_rows in (("tiny", None, 16, 256), ("decode", 16, 16, 1024),
+                                        ("prefill", None, 64, 512)):
+            d = synth.make_config(name, M=M)
+            reps, el, nb, fl = oracle_linear_sample(d["A"], d["W"], a_rows, w_rows, "block",
+                                                    target_s)
+            out.append({"workload": name, "threads": 1, "GB/s": nb / el / 1e9,
+                        "GFLOP/s": fl / el / 1e9, "seconds": round(el, 2),
+                        "sample": f"quant_act of {a_rows} rows of A (K={d['K']}) + fp64 GEMM "
+                                  f"against {w_rows} of {d['N']} weight rows, repeated {reps}x"})
+    finally:
+        if limit is not None:
+            limit.unregister()
+    return out
 
 
 def cpu_baseline(wl, target_s):
-    """Oracle timed on the host on a bounded sample of the same step."""
-    from oracle import gemm, quant
-    try:
-        import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
-    except Exception:
-        threads = os.cpu_count() or 1
-    if wl.mode == "block":
-        # weight quantization is offline: done once, outside the timed sample
-        if len(wl.Ms) > 1:
-            rows = wl.N
-        else:
-            rows = 128 * max(1, min(wl.N // 128, 4))
-        rwq, rws = quant.quant_weight_block_ref(wl.W_bits[:rows])
+    """Oracle timed on the host on a bounded sample of the same step, with
+    all BLAS threads, then on one thread for the tiny, decode and prefill
+    workloads."""
+    threads = blas_threads()
+    if len(wl.Ms) > 1 or wl.mode != "block":
+        rows = wl.N if len(wl.Ms) > 1 else 128 * max(1, min(wl.N // 128, 4))
     else:
         rows = 128 * max(1, min(wl.N // 128, 4))
-        amax_w = quant.tensor_amax_ref(wl.W_bits)
-        rwq, rws = quant.quant_tensor_with_amax_ref(wl.W_bits[:rows], amax_w)
     a_rows = [min(M, 256) for M in wl.Ms]
-    nbytes = 0
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        for j, M in enumerate(wl.Ms):
-            ab = wl.A_bits[j][:a_rows[j]]
-            if wl.mode == "block":
-                aq, as_ = quant.quant_act_ref(ab)
-                gemm.gemm_block_ref(aq, as_, rwq, rws)
-                nbytes += quant_bytes(a_rows[j], wl.K) + gemm_bytes(a_rows[j], rows, wl.K)
-            else:
-                aq, as_ = quant.quant_tensor_ref(ab)
-                gemm.gemm_tensor_ref(aq, as_, rwq, rws)
-                nbytes += quant_bytes(a_rows[j], wl.K) + gemm_bytes(a_rows[j], rows, wl.K, True)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= target_s or reps >= 1000:
-            break
-    flops = sum(gemm_flops(r, rows, wl.K) for r in a_rows) * reps
+    nbytes, flops, el_all, reps_all = 0, 0, 0.0, []
+    per = target_s / len(wl.Ms)
+    for j, M in enumerate(wl.Ms):
+        reps, el, nb, fl = oracle_linear_sample(wl.A_bits[j], wl.W_bits, a_rows[j], rows,
+                                                wl.mode, per)
+        nbytes += nb
+        flops += fl
+        el_all += el
+        reps_all.append(reps)
     sample = (f"oracle quant_act + fp64 GEMM, rows M={a_rows} of A against {rows} of {wl.N} "
-              f"weight rows, K={wl.K}, repeated {reps}x; weight quantized beforehand")
+              f"weight rows, K={wl.K}, repeated {reps_all}x; weight quantized beforehand")
+    res = {"cores": threads, "kind": "oracle", "sample": sample, "seconds": round(el_all, 2),
+           "cpu_model": cpu_model(), "logical_cpus": os.cpu_count()}
     if len(wl.Ms) > 1:
-        return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-                "sample": sample, "seconds": round(el, 2)}
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": round(el, 2)}
+        res.update({"value": nbytes / el_all / 1e9, "unit": "GB/s"})
+    else:
+        res.update({"value": flops / el_all / 1e12, "unit": "TFLOP/s"})
+    res["single_thread"] = single_thread_baselines(min(3.0, target_s / 3))
+    return res
 
 
 def kv_write_bytes(T, HD):
@@ -738,28 +847,31 @@ def main():
     flops = wl.flops_per_step()
     Ms, N_, K_, mode, ncopy = wl.Ms, wl.N, wl.K, wl.mode, wl.ncopy
 
-    n_l = 96 if decode else 24
-    g_ms_mean, n_l = time_gemm_launches(wl, n_l)
-    gemm_bytes_per_launch = g_b / wl.launches_per_step
-    flops_per_launch = flops / wl.launches_per_step
+    n_l = 32 if decode else 24
+    launches = time_step_kernels(wl, n_l)
+    tot_us = sum(r["avg_launch_us"] for r in launches)
+    tot_b = sum(r["algorithmic_bytes"] for r in launches)
+    tot_f = sum(r["flop"] for r in launches)
+    kernels = sorted({r["kernel"] for r in launches})
 
     if decode:
         metric_value = total_b / (sec / K) / 1e9
         unit = "GB/s"
-        roof = {"bound": "hbm", "achieved": gemm_bytes_per_launch / (g_ms_mean * 1e-3) / 1e9,
+        roof = {"bound": "hbm", "achieved": tot_b / (tot_us * 1e-6) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
         metric_value = flops / (sec / K) / 1e12
         unit = "TFLOP/s"
-        roof = {"bound": "mfma", "achieved": flops_per_launch / (g_ms_mean * 1e-3) / 1e12,
+        roof = {"bound": "mfma", "achieved": tot_f / (tot_us * 1e-6) / 1e12,
                 "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(args.workload)
-    roof["kernel"] = dominant_kernel(args.workload, decode)
-    roof["avg_launch_us"] = g_ms_mean * 1e3
-    roof["launches_timed"] = n_l
+    roof["kernel"] = " + ".join(kernels)
+    roof["avg_launch_us"] = tot_us / len(launches)
+    roof["launches_timed"] = n_l * len(launches)
     roof["algorithmic_bytes_per_launch" if decode else "flop_per_launch"] = (
-        gemm_bytes_per_launch if decode else flops_per_launch)
+        tot_b / len(launches) if decode else tot_f / len(launches))
+    roof["per_launch"] = launches
     roof["kernel_source_hash"] = kernel_source_hash()
 
     quantizer = time_quantizer(wl)
@@ -767,10 +879,11 @@ def main():
     if args.cpu_baseline_seconds > 0:
         cpu = cpu_baseline(wl, args.cpu_baseline_seconds)
     secondary = None
+    hbm_ref = hbm_reference()
     if decode and not args.no_secondary:
         del wl
         torch.cuda.empty_cache()
-        secondary = secondary_prefill()
+        secondary = [secondary_gemm(n) for n in SECONDARY]
 
     config = {"workload": args.workload, "M": Ms if decode else Ms[0], "N": N_, "K": K_,
               "scales": "per-tensor" if mode == "tensor" else "A 1x128, W 128x128",
@@ -799,6 +912,7 @@ def main():
         "tflops_per_step": flops / (sec / K) / 1e12,
         "secondary": secondary,
         "quantizer": quantizer,
+        "hbm_reference": hbm_ref,
     }
     print(json.dumps(line), flush=True)
 

@@ -81,8 +81,22 @@ def test_decode_line_fields():
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-12
     assert 0 < roof["frac"] < 1
-    assert roof["kernel"] == "gemm_decode_kernel"
+    # the step's GEMM-carrying launches: the fused linear kernel for M = 1
+    # and 4, the decode GEMM for M = 16 (its activation quantized before)
+    assert roof["kernel"] == "gemm_decode_kernel + linear_decode_kernel"
+    per = {r["M"]: r for r in roof["per_launch"]}
+    assert sorted(per) == [1, 4, 16]
+    assert per[1]["kernel"] == per[4]["kernel"] == "linear_decode_kernel"
+    assert per[16]["kernel"] == "gemm_decode_kernel"
+    us = sum(r["avg_launch_us"] for r in per.values())
+    b = sum(r["algorithmic_bytes"] for r in per.values())
+    assert abs(roof["achieved"] - b / (us * 1e-6) / 1e9) < 1e-6 * roof["achieved"]
     assert "traffic" in roof
+    ref = line["hbm_reference"]
+    assert ref["copy"]["GB/s"] > 0 and ref["read_sum"]["GB/s"] > 0
     cpu = line["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1
     assert isinstance(cpu["sample"], str) and cpu["unit"] == "GB/s"
+    assert isinstance(cpu["cpu_model"], str) and cpu["cpu_model"]
+    assert [r["workload"] for r in cpu["single_thread"]] == ["tiny", "decode", "prefill"]
+    assert all(r["threads"] == 1 and r["GFLOP/s"] > 0 for r in cpu["single_thread"])
