@@ -42,6 +42,16 @@ bool mode_ok(int scale_mode) {
          scale_mode == FP8_SCALE_ROW;
 }
 
+// Work-items of the quantizer's grid for R rows of K (per-tensor mode
+// strides over the data with a bounded grid).
+uint64_t quant_items(int64_t R, int64_t K, int scale_mode, bool rows_blocked) {
+  if (R <= 0) return 0;
+  if (scale_mode == FP8_SCALE_BLOCK)
+    return rows_blocked ? fp8k::quant_weight_block_items(R, K) : fp8k::quant_act_block_items(R, K);
+  if (scale_mode == FP8_SCALE_ROW) return fp8k::quant_rows_items(R);
+  return 0;
+}
+
 fp8_status validate_quant(const uint16_t* x, int64_t R, int64_t K, int64_t ld_x,
                           const uint8_t* q, int64_t ld_q, const float* scales, int64_t ld_s,
                           int scale_mode, const void* ws, size_t ws_bytes, bool rows_blocked) {
@@ -49,6 +59,7 @@ fp8_status validate_quant(const uint16_t* x, int64_t R, int64_t K, int64_t ld_x,
   if (R < 0 || R >= kMaxDim || !shape_ok_kn(K)) return FP8_ERR_SHAPE;
   if (rows_blocked && scale_mode == FP8_SCALE_BLOCK && R % 128 != 0) return FP8_ERR_SHAPE;
   if (R > 0 && R * K > kMaxElems) return FP8_ERR_SHAPE;
+  if (quant_items(R, K, scale_mode, rows_blocked) >= fp8k::kMaxGridItems) return FP8_ERR_SHAPE;
   if (R == 0) return FP8_OK;
   if (!x || !q || !scales) return FP8_ERR_NULL;
   const int64_t groups = K / 128;
@@ -88,6 +99,7 @@ fp8_status validate_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, int
   if (!mode_ok(scale_mode)) return FP8_ERR_SCHEME;
   if (M < 0 || M >= kMaxDim || !shape_ok_kn(K) || !shape_ok_kn(N)) return FP8_ERR_SHAPE;
   if (M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems) return FP8_ERR_SHAPE;
+  if (M > 0 && fp8k::gemm_items(M, N, K) >= fp8k::kMaxGridItems) return FP8_ERR_SHAPE;
   if (M == 0) return FP8_OK;
   if (!a_q || !a_s || !w_q || !w_s || !out) return FP8_ERR_NULL;
   const int64_t KB = K / 128;
@@ -157,6 +169,15 @@ LinearLayout linear_layout(int64_t M, int64_t K, int scale_mode) {
                 ? l.partials + (size_t)fp8k::kTensorPartials * sizeof(uint32_t)
                 : l.partials;
   return l;
+}
+
+// Work-items of the largest grid fp8_linear launches: the fused decode
+// kernel, or the quantizer and then the GEMM.
+uint64_t linear_items(int64_t M, int64_t N, int64_t K, int scale_mode) {
+  if (scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, K))
+    return fp8k::linear_decode_items(N);
+  const uint64_t q = quant_items(M, K, scale_mode, false), g = fp8k::gemm_items(M, N, K);
+  return q > g ? q : g;
 }
 
 }  // namespace
@@ -268,13 +289,21 @@ fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, in
                                     (hipStream_t)stream));
 }
 
-fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
-                      const float* w_s, int64_t ld_ws, uint16_t* out, int64_t ld_out,
-                      int64_t M, int64_t N, int64_t K, int scale_mode, void* workspace,
-                      size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of fp8_linear and fp8_linear_noalloc (everything but the
+// workspace).  Sets fused (one launch, no workspace) and the workspace
+// layout of the unfused path.
+fp8_status validate_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
+                           const float* w_s, int64_t ld_ws, const uint16_t* out, int64_t ld_out,
+                           int64_t M, int64_t N, int64_t K, int scale_mode, bool& fused,
+                           LinearLayout& lay) {
   if (!mode_ok(scale_mode)) return FP8_ERR_SCHEME;
   if (M < 0 || M >= kMaxDim || !shape_ok_kn(K) || !shape_ok_kn(N)) return FP8_ERR_SHAPE;
   if (M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems) return FP8_ERR_SHAPE;
+  if (M > 0 && linear_items(M, N, K, scale_mode) >= fp8k::kMaxGridItems) return FP8_ERR_SHAPE;
   if (M == 0) return FP8_OK;
   if (!x || !w_q || !w_s || !out) return FP8_ERR_NULL;
   const int64_t KB = K / 128;
@@ -293,20 +322,36 @@ fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
               : scale_mode == FP8_SCALE_ROW ? row_scales(w_s, N, ld_ws)
                                             : range_of(w_s, 1, 1, 1, 4);
   if (overlap(ro, rx) || overlap(ro, rw) || overlap(ro, rws)) return FP8_ERR_ALIAS;
-  const bool fused = scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, K);
-  LinearLayout lay = linear_layout(M, K, scale_mode);
-  if (!fused) {
-    if (!workspace || ws_bytes < lay.total || !aligned(workspace, 16)) return FP8_ERR_WORKSPACE;
-    Range rws2 = {(uintptr_t)workspace, (uintptr_t)workspace + lay.total};
-    if (overlap(rws2, ro) || overlap(rws2, rx) || overlap(rws2, rw) || overlap(rws2, rws))
-      return FP8_ERR_ALIAS;
-  }
-  fp8_status st = check_device();
-  if (st != FP8_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
+  fused = scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, K);
+  lay = linear_layout(M, K, scale_mode);
+  return FP8_OK;
+}
+
+// The workspace of an unfused call must not overlap its tensors.
+bool linear_workspace_clear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
+                            const float* w_s, int64_t ld_ws, const uint16_t* out, int64_t ld_out,
+                            int64_t M, int64_t N, int64_t K, int scale_mode, const void* ws,
+                            size_t bytes) {
+  const int64_t KB = K / 128;
+  Range rws = scale_mode == FP8_SCALE_BLOCK ? range_of(w_s, N / 128, KB, ld_ws, 4)
+              : scale_mode == FP8_SCALE_ROW ? row_scales(w_s, N, ld_ws)
+                                            : range_of(w_s, 1, 1, 1, 4);
+  Range r = {(uintptr_t)ws, (uintptr_t)ws + bytes};
+  return !overlap(r, range_of(out, M, N, ld_out, 2)) && !overlap(r, range_of(x, M, K, ld_x, 2)) &&
+         !overlap(r, range_of(w_q, N, K, ld_w, 1)) && !overlap(r, rws);
+}
+
+// Enqueue a validated linear call: the fused decode kernel, or the quantizer
+// into the workspace (activation codes, scales, per-tensor partials) and the
+// GEMM.
+fp8_status run_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
+                      const float* w_s, int64_t ld_ws, uint16_t* out, int64_t ld_out, int64_t M,
+                      int64_t N, int64_t K, int scale_mode, bool fused, const LinearLayout& lay,
+                      void* workspace, hipStream_t s) {
   if (fused)
     return launched(fp8k::launch_linear_decode(x, ld_x, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N,
                                                K, s));
+  const int64_t KB = K / 128;
   uint8_t* ws8 = (uint8_t*)workspace;
   uint8_t* q = ws8 + lay.codes;
   float* sa = (float*)(ws8 + lay.scales);
@@ -323,6 +368,30 @@ fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
   const int64_t lsw = scale_mode == FP8_SCALE_TENSOR ? 0 : ld_ws;
   return launched(fp8k::launch_gemm(q, lay.ld_q, sa, lsa, w_q, ld_w, w_s, lsw, out, ld_out, M, N,
                                     K, scale_mode != FP8_SCALE_BLOCK, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
+                      const float* w_s, int64_t ld_ws, uint16_t* out, int64_t ld_out,
+                      int64_t M, int64_t N, int64_t K, int scale_mode, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  bool fused = false;
+  LinearLayout lay{};
+  fp8_status st = validate_linear(x, ld_x, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N, K,
+                                  scale_mode, fused, lay);
+  if (st != FP8_OK || M == 0) return st;
+  if (!fused) {
+    if (!workspace || ws_bytes < lay.total || !aligned(workspace, 16)) return FP8_ERR_WORKSPACE;
+    if (!linear_workspace_clear(x, ld_x, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N, K, scale_mode,
+                                workspace, lay.total))
+      return FP8_ERR_ALIAS;
+  }
+  if ((st = check_device()) != FP8_OK) return st;
+  return run_linear(x, ld_x, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N, K, scale_mode, fused, lay,
+                    workspace, (hipStream_t)stream);
 }
 
 fp8_status fp8_validate_quant_act_static(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
@@ -359,6 +428,7 @@ fp8_status fp8_validate_grouped_gemm(const uint8_t* a_q, int64_t ld_a, const flo
   if (E < 0 || E > 65535) return FP8_ERR_SHAPE;
   if (M < 0 || M >= kMaxDim || !shape_ok_kn(K) || !shape_ok_kn(N)) return FP8_ERR_SHAPE;
   if (K / 128 > fp8k::kGroupedMaxKB) return FP8_ERR_SHAPE;
+  if (fp8k::grouped_items(N) >= fp8k::kMaxGridItems) return FP8_ERR_SHAPE;
   if (M * K > kMaxElems || M * N > kMaxElems || N * K > kMaxElems / (E > 0 ? E : 1))
     return FP8_ERR_SHAPE;
   if (M == 0 || E == 0) return FP8_OK;
@@ -488,7 +558,8 @@ fp8_status fp8_kv_cache_read(const uint8_t* cache, int64_t num_blocks, int64_t b
 }
 
 fp8_status fp8_e4m3_encode_f32(const float* x, int64_t n, uint8_t* codes, void* stream) {
-  if (n < 0 || n > kMaxElems) return FP8_ERR_SHAPE;
+  if (n < 0 || n > kMaxElems || fp8k::encode_items(n) >= fp8k::kMaxGridItems)
+    return FP8_ERR_SHAPE;
   if (n == 0) return FP8_OK;
   if (!x || !codes) return FP8_ERR_NULL;
   if (!aligned(x, 4)) return FP8_ERR_ALIGN;

@@ -814,13 +814,13 @@ __device__ __forceinline__ bool grouped_tile(const int64_t* __restrict__ offsets
 // NW = 8: 256 x 256 tiles, two waves per SIMD.  NW = 4: 256 x 128 tiles, one
 // wave per SIMD, for grids that would otherwise leave CUs idle (the same
 // 128 x 64 wave tile, so the K loop is the same schedule).
-// E > 0: the grouped (MoE) form, chosen at run time so the K loop exists
-// once per variant (its labels are fixed names).  The grid enumerates the
-// tiles of all experts (rounded up to a multiple of 8; workgroups past the
-// last tile exit at once), consecutive numbers on one XCD; each workgroup
-// finds its expert and tile and then runs the plain kernel on that expert's rows (A, scales and output rebased to the
-// expert's first row, M = its row count) and weight (w + e * w_es, sw +
-// e * sw_es).  The range-checked descriptors end at the expert's last row,
+// E > 0: the grouped (MoE) form, chosen at run time so the K loop's code
+// exists once per variant.  The grid enumerates the tiles of all experts
+// (rounded up to a multiple of 8; workgroups past the last tile exit at
+// once), consecutive numbers on one XCD; each workgroup finds its expert and
+// tile and then runs the plain kernel on that expert's rows (A, scales and
+// output rebased to the expert's first row, M = its row count) and weight
+// (w + e * w_es, sw + e * sw_es).  The range-checked descriptors end at the expert's last row,
 // so the next expert's rows are neither read nor written.
 template <bool KCONST, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
@@ -1187,6 +1187,22 @@ bool linear_decode_supported(int64_t M, int64_t K) {
   return M >= 1 && M <= FP8_LINEAR_FUSED_MAX_M && K / 128 <= kDecodeMaxKB;
 }
 
+// Work-items of the grid a GEMM launches: the decode tile (16 columns per
+// 64 * KSPLIT-thread workgroup) up to 64 rows, otherwise at most the
+// 128 x 128 tile kernel's (256 threads per 128 x 128 tile), which bounds the
+// prefill kernels' 256 x 128 and 256 x 256 tiles too.
+uint64_t gemm_items(int64_t M, int64_t N, int64_t K) {
+  if (M <= FP8_DECODE_MAX_M && K / 128 <= kDecodeMaxKB)
+    return (uint64_t)(N / 16) * 64u * FP8_DECODE_KSPLIT;
+  return (uint64_t)((M + kBM - 1) / kBM) * (uint64_t)(N / kBN) * 256u;
+}
+
+uint64_t linear_decode_items(int64_t N) { return (uint64_t)(N / 16) * 64u * FP8_DECODE_KSPLIT; }
+
+// The grouped call's decode-tile path (grid x: 16 columns per workgroup);
+// the grouped prefill path is taken only when its own grid fits.
+uint64_t grouped_items(int64_t N) { return (uint64_t)(N / 16) * 64u * FP8_DECODE_KSPLIT; }
+
 hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                        const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
                        uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
@@ -1265,10 +1281,15 @@ static_assert(kGroupedMaxKB <= kDecodeMaxKB, "grouped calls must fit the decode 
 bool grouped_prefill_ok(int64_t M, int64_t E, int64_t N, int64_t K, int64_t ld_a, int64_t ld_w,
                         int64_t ld_sa, int64_t ld_sw, int64_t ld_out) {
   const int64_t KB = K / 128;
+  // grid: at most (M + 255 E) / 256 M tiles times the N tiles of either tile
+  // shape, rounded up to a multiple of 8 workgroups
+  const uint64_t tm = (uint64_t)((M + (kPM - 1) * E) / kPM);
+  const uint64_t g8 = (tm * (uint64_t)((N + 255) / 256) + 7) / 8 * 8 * 512u;
+  const uint64_t g4 = (tm * (uint64_t)(N / 128) + 7) / 8 * 8 * 256u;
   return FP8_PREFILL_ASM && M > FP8_GROUPED_DECODE_MAX_AVG * E && KB % kPfKbGroup == 0 &&
          KB <= kPrefillMaxKB && ld_a < kPrefillMaxLd && ld_w < kPrefillMaxLd &&
          ld_out < kPrefillMaxLd / 2 && ld_sa < kPrefillMaxLd / 4 && ld_sw < kPrefillMaxLd &&
-         (M + (kPM - 1) * E) / kPM * (N / 128) < ((int64_t)1 << 31);
+         g8 < kMaxGridItems && g4 < kMaxGridItems;
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,

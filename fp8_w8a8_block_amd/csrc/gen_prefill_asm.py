@@ -16,8 +16,11 @@ K step is 32 MFMA slots (4 weight x 8 activation fragments of the wave's
 folded four MFMAs after it was issued, and every LDS counter wait is computed
 from the issue order.
 
-M0 is written by the copies and not listed as clobbered (the compiler reserves
-it): the statement is the last thing the kernel does.
+M0 is written by the copies (the LDS destination of buffer_load ... lds) and is
+listed among the clobbers with the fixed registers, so the compiler keeps no
+value of its own in it across the statement.  Labels end in %=, which the
+compiler replaces by a number unique to each instance of the statement, so a
+duplicated statement cannot redefine a label.
 
 Run:  python gen_prefill_asm.py   (rewrites prefill_asm.inc next to it)
 """
@@ -173,7 +176,7 @@ def dma_scale_group(prog, buf, tag, first=None):
     g = min(first K block of the next group, KB - 4) (or `first`), into group
     buffer `buf`.  Waves 4-7 branch around."""
     _label[0] += 1
-    skip = f"fp8pf_sa_{tag}_{_label[0]}"
+    skip = f"fp8pf_sa_{tag}_{_label[0]}_%="
     prog.emit("s_cmp_eq_u32 %[wsa], 0", f"s_cbranch_scc1 {skip}")
     if first is None:
         prog.emit(f"s_add_u32 {S_T}, {S_KB}, {KB_GROUP - 1}",
@@ -400,7 +403,7 @@ def gen_epilogue(block, tag, nw):
                           f"v_mul_f32_e32 v{acc(i, j, r)}, v{vt[0]}, v{acc(i, j, r)}"]
     # every wave's copies and fragment reads are done: the stages are free
     L += ["s_waitcnt vmcnt(0) lgkmcnt(0)", "s_barrier",
-          "s_cmp_eq_u32 %[colok], 0", f"s_cbranch_scc1 fp8pf_done_{tag}"]
+          "s_cmp_eq_u32 %[colok], 0", f"s_cbranch_scc1 fp8pf_done_{tag}_%="]
     vl, vt, vk, vw, vrd, vo = (FW0 + k for k in range(6))
     buf = FW0 + 8                      # 32 VGPRs of read-back data
     s_reg, s_ldo2, s_uni, s_step = S_KB, S_DK, S_DK4, S_T
@@ -454,7 +457,7 @@ def gen_epilogue(block, tag, nw):
             L.append(f"buffer_store_dwordx4 {vr(buf + 4 * q, 4)}, v{vo}, %[dOut], 0 offen")
             L.append("s_nop 0")
             L.append(f"v_add_u32 v{vo}, {s_step}, v{vo}")
-    L.append(f"fp8pf_done_{tag}:")
+    L.append(f"fp8pf_done_{tag}_%=:")
     return L
 
 
@@ -464,12 +467,12 @@ def gen(block, nw=8):
     _label[0] = 0
     first, second, max_out = gen_loop(block, nw)
     L = gen_prologue(block, nw)
-    L.append(f"fp8pf_loop_{tag}:")
+    L.append(f"fp8pf_loop_{tag}_%=:")
     L += first
-    L += [f"s_cmp_eq_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_tail_{tag}"]
+    L += [f"s_cmp_eq_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_tail_{tag}_%="]
     L += second
-    L += [f"s_cmp_lt_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_loop_{tag}"]
-    L.append(f"fp8pf_tail_{tag}:")
+    L += [f"s_cmp_lt_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_loop_{tag}_%="]
+    L.append(f"fp8pf_tail_{tag}_%=:")
     L += gen_epilogue(block, tag, nw)
     return L, max_out
 
@@ -491,7 +494,7 @@ def main(path=OUT):
         out.append("")
     vg = ", ".join(f'"v{k}"' for k in range(NUM_FIXED_VGPR))
     sg = ", ".join(f'"s{k}"' for k in range(*CLOBBER_SGPR))
-    out.append(f'#define FP8_PREFILL_ASM_CLOBBERS {vg}, {sg}, "scc", "memory"')
+    out.append(f'#define FP8_PREFILL_ASM_CLOBBERS {vg}, {sg}, "m0", "scc", "memory"')
     out.append(f"#define FP8_PREFILL_ASM_FIXED_VGPRS {NUM_FIXED_VGPR}")
     out.append(f"#define FP8_PREFILL_LDS_BYTES {LDS_BYTES}")
     out.append(f"#define FP8_PREFILL_LDS_SA {SA_GROUP[0]}")

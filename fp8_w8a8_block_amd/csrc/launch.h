@@ -13,6 +13,20 @@ namespace fp8k {
 // the first pass
 constexpr int kTensorPartials = 1024;
 
+// Work-items of the largest grid a call launches.  A dispatch packet holds
+// the grid size in work-items as a 32-bit value, so every launch must stay
+// below 2^32; the ABI rejects larger calls as shapes before anything is
+// enqueued.  (The per-tensor, static and KV-cache kernels stride over their
+// data with at most 8192 workgroups and never come near the limit.)
+constexpr uint64_t kMaxGridItems = (uint64_t)1 << 32;
+uint64_t quant_act_block_items(int64_t M, int64_t K);
+uint64_t quant_weight_block_items(int64_t N, int64_t K);
+uint64_t quant_rows_items(int64_t R);
+uint64_t encode_items(int64_t n);
+uint64_t gemm_items(int64_t M, int64_t N, int64_t K);
+uint64_t grouped_items(int64_t N);
+uint64_t linear_decode_items(int64_t N);
+
 hipError_t launch_quant_act_block(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                                   uint8_t* q, int64_t ld_q, float* s, int64_t ld_s,
                                   hipStream_t st);

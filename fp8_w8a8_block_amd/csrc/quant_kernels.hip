@@ -242,16 +242,40 @@ __global__ __launch_bounds__(256) void encode_f32_kernel(const float* __restrict
 
 }  // namespace
 
+// the flattened 1x128 kernel serves rows narrower than a workgroup's
+// 16 GPT groups when its grid fits a dispatch
+constexpr uint32_t kActGPT = 2;
+constexpr uint32_t kActGroupsPerWG = 16u * kActGPT;
+
+static bool act_flat(uint64_t groups, uint64_t total) {
+  return groups < kActGroupsPerWG &&
+         (total + kActGroupsPerWG - 1) / kActGroupsPerWG * 256u < kMaxGridItems;
+}
+
+uint64_t quant_act_block_items(int64_t M, int64_t K) {
+  const uint64_t groups = (uint64_t)(K / kGroup), total = (uint64_t)M * groups;
+  if (act_flat(groups, total)) return (total + kActGroupsPerWG - 1) / kActGroupsPerWG * 256u;
+  return (groups + kActGroupsPerWG - 1) / kActGroupsPerWG * (uint64_t)M * 256u;
+}
+
+uint64_t quant_weight_block_items(int64_t N, int64_t K) {
+  return (uint64_t)(N / kGroup) * (uint64_t)(K / kGroup) * 256u;
+}
+
+uint64_t quant_rows_items(int64_t R) { return ((uint64_t)R + 3) / 4 * 256u; }
+
+uint64_t encode_items(int64_t n) { return ((uint64_t)n + 255) / 256 * 256u; }
+
 hipError_t launch_quant_act_block(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                                   uint8_t* q, int64_t ld_q, float* s, int64_t ld_s,
                                   hipStream_t st) {
-  constexpr int GPT = 2;
+  constexpr int GPT = kActGPT;
   const uint32_t groups = (uint32_t)(K / kGroup);
   const uint64_t total = (uint64_t)M * groups;
   // rows narrower than a workgroup's 16 GPT groups: number the groups across
   // rows so no lane idles (measured at K = 512, M = 4096: 4.8 -> 3.5 us);
   // wider rows keep one run of workgroups per row, which measured faster
-  if (groups < 16u * GPT && total < ((uint64_t)1 << 32) - 64u) {
+  if (act_flat(groups, total)) {
     const uint64_t grid = (total + 16u * GPT - 1) / (16u * GPT);
     hipLaunchKernelGGL(quant_act_flat_kernel<GPT>, dim3((uint32_t)grid), dim3(256), 0, st, x,
                        ld_x, q, ld_q, s, ld_s, groups, (uint32_t)total);

@@ -324,9 +324,36 @@ def test_leading_dimensions_are_bounded():
     assert vg(ld_as=huge) == STRIDE
     assert vg(ld_ws=huge) == STRIDE
     assert vg(ld_as=huge, mode=1) == OK                    # per-tensor scales have no ld
-    assert vg(mode=2, ld_as=(1 << 31) - 1, ld_ws=1, M=(1 << 30)) == STRIDE
+    assert vg(mode=2, ld_as=(1 << 31) - 1, ld_ws=1, M=(1 << 26)) == STRIDE
     assert vgg(ld_a=huge) == STRIDE
     assert vgg(ld_w=huge) == STRIDE
     assert vgg(ld_ws=huge) == STRIDE
     assert vkw(ld_k=huge) == STRIDE
     assert vkr(ld_out=huge) == STRIDE
+
+
+def test_grids_beyond_32_bit_work_items_are_shapes():
+    # every launch must stay below 2^32 work-items (the dispatch packet's
+    # grid size is 32-bit): such calls are refused as shapes up front.
+    # Fake tensors 2^44 bytes apart, so these sizes do not overlap.
+    far = dict(x=1 << 44, q=2 << 44, s=3 << 44)
+    assert vq(M=(1 << 24) - 1, K=4096, **far) == OK          # 256 threads per row: just fits
+    assert vq(M=1 << 24, K=4096, **far) == SHAPE
+    assert vq(M=1 << 25, K=512, **far) == OK                  # groups numbered across rows
+    assert vq(M=1 << 30, K=512, **far) == SHAPE
+    assert vq(M=(1 << 26) - 4, K=128, ld_s=1, mode=2, **far) == OK   # per row: 4 rows a group
+    assert vq(M=1 << 26, K=128, ld_s=1, mode=2, **far) == SHAPE
+    farw = dict(w=1 << 44, q=2 << 44, s=3 << 44)
+    assert vw(N=1 << 20, K=1 << 17, **farw) == OK             # a workgroup per 128 x 128 block
+    assert vw(N=1 << 20, K=1 << 18, **farw) == SHAPE
+    farg = dict(a=1 << 44, w=2 << 44, out=3 << 44, sa=4 << 44, sw=5 << 44)
+    assert vg(M=16, N=(1 << 27) - 128, K=128, **farg) == OK   # decode tile: 16 columns a group
+    assert vg(M=16, N=1 << 27, K=128, **farg) == SHAPE
+    assert vg(M=1 << 19, N=1 << 18, K=128, **farg) == OK      # tile grid of the large-M kernels
+    assert vg(M=1 << 19, N=1 << 19, K=128, **farg) == SHAPE
+    assert vgg(N=1 << 27, K=128) == SHAPE
+    lib = _lib.lib()
+    # fp8_e4m3_encode_f32 and fp8_linear validate before they touch a device
+    assert lib.fp8_e4m3_encode_f32(X, 1 << 32, Q, None) == SHAPE
+    assert lib.fp8_linear(X, 128, Q, 128, S, 1, O, 1 << 27, 1, 1 << 27, 128, 0, None, 0,
+                          None) == SHAPE
