@@ -6,6 +6,6 @@ ABI declared in include/fp8w8a8.h); this package is its Python binding.
 
 from ._lib import (  # noqa: F401
     LIB_PATH, SCALE_BLOCK, SCALE_ROW, SCALE_TENSOR, block_gemm, encode_f32, grouped_gemm,
-    kv_cache_read, kv_cache_write, lib, linear, quant_act, quant_act_static, quant_weight_block,
+    kv_cache_read, kv_cache_write, lib, linear, linear_noalloc, quant_act, quant_act_static, quant_weight_block,
     status_str, workspace_bytes,
 )

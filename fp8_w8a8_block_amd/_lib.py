@@ -49,6 +49,8 @@ _SIGS = {
     "fp8_e4m3_encode_f32": (_int, [_vp, _i64, _vp, _vp]),
     "fp8_linear": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp,
                           _sz, _vp]),
+    "fp8_linear_noalloc": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64,
+                                  _int, _vp]),
     "fp8_quant_act_static": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "fp8_validate_quant_act_static": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp]),
     "fp8_grouped_gemm": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
@@ -294,6 +296,33 @@ def linear(x, w_q, w_s, scale_mode="block", out=None, workspace=None):
         ws_ptr, ws_len = _workspace(workspace, x.device)
         _check(lib().fp8_linear(x.data_ptr(), ld_x, w_q.data_ptr(), ld_w, w_s.data_ptr(), ld_ws,
                                 out.data_ptr(), ld_out, M, N, K, mode, ws_ptr, ws_len, _stream(x)))
+    return out
+
+
+def linear_noalloc(x, w_q, w_s, out, scale_mode="block"):
+    """fp8_linear_noalloc: the linear call with the library's own per-device
+    scratch instead of a workspace (for callers that cannot allocate; the
+    caller passes the output).  Bit-identical to linear()."""
+    mode = _mode(scale_mode)
+    M, K, ld_x = _rows(x, torch.bfloat16, "x")
+    N, K2, ld_w = _rows(w_q, torch.uint8, "w_q")
+    if K2 != K:
+        raise ValueError(f"K mismatch: x has {K}, w_q has {K2}")
+    _device_tensor(w_q, "w_q", torch.uint8, x.device)
+    _device_tensor(w_s, "w_s", torch.float32, x.device)
+    if mode == SCALE_ROW:
+        ld_ws = _vec_ld(w_s, N, "w_s")
+    elif mode == SCALE_BLOCK:
+        ld_ws = _scale_matrix(w_s, "w_s", N // 128, K // 128, x.device)
+    else:
+        if w_s.numel() != 1:
+            raise ValueError("a per-tensor weight scale is one value")
+        ld_ws = 1
+    _device_tensor(out, "out", torch.bfloat16, x.device, (M, N))
+    ld_out = _rows(out, torch.bfloat16, "out")[2]
+    with torch.cuda.device(x.device):
+        _check(lib().fp8_linear_noalloc(x.data_ptr(), ld_x, w_q.data_ptr(), ld_w, w_s.data_ptr(),
+                                        ld_ws, out.data_ptr(), ld_out, M, N, K, mode, _stream(x)))
     return out
 
 

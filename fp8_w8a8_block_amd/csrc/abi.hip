@@ -197,6 +197,9 @@ const char* fp8_status_str(fp8_status s) {
     case FP8_ERR_DEVICE: return "no gfx950 device is current";
     case FP8_ERR_LAUNCH: return "kernel launch failed";
     case FP8_ERR_ALIAS: return "an output overlaps another tensor";
+    case FP8_ERR_SCRATCH:
+      return "the call needs more scratch than the allocation-free entry point holds "
+             "(FP8_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -370,6 +373,26 @@ fp8_status run_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
                                     K, scale_mode != FP8_SCALE_BLOCK, s));
 }
 
+// Scratch of fp8_linear_noalloc: a file-scope device array, one copy per
+// device, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is looked up
+// once per device with hipGetSymbolAddress (no allocation) and only that
+// address is handed to kernels.
+__device__ __align__(256) uint8_t scratch[FP8_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+fp8_status device_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8_ERR_DEVICE;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP8_ERR_DEVICE;
+    g_scratch[dev].store(p, std::memory_order_release);   // racing threads store the same address
+  }
+  *ptr = p;
+  return FP8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -392,6 +415,22 @@ fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
   if ((st = check_device()) != FP8_OK) return st;
   return run_linear(x, ld_x, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N, K, scale_mode, fused, lay,
                     workspace, (hipStream_t)stream);
+}
+
+fp8_status fp8_linear_noalloc(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
+                              const float* w_s, int64_t ld_ws, uint16_t* out, int64_t ld_out,
+                              int64_t M, int64_t N, int64_t K, int scale_mode, void* stream) {
+  bool fused = false;
+  LinearLayout lay{};
+  fp8_status st = validate_linear(x, ld_x, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N, K,
+                                  scale_mode, fused, lay);
+  if (st != FP8_OK || M == 0) return st;
+  if (!fused && lay.total > (size_t)FP8_NOALLOC_SCRATCH_BYTES) return FP8_ERR_SCRATCH;
+  if ((st = check_device()) != FP8_OK) return st;
+  void* ws = nullptr;
+  if (!fused && (st = device_scratch(&ws)) != FP8_OK) return st;
+  return run_linear(x, ld_x, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N, K, scale_mode, fused, lay,
+                    ws, (hipStream_t)stream);
 }
 
 fp8_status fp8_validate_quant_act_static(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,

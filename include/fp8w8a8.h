@@ -28,8 +28,9 @@
  *     scale pointers 4-byte aligned; ld of bf16 tensors a multiple of 8,
  *     of FP8 tensors a multiple of 16 (FP8_ERR_ALIGN).
  *   - Calls are thread-safe; the only global state is a per-device cache of
- *     the architecture check.  Calls on one stream are ordered; calls on
- *     different streams that write the same buffers race (caller's duty).
+ *     the architecture check (and fp8_linear_noalloc's scratch, see there).
+ *     Calls on one stream are ordered; calls on different streams that
+ *     write the same buffers race (caller's duty).
  *   - The dynamic quantizers (scales derived from the data) assume finite
  *     bf16 inputs: a NaN or infinity in a group makes its scale non-finite.
  *     The static-scale calls (fp8_quant_act_static, fp8_kv_cache_write)
@@ -62,7 +63,8 @@ typedef enum {
   FP8_ERR_WORKSPACE = 7,  /* workspace missing or smaller than fp8_workspace_bytes() */
   FP8_ERR_DEVICE = 8,     /* current device is not gfx950, or no device */
   FP8_ERR_LAUNCH = 9,     /* the kernel launch failed */
-  FP8_ERR_ALIAS = 10      /* an output overlaps an input or another output */
+  FP8_ERR_ALIAS = 10,     /* an output overlaps an input or another output */
+  FP8_ERR_SCRATCH = 11    /* fp8_linear_noalloc: the call needs more than its scratch */
 } fp8_status;
 
 /* Scale modes.
@@ -177,6 +179,27 @@ fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
                       const float* w_s, int64_t ld_ws, uint16_t* out, int64_t ld_out,
                       int64_t M, int64_t N, int64_t K, int scale_mode, void* workspace,
                       size_t ws_bytes, void* stream);
+
+/* fp8_linear_noalloc -- fp8_linear for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, arithmetic and result as fp8_linear,
+ * bit for bit, without the workspace: the unfused path (anything but
+ * FP8_SCALE_BLOCK with 1 <= M <= 4) keeps its activation codes, scales and
+ * per-tensor partials in a scratch buffer of FP8_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every device it runs on, from the first call on that
+ * device until the process ends (a static device array; its address is
+ * looked up once per device, nothing is allocated).  A call whose workspace
+ * (fp8_workspace_bytes(FP8_OP_LINEAR, M, N, K, scale_mode)) exceeds it
+ * returns FP8_ERR_SCRATCH before anything is enqueued.
+ *   Every call on one device shares that device's buffer, which keeps the
+ *   last call's contents: calls that can overlap on one device (different
+ *   streams, or threads without ordering) race and are the caller's to
+ *   order.  No byte of it needs to start at any value (each call writes
+ *   everything it reads). */
+#define FP8_NOALLOC_SCRATCH_BYTES (32u << 20)
+fp8_status fp8_linear_noalloc(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
+                              const float* w_s, int64_t ld_ws, uint16_t* out, int64_t ld_out,
+                              int64_t M, int64_t N, int64_t K, int scale_mode, void* stream);
 
 /* fp8_quant_act_static -- static activation quantization with a scale
  * calibrated beforehand ("[vLLM] FP8", scaling strategies: static

@@ -32,13 +32,13 @@ def header_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings():
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = _lib.status_str(code)
         assert s and s != "unknown status"
     assert _lib.status_str(99) == "unknown status"
