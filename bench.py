@@ -335,10 +335,10 @@ def hbm_reference(nbytes=1 << 30, n=10):
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     src.fill_(1)
     dst = torch.empty_like(src)
-    acc = torch.empty((), dtype=torch.int64, device="cuda")
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     c_ms = time_launches(lambda i: dst.copy_(src), n)
-    r_ms = time_launches(lambda i: torch.sum(src.view(torch.int32), dim=0, out=acc), n)
+    r_ms = time_launches(lambda i: torch.sum(src.view(torch.float32), dim=0, out=acc), n)
     del src, dst
     torch.cuda.empty_cache()
     return {"copy": {"bytes_moved": 2 * nbytes, "avg_launch_us": c_ms * 1e3,

@@ -692,9 +692,12 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
 //    step's fragments are read as soon as its copy is visible, and the
 //    barrier that releases a stage sits before the last fragment group's
 //    MFMAs rather than after them (the matrix unit does not drain on it);
-//  * the copies of K block kb + 2 (and its activation scales) go out one per
-//    slot after that barrier; the block index is clamped to the last block,
-//    so no copy ever addresses past the operands' K extent.
+//  * the copies of K block kb + S (and its activation scales) go out one per
+//    slot after that barrier, S the number of LDS stages (2 for 256 x 256
+//    tiles, 3 for 256 x 128 tiles, whose one wave per SIMD has no other wave
+//    to cover a wait: its copies get two K steps to land); each barrier waits
+//    only for the copies of the next block.  The block index is clamped to
+//    the last block, so no copy ever addresses past the operands' K extent.
 //
 // Activation scales travel by DMA too, four K blocks at a time: every fourth
 // step waves 0-3 copy sa[m0 + row, g .. g + 3] (16 bytes per row, one row per
@@ -716,20 +719,39 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
 // past N skips its stores.
 #include "prefill_asm.inc"
 
-// LDS byte offsets (mirrors the constants of gen_prefill_asm.py)
-constexpr int kPfLdsBytes = FP8_PREFILL_LDS_BYTES;
-constexpr int kPfLdsW = FP8_PREFILL_LDS_W;
-constexpr int kPfLdsSa = FP8_PREFILL_LDS_SA;
-constexpr int kPfSaGroup = FP8_PREFILL_LDS_SA_GROUP_BYTES;
-constexpr int kPfLdsSw = FP8_PREFILL_LDS_SW;
+// LDS layout of each workgroup shape (the offsets of gen_prefill_asm.py):
+// `stages` activation stages (256 rows x 128 B), `stages` weight stages
+// (32 NW rows x 128 B), two activation-scale group buffers, the weight-scale
+// table.  The 256 x 256 shape has two stages, the 256 x 128 shape three.
 constexpr int kPfKbGroup = FP8_PREFILL_KB_GROUP;   // K blocks per activation-scale copy
 constexpr int kPrefillMaxKB = 256;            // weight-scale table rows: K <= 32768
-static_assert(kPfLdsW == 2 * kPM * 128, "two activation stages precede the weight stages");
-static_assert(kPfLdsSa == kPfLdsW + 2 * kPN * 128, "scale groups follow the operand stages");
-static_assert(kPfSaGroup == kPM * kPfKbGroup * 4, "a scale group holds 4 K blocks of 256 rows");
-static_assert(kPfLdsSw == kPfLdsSa + 2 * kPfSaGroup, "weight-scale table follows the groups");
-static_assert(kPfLdsBytes == kPfLdsSw + 2 * kPrefillMaxKB * 4, "table ends the layout");
-static_assert(kPfLdsBytes <= 160 * 1024, "LDS of one CU");
+
+template <int NW>
+struct PfLayout;
+template <>
+struct PfLayout<8> {
+  static constexpr int stages = FP8_PREFILL_W8_STAGES, bytes = FP8_PREFILL_W8_LDS_BYTES,
+                       w = FP8_PREFILL_W8_LDS_W, sa = FP8_PREFILL_W8_LDS_SA,
+                       sa_group = FP8_PREFILL_W8_LDS_SA_GROUP_BYTES, sw = FP8_PREFILL_W8_LDS_SW;
+};
+template <>
+struct PfLayout<4> {
+  static constexpr int stages = FP8_PREFILL_W4_STAGES, bytes = FP8_PREFILL_W4_LDS_BYTES,
+                       w = FP8_PREFILL_W4_LDS_W, sa = FP8_PREFILL_W4_LDS_SA,
+                       sa_group = FP8_PREFILL_W4_LDS_SA_GROUP_BYTES, sw = FP8_PREFILL_W4_LDS_SW;
+};
+
+template <int NW>
+constexpr bool pf_layout_ok() {
+  using L = PfLayout<NW>;
+  return L::w == L::stages * kPM * 128 &&                  // activation stages first
+         L::sa == L::w + L::stages * 32 * NW * 128 &&       // then the weight stages
+         L::sa_group == kPM * kPfKbGroup * 4 &&             // a group: 4 K blocks of 256 rows
+         L::sw == L::sa + 2 * L::sa_group &&                // two groups, then the table
+         L::bytes == L::sw + 2 * kPrefillMaxKB * 4 &&       // which ends the layout
+         L::bytes <= 160 * 1024;                            // LDS of one CU
+}
+static_assert(pf_layout_ok<8>() && pf_layout_ok<4>(), "LDS layout of the generated loop");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -830,7 +852,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
     int tiles_n, const int64_t* __restrict__ offsets, int E, int64_t w_es, int64_t sw_es) {
   constexpr int kTN = 32 * NW;                 // tile width (weight rows)
   constexpr int kWN = NW / 2;                  // waves along N
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kPfLdsBytes];
+  using Lay = PfLayout<NW>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Lay::bytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -889,7 +912,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   // (2 kg) ^ swz_pair(r16) and the next one
   const int p0 = (2 * kg) ^ swz_pair(r16);
   const uint32_t rdA = lds0 + (uint32_t)(wm * kPWM * 128 + r16 * 128 + p0 * 16);
-  const uint32_t rdW = lds0 + (uint32_t)(kPfLdsW + wn * kPWN * 128 + r16 * 128 + p0 * 16);
+  const uint32_t rdW = lds0 + (uint32_t)(Lay::w + wn * kPWN * 128 + r16 * 128 + p0 * 16);
 
   // activation scales, copied by waves 0..3 every four K blocks: lane
   // r = 64 wave + lane copies the 16 bytes sa[m0 + r, g .. g + 3] to 16 r of a
@@ -899,11 +922,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   const uint32_t offSa = (uint32_t)((64 * (wave & 3) + lane) * ld_sa * 4);
   const v4i dSa = pf_desc(sa + m0 * ld_sa, ((int64_t)M - m0) * ld_sa * 4);
   const int wsa = pf_uni(wave < 4 ? 1 : 0);
-  const uint32_t sam0 = pf_uni(lds0 + (uint32_t)(kPfLdsSa + (wave & 3) * 1024));
-  const uint32_t scL0 = lds0 + (uint32_t)(kPfLdsSa + (wm * kPWM + r16) * 16);
+  const uint32_t sam0 = pf_uni(lds0 + (uint32_t)(Lay::sa + (wave & 3) * 1024));
+  const uint32_t scL0 = lds0 + (uint32_t)(Lay::sa + (wm * kPWM + r16) * 16);
   const uint32_t scH0 = scL0 + 4u * 16u * 16u;
-  const uint32_t scL1 = scL0 + (uint32_t)kPfSaGroup;
-  const uint32_t scH1 = scH0 + (uint32_t)kPfSaGroup;
+  const uint32_t scL1 = scL0 + (uint32_t)Lay::sa_group;
+  const uint32_t scH1 = scH0 + (uint32_t)Lay::sa_group;
 
   // weight-scale table [2][kPrefillMaxKB]: wave w copies row w / 4, blocks
   // 64 (w % 4) + lane; the descriptor ends at the last weight block's last
@@ -911,8 +934,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   const int nb0 = (int)(n0 >> 7);
   const uint32_t offSw = (uint32_t)(((wave >> 2) * ld_sw + 64 * (wave & 3) + lane) * 4);
   const v4i dSw = pf_desc(sw + (int64_t)nb0 * ld_sw, (((int64_t)(N / 128) - nb0 - 1) * ld_sw + KB) * 4);
-  const uint32_t swm0 = pf_uni(lds0 + (uint32_t)(kPfLdsSw + wave * 256));
-  uint32_t swrd = lds0 + (uint32_t)(kPfLdsSw + ((wn * kPWN) >> 7) * kPrefillMaxKB * 4);
+  const uint32_t swm0 = pf_uni(lds0 + (uint32_t)(Lay::sw + wave * 256));
+  uint32_t swrd = lds0 + (uint32_t)(Lay::sw + ((wn * kPWN) >> 7) * kPrefillMaxKB * 4);
 
   // output: bf16 rows from m0, columns from n0; the epilogue derives its
   // lane offsets from the lane id

@@ -31,14 +31,29 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 OUT = os.path.join(HERE, "prefill_asm.inc")
 
 # ---------------------------------------------------------------------------
-# LDS layout (bytes from the kernel's LDS base).  Kept in step with the
-# constants in gemm_kernels.hip (kPfLds*), which static_asserts them.
-A_STAGE = (0, 32768)              # 256 activation rows x 128 B per stage
-W_STAGE = (65536, 98304)          # 256 weight rows x 128 B per stage
-SA_GROUP = (131072, 135168)       # activation scales of 4 K blocks x 256 rows (permuted), x2
-SW_TABLE = 139264                 # weight scales [2][256] of the tile's two weight blocks
-LDS_BYTES = 141312
+# LDS layout (bytes from the kernel's LDS base), one per workgroup shape.
+# gemm_kernels.hip takes its copy of these offsets from the #defines written
+# below and static_asserts the ones it derives itself.
 KB_GROUP = 4                      # K blocks per activation-scale copy
+
+
+class Layout:
+    """Operand stages (activation 256 rows x 128 B, weight 32 NW rows x 128
+    B, `stages` of each), then the two activation-scale group buffers
+    (4 K blocks x 256 rows each), then the weight-scale table [2][256]."""
+
+    def __init__(self, nw, stages):
+        self.nw, self.stages = nw, stages
+        a_bytes, w_bytes = 256 * 128, 32 * nw * 128
+        self.A = tuple(i * a_bytes for i in range(stages))
+        w0 = stages * a_bytes
+        self.W = tuple(w0 + i * w_bytes for i in range(stages))
+        sa0 = w0 + stages * w_bytes
+        self.SA = (sa0, sa0 + 256 * KB_GROUP * 4)
+        self.SW = self.SA[1] + 256 * KB_GROUP * 4
+        self.bytes = self.SW + 2 * 256 * 4
+        assert self.bytes <= 160 * 1024
+
 
 # ---------------------------------------------------------------------------
 # Register map (fixed physical VGPRs; the operands handed in from C++ are
@@ -51,7 +66,9 @@ SC0 = 232                         # eight activation scales (times the weight sc
 SPREV = 240                       # scale of fragment 7 of the previous K step
 SWN = 241                         # weight scale of the next K step
 VCOPY = (242, 243)                # per-copy source offsets (alternating)
-NUM_FIXED_VGPR = 244
+RDA_HI = 244                      # fragment-read base 64 KiB above rdA (a third stage)
+NUM_FIXED_VGPR = 245
+DS_OFFSET_MAX = 65535             # ds_read immediate offsets are 16-bit
 # scalar scratch
 S_KB, S_DK, S_DK4, S_T, S_R = "s84", "s85", "s86", "s87", "s88"
 CLOBBER_SGPR = (84, 89)
@@ -59,8 +76,11 @@ CLOBBER_SGPR = (84, 89)
 # Workgroup shapes: NW waves in a 2 x (NW / 2) grid of 128 x 64 wave tiles,
 # so the workgroup tile is 256 x (32 NW).  Copy t of wave w carries tile rows
 # 8 (w + NW t) .. + 7; the activation tile takes 32 / NW copies per wave, the
-# weight tile 4.
+# weight tile 4.  The 256 x 256 shape (two waves per SIMD) fills the LDS with
+# two stages; the 256 x 128 shape (one wave per SIMD, nothing to cover a wave
+# that waits) has room for three, so its copies run two K steps ahead.
 SHAPES = (8, 4)
+STAGES = {8: 2, 4: 3}
 
 
 def copies(nw):
@@ -117,6 +137,7 @@ class Program:
         self.done_upto = 0              # LDS ops known complete (waited for)
         self.where = {}                 # key -> index (1-based) of its last LDS op
         self.max_out = 0
+        self.vm_ops = []                # vector-memory ops issued: (key, every wave issues it)
 
     def emit(self, *ls):
         self.lines.extend(ls)
@@ -139,6 +160,22 @@ class Program:
         self.emit(f"s_waitcnt lgkmcnt({n})")
         self.done_upto = last
 
+    def vm(self, key, *ls, every_wave=True):
+        """A vector-memory op (a copy into LDS) tagged with key; every_wave
+        False for ops some waves branch around."""
+        self.emit(*ls)
+        self.vm_ops.append((key, every_wave))
+
+    def vm_wait_for(self, key):
+        """Wait until the ops tagged key have completed.  Copies complete in
+        issue order, so the ops every wave issued after key's last one may
+        stay out (ops only some waves issue are not counted: a wave that
+        issued them waits for more than it needs)."""
+        last = max((i for i, (k, _) in enumerate(self.vm_ops) if k == key), default=None)
+        n = 0 if last is None else sum(1 for _, e in self.vm_ops[last + 1:] if e)
+        assert 0 <= n <= 63
+        self.emit(f"s_waitcnt vmcnt({n})")
+
     def wait_all_lds(self):
         if self.done_upto < self.issued:
             self.emit("s_waitcnt lgkmcnt(0)")
@@ -147,31 +184,37 @@ class Program:
 
 # ---------------------------------------------------------------------------
 def frag_read(prog, key, dst, base, off):
-    prog.lds(key, f"ds_read_b128 {vr(dst, 4)}, %[{base}] offset:{off}",
-             f"ds_read_b128 {vr(dst + 4, 4)}, %[{base}] offset:{off + 16}")
+    """The two 16-byte reads of a fragment at base operand + off; activation
+    offsets past the 16-bit field go through RDA_HI (rdA + 64 KiB)."""
+    reg = f"%[{base}]"
+    if base == "rdA" and off + 16 > DS_OFFSET_MAX:
+        reg, off = f"v{RDA_HI}", off - 65536
+    assert 0 <= off and off + 16 <= DS_OFFSET_MAX
+    prog.lds(key, f"ds_read_b128 {vr(dst, 4)}, {reg} offset:{off}",
+             f"ds_read_b128 {vr(dst + 4, 4)}, {reg} offset:{off + 16}")
 
 
-def dma_copy(prog, op, t, stage, nw, k):
+def dma_copy(prog, lay, op, t, stage, k, blk):
     """Copy t (tile rows 8 (wave + nw t) .. + 7) of operand op, K block S_DK,
-    into stage.  The row offset t * nw * 8 * ld is added to the lane's offset
-    in a VGPR (the descriptor's range check sees it: rows past M or N read
-    zero); the K offset is the scalar offset."""
-    base = (A_STAGE if op == "A" else W_STAGE)[stage] + t * nw * 1024
+    into stage; the copy is tagged as part of K block blk.  The row offset
+    t * nw * 8 * ld is added to the lane's offset in a VGPR (the descriptor's
+    range check sees it: rows past M or N read zero); the K offset is the
+    scalar offset."""
+    base = (lay.A if op == "A" else lay.W)[stage] + t * lay.nw * 1024
     v = VCOPY[k % 2]
     if t == 0:
         prog.emit(f"v_mov_b32 v{v}, %[off{op}]")
     else:
         prog.emit(f"s_mul_i32 {S_R}, %[rs{op}], {t}",
                   f"v_add_u32 v{v}, {S_R}, %[off{op}]")
-    prog.emit(f"s_add_u32 m0, %[wave1k], {base}",
-              "s_nop 0",
-              f"buffer_load_dwordx4 v{v}, %[d{op}], {S_DK} offen lds")
+    prog.emit(f"s_add_u32 m0, %[wave1k], {base}", "s_nop 0")
+    prog.vm(("blk", blk), f"buffer_load_dwordx4 v{v}, %[d{op}], {S_DK} offen lds")
 
 
 _label = [0]
 
 
-def dma_scale_group(prog, buf, tag, first=None):
+def dma_scale_group(prog, lay, buf, tag, first=None):
     """Waves 0-3: each lane copies the 16 bytes sa[row, g .. g + 3] of its row,
     g = min(first K block of the next group, KB - 4) (or `first`), into group
     buffer `buf`.  Waves 4-7 branch around."""
@@ -185,10 +228,10 @@ def dma_scale_group(prog, buf, tag, first=None):
                   f"s_lshl_b32 {S_T}, {S_T}, 2")
     else:
         prog.emit(f"s_mov_b32 {S_T}, {4 * first}")
-    prog.emit(f"s_add_u32 m0, %[sam0], {SA_GROUP[buf] - SA_GROUP[0]}",
-              "s_nop 0",
-              f"buffer_load_dwordx4 %[offSa], %[dSa], {S_T} offen lds",
-              f"{skip}:")
+    prog.emit(f"s_add_u32 m0, %[sam0], {lay.SA[buf] - lay.SA[0]}", "s_nop 0")
+    prog.vm(("sa", buf), f"buffer_load_dwordx4 %[offSa], %[dSa], {S_T} offen lds",
+            every_wave=lay.nw == 4)
+    prog.emit(f"{skip}:")
 
 
 def scale_reads(prog, key, kb_next, half):
@@ -217,44 +260,54 @@ def set_dk(prog, ahead):
               f"s_lshl_b32 {S_DK}, {S_DK}, 7")
 
 
-def gen_loop(block, nw):
-    """Steady-state K steps.  Returns the text of 2 x KB_GROUP consecutive
-    steps as two halves (K blocks 0 .. 7 mod 8: LDS stages alternate every
-    step, activation-scale group buffers every four), taken from the middle
-    of a longer run so that the counter waits see the operations the
-    previous steps left in flight."""
+def loop_period(stages):
+    """Steps after which the loop's code repeats: LDS stages cycle every
+    `stages` steps, weight-fragment register sets every 2, activation-scale
+    group buffers every 2 KB_GROUP."""
+    from math import lcm
+    return lcm(stages, 2, 2 * KB_GROUP)
+
+
+def gen_loop(block, lay):
+    """Steady-state K steps.  Returns the text of one period of consecutive
+    steps (loop_period) as chunks of KB_GROUP steps, taken from the middle of
+    a longer run so that the counter waits see the operations the previous
+    steps left in flight."""
+    nw, S = lay.nw, lay.stages
     prog = Program()
     sched = {}
 
     def at(gslot, fn):
         sched.setdefault(gslot, []).append(fn)
 
-    nsteps = 6 * KB_GROUP
+    P = loop_period(S)
+    nsteps = 3 * P
     bar_slot = 26
     for st in range(nsteps):
-        p = st % 2                   # LDS stage of this step = weight-fragment set
+        p = st % S                   # LDS stage of this step
+        q = (st + 1) % S             # LDS stage of the next step
+        rq = (st + 1) % 2            # weight-fragment register set of the next step
         base = 32 * st
         # activation fragment j (1..7) of this step: after the last MFMA of
         # fragment j - 2 (same buffer), five slots before its first use
         for j in range(1, 8):
             at(base + 4 * j - 5, lambda st=st, j=j, p=p: frag_read(
-                prog, ("fa", st, j), fa(j % 2), "rdA", A_STAGE[p] - A_STAGE[0] + j * 2048))
+                prog, ("fa", st, j), fa(j % 2), "rdA", lay.A[p] - lay.A[0] + j * 2048))
 
         def barrier(st=st):
+            # this wave's reads of stage p are done and its copies of K block
+            # st + 1 have landed; after the barrier every wave's have
             prog.wait_all_lds()
-            prog.emit("s_waitcnt vmcnt(0)", "s_barrier")
-            set_dk(prog, 2)
+            prog.vm_wait_for(("blk", st + 1))
+            prog.emit("s_barrier")
+            set_dk(prog, S)
         at(base + bar_slot, barrier)
-        q = 1 - p
-        at(base + 27, lambda st=st, q=q: (
-            frag_read(prog, ("fa", st + 1, 0), fa(0), "rdA", A_STAGE[q] - A_STAGE[0]),
-            frag_read(prog, ("fw", st + 1, 0), fw(q, 0), "rdW", W_STAGE[q] - W_STAGE[0])))
-        at(base + 28, lambda st=st, q=q: frag_read(
-            prog, ("fw", st + 1, 1), fw(q, 1), "rdW", W_STAGE[q] - W_STAGE[0] + 2048))
-        at(base + 29, lambda st=st, q=q: frag_read(
-            prog, ("fw", st + 1, 2), fw(q, 2), "rdW", W_STAGE[q] - W_STAGE[0] + 4096))
-        at(base + 30, lambda st=st, q=q: frag_read(
-            prog, ("fw", st + 1, 3), fw(q, 3), "rdW", W_STAGE[q] - W_STAGE[0] + 6144))
+        at(base + 27, lambda st=st, q=q, rq=rq: (
+            frag_read(prog, ("fa", st + 1, 0), fa(0), "rdA", lay.A[q] - lay.A[0]),
+            frag_read(prog, ("fw", st + 1, 0), fw(rq, 0), "rdW", lay.W[q] - lay.W[0])))
+        for i in (1, 2, 3):
+            at(base + 27 + i, lambda st=st, q=q, rq=rq, i=i: frag_read(
+                prog, ("fw", st + 1, i), fw(rq, i), "rdW", lay.W[q] - lay.W[0] + 2048 * i))
         if block:
             def scales_lo(st=st):
                 prog.emit(f"v_mov_b32 v{SPREV}, v{SC0 + 7}")
@@ -278,11 +331,12 @@ def gen_loop(block, nw):
             at(base + 12, mul_hi)
             if st % KB_GROUP == 1:
                 nbuf = (st // KB_GROUP + 1) % 2
-                at(base + 30, lambda nbuf=nbuf: dma_scale_group(prog, nbuf, f"blk{nw}"))
-        # copies of K block kb + 2 into this step's stage (released at the
+                at(base + 30, lambda nbuf=nbuf: dma_scale_group(prog, lay, nbuf, f"blk{nw}"))
+        # copies of K block kb + S into this step's stage (released at the
         # barrier), one per slot from slot 28 on
         for k, (op, t) in enumerate(copies(nw)):
-            at(base + 28 + k, lambda op=op, t=t, p=p, k=k: dma_copy(prog, op, t, p, nw, k))
+            at(base + 28 + k, lambda st=st, op=op, t=t, p=p, k=k: dma_copy(
+                prog, lay, op, t, p, k, st + S))
 
     total = 32 * nsteps
     marks = {}
@@ -309,17 +363,19 @@ def gen_loop(block, nw):
         if qq == 31:
             prog.emit(f"s_add_u32 {S_KB}, {S_KB}, 1")
     marks[nsteps] = len(prog.lines)
-    first = prog.lines[marks[2 * KB_GROUP]:marks[3 * KB_GROUP]]
-    second = prog.lines[marks[3 * KB_GROUP]:marks[4 * KB_GROUP]]
-    return first, second, prog.max_out
+    chunks = [prog.lines[marks[P + c]:marks[P + c + KB_GROUP]] for c in range(0, P, KB_GROUP)]
+    return chunks, prog.max_out
 
 
-def gen_prologue(block, nw):
+def gen_prologue(block, lay):
+    nw, S = lay.nw, lay.stages
     # some scalar operands were just written by v_readfirstlane; VMEM reads of
     # an SGPR written by the VALU need wait states
     L = ["s_nop 7"]
     for k in range(128):
         L.append(f"v_mov_b32 v{ACC0 + k}, 0")
+    if lay.A[-1] - lay.A[0] + 8 * 2048 > DS_OFFSET_MAX:
+        L.append(f"v_add_u32 v{RDA_HI}, 0x10000, %[rdA]")
     if block:
         for k in range(24):
             L.append(f"v_mov_b32 v{P0 + k}, 0")
@@ -330,14 +386,15 @@ def gen_prologue(block, nw):
     prog = Program()
     prog.emit(*L)
     if block:
-        dma_scale_group(prog, 0, f"pro{nw}", first=0)
-    # K blocks 0 and 1 into stages 0 and 1
-    for stage, ahead in ((0, 0), (1, 1)):
-        set_dk(prog, ahead)
+        dma_scale_group(prog, lay, 0, f"pro{nw}", first=0)
+    # K blocks 0 .. S - 1 into stages 0 .. S - 1
+    for stage in range(S):
+        set_dk(prog, stage)
         for k, (op, t) in enumerate(copies(nw)):
-            dma_copy(prog, op, t, stage, nw, k)
-    prog.emit(f"s_waitcnt vmcnt({len(copies(nw))})", "s_barrier")
-    # leave S_DK on block 1: the first step re-issues the tail of that copy
+            dma_copy(prog, lay, op, t, stage, k, stage)
+    prog.vm_wait_for(("blk", 0))
+    prog.emit("s_barrier")
+    # leave S_DK on block S - 1: the first step re-issues the tail of that copy
     for i in range(4):
         frag_read(prog, None, fw(0, i), "rdW", i * 2048)
     frag_read(prog, None, fa(0), "rdA", 0)
@@ -465,12 +522,14 @@ def gen(block, nw=8):
     """KB must be a positive multiple of KB_GROUP (the caller checks)."""
     tag = ("blk" if block else "pt") + str(nw)
     _label[0] = 0
-    first, second, max_out = gen_loop(block, nw)
-    L = gen_prologue(block, nw)
+    lay = Layout(nw, STAGES[nw])
+    chunks, max_out = gen_loop(block, lay)
+    L = gen_prologue(block, lay)
     L.append(f"fp8pf_loop_{tag}_%=:")
-    L += first
-    L += [f"s_cmp_eq_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_tail_{tag}_%="]
-    L += second
+    for c, chunk in enumerate(chunks):
+        L += chunk
+        if c + 1 < len(chunks):              # K is any multiple of KB_GROUP blocks
+            L += [f"s_cmp_eq_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_tail_{tag}_%="]
     L += [f"s_cmp_lt_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_loop_{tag}_%="]
     L.append(f"fp8pf_tail_{tag}_%=:")
     L += gen_epilogue(block, tag, nw)
@@ -496,12 +555,15 @@ def main(path=OUT):
     sg = ", ".join(f'"s{k}"' for k in range(*CLOBBER_SGPR))
     out.append(f'#define FP8_PREFILL_ASM_CLOBBERS {vg}, {sg}, "m0", "scc", "memory"')
     out.append(f"#define FP8_PREFILL_ASM_FIXED_VGPRS {NUM_FIXED_VGPR}")
-    out.append(f"#define FP8_PREFILL_LDS_BYTES {LDS_BYTES}")
-    out.append(f"#define FP8_PREFILL_LDS_SA {SA_GROUP[0]}")
-    out.append(f"#define FP8_PREFILL_LDS_SA_GROUP_BYTES {SA_GROUP[1] - SA_GROUP[0]}")
-    out.append(f"#define FP8_PREFILL_LDS_SW {SW_TABLE}")
     out.append(f"#define FP8_PREFILL_KB_GROUP {KB_GROUP}")
-    out.append(f"#define FP8_PREFILL_LDS_W {W_STAGE[0]}")
+    for nw in SHAPES:
+        lay = Layout(nw, STAGES[nw])
+        out.append(f"#define FP8_PREFILL_W{nw}_STAGES {lay.stages}")
+        out.append(f"#define FP8_PREFILL_W{nw}_LDS_BYTES {lay.bytes}")
+        out.append(f"#define FP8_PREFILL_W{nw}_LDS_W {lay.W[0]}")
+        out.append(f"#define FP8_PREFILL_W{nw}_LDS_SA {lay.SA[0]}")
+        out.append(f"#define FP8_PREFILL_W{nw}_LDS_SA_GROUP_BYTES {lay.SA[1] - lay.SA[0]}")
+        out.append(f"#define FP8_PREFILL_W{nw}_LDS_SW {lay.SW}")
     text = "\n".join(out) + "\n"
     if path is None:
         return text
