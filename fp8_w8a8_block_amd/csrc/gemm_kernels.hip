@@ -730,13 +730,15 @@ template <int NW>
 struct PfLayout;
 template <>
 struct PfLayout<8> {
-  static constexpr int stages = FP8_PREFILL_W8_STAGES, bytes = FP8_PREFILL_W8_LDS_BYTES,
+  static constexpr int stages = FP8_PREFILL_W8_STAGES, unit = FP8_PREFILL_W8_LDS_UNIT,
+                       bytes = FP8_PREFILL_W8_LDS_BYTES,
                        w = FP8_PREFILL_W8_LDS_W, sa = FP8_PREFILL_W8_LDS_SA,
                        sa_group = FP8_PREFILL_W8_LDS_SA_GROUP_BYTES, sw = FP8_PREFILL_W8_LDS_SW;
 };
 template <>
 struct PfLayout<4> {
-  static constexpr int stages = FP8_PREFILL_W4_STAGES, bytes = FP8_PREFILL_W4_LDS_BYTES,
+  static constexpr int stages = FP8_PREFILL_W4_STAGES, unit = FP8_PREFILL_W4_LDS_UNIT,
+                       bytes = FP8_PREFILL_W4_LDS_BYTES,
                        w = FP8_PREFILL_W4_LDS_W, sa = FP8_PREFILL_W4_LDS_SA,
                        sa_group = FP8_PREFILL_W4_LDS_SA_GROUP_BYTES, sw = FP8_PREFILL_W4_LDS_SW;
 };
@@ -744,8 +746,9 @@ struct PfLayout<4> {
 template <int NW>
 constexpr bool pf_layout_ok() {
   using L = PfLayout<NW>;
-  return L::w == L::stages * kPM * 128 &&                  // activation stages first
-         L::sa == L::w + L::stages * 32 * NW * 128 &&       // then the weight stages
+  return L::unit >= 1024 && L::unit % 16 == 0 &&           // 8 rows of 128 B, then a pad
+         L::w == L::stages * (kPM / 8) * L::unit &&         // activation stages first
+         L::sa == L::w + L::stages * 4 * NW * L::unit &&    // then the weight stages
          L::sa_group == kPM * kPfKbGroup * 4 &&             // a group: 4 K blocks of 256 rows
          L::sw == L::sa + 2 * L::sa_group &&                // two groups, then the table
          L::bytes == L::sw + 2 * kPrefillMaxKB * 4 &&       // which ends the layout
@@ -757,10 +760,11 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 // pair-preserving swizzle: chunk pairs (2c, 2c + 1) stay adjacent, so the two
 // 16-byte halves of a lane's fragment are 16 bytes apart in LDS; any eight
-// consecutive rows still land on eight distinct 16-byte bank groups.  A
-// 16-row fragment read meets itself twice in every bank (the LDS serves 16
-// lanes over 64 banks per cycle); 16 bytes of padding per 8 rows remove that
-// conflict, but measured no faster, so the rows stay unpadded.
+// consecutive rows still land on eight distinct 16-byte bank groups.  The
+// LDS serves 16 lanes per cycle over 64 four-byte banks, and a fragment read
+// spans 16 rows: the pad after every 8 rows (the layout's unit is 1 KiB plus
+// 16 bytes) moves rows 8-15 one bank group along, so the 16 rows meet 16
+// distinct groups and the read takes one pass instead of two.
 __device__ __forceinline__ int swz_pair(int r) { return 2 * ((r >> 1) & 3); }
 
 // the scalar operands of the assembly must sit in SGPRs: every one passes
@@ -906,13 +910,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   const v4i dW = pf_desc(w + n0 * ld_w, ((int64_t)N - n0) * ld_w);
   const uint32_t rsA = pf_uni((uint32_t)(NW * 8 * ld_a));
   const uint32_t rsW = pf_uni((uint32_t)(NW * 8 * ld_w));
-  const uint32_t wave1k = pf_uni(lds0 + (uint32_t)wave * 1024u);
+  // operand rows sit in units of 8 (Lay::unit bytes: 1 KiB and a pad); copy
+  // t of this wave fills unit wave + NW t
+  const uint32_t wave1k = pf_uni(lds0 + (uint32_t)(wave * Lay::unit));
 
   // fragment reads: row r16 of the wave's 16-row group, stored chunk
   // (2 kg) ^ swz_pair(r16) and the next one
   const int p0 = (2 * kg) ^ swz_pair(r16);
-  const uint32_t rdA = lds0 + (uint32_t)(wm * kPWM * 128 + r16 * 128 + p0 * 16);
-  const uint32_t rdW = lds0 + (uint32_t)(Lay::w + wn * kPWN * 128 + r16 * 128 + p0 * 16);
+  const int rd_row = (r16 >> 3) * Lay::unit + (r16 & 7) * 128 + p0 * 16;
+  const uint32_t rdA = lds0 + (uint32_t)(wm * (kPWM / 8) * Lay::unit + rd_row);
+  const uint32_t rdW = lds0 + (uint32_t)(Lay::w + wn * (kPWN / 8) * Lay::unit + rd_row);
 
   // activation scales, copied by waves 0..3 every four K blocks: lane
   // r = 64 wave + lane copies the 16 bytes sa[m0 + r, g .. g + 3] to 16 r of a

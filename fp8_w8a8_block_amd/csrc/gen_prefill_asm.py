@@ -35,16 +35,27 @@ OUT = os.path.join(HERE, "prefill_asm.inc")
 # gemm_kernels.hip takes its copy of these offsets from the #defines written
 # below and static_asserts the ones it derives itself.
 KB_GROUP = 4                      # K blocks per activation-scale copy
+ROW_PAD = 16                      # bytes after every 8 operand rows
 
 
 class Layout:
     """Operand stages (activation 256 rows x 128 B, weight 32 NW rows x 128
     B, `stages` of each), then the two activation-scale group buffers
-    (4 K blocks x 256 rows each), then the weight-scale table [2][256]."""
+    (4 K blocks x 256 rows each), then the weight-scale table [2][256].
 
-    def __init__(self, nw, stages):
+    Operand rows are stored in units of 8 (1 KiB, what one copy instruction
+    writes) followed by ROW_PAD bytes.  A fragment read takes one 16-byte
+    chunk from each of 16 rows, and the LDS serves 16 lanes per cycle from
+    64 four-byte banks (256 bytes).  Unpadded, rows r and r + 8 of a fragment
+    start at the same bank, and the chunk swizzle (which keeps a lane's two
+    chunks adjacent) cannot separate them, so every read took two cycles; the
+    16-byte shift of the second unit puts them on different banks."""
+
+    def __init__(self, nw, stages, pad=ROW_PAD):
         self.nw, self.stages = nw, stages
-        a_bytes, w_bytes = 256 * 128, 32 * nw * 128
+        self.unit = 1024 + pad            # 8 rows and the pad
+        self.frag = 2 * self.unit         # 16 rows: one MFMA operand fragment
+        a_bytes, w_bytes = 32 * self.unit, 4 * nw * self.unit
         self.A = tuple(i * a_bytes for i in range(stages))
         w0 = stages * a_bytes
         self.W = tuple(w0 + i * w_bytes for i in range(stages))
@@ -200,7 +211,7 @@ def dma_copy(prog, lay, op, t, stage, k, blk):
     t * nw * 8 * ld is added to the lane's offset in a VGPR (the descriptor's
     range check sees it: rows past M or N read zero); the K offset is the
     scalar offset."""
-    base = (lay.A if op == "A" else lay.W)[stage] + t * lay.nw * 1024
+    base = (lay.A if op == "A" else lay.W)[stage] + t * lay.nw * lay.unit
     v = VCOPY[k % 2]
     if t == 0:
         prog.emit(f"v_mov_b32 v{v}, %[off{op}]")
@@ -292,7 +303,7 @@ def gen_loop(block, lay):
         # fragment j - 2 (same buffer), five slots before its first use
         for j in range(1, 8):
             at(base + 4 * j - 5, lambda st=st, j=j, p=p: frag_read(
-                prog, ("fa", st, j), fa(j % 2), "rdA", lay.A[p] - lay.A[0] + j * 2048))
+                prog, ("fa", st, j), fa(j % 2), "rdA", lay.A[p] - lay.A[0] + j * lay.frag))
 
         def barrier(st=st):
             # this wave's reads of stage p are done and its copies of K block
@@ -307,7 +318,7 @@ def gen_loop(block, lay):
             frag_read(prog, ("fw", st + 1, 0), fw(rq, 0), "rdW", lay.W[q] - lay.W[0])))
         for i in (1, 2, 3):
             at(base + 27 + i, lambda st=st, q=q, rq=rq, i=i: frag_read(
-                prog, ("fw", st + 1, i), fw(rq, i), "rdW", lay.W[q] - lay.W[0] + 2048 * i))
+                prog, ("fw", st + 1, i), fw(rq, i), "rdW", lay.W[q] - lay.W[0] + lay.frag * i))
         if block:
             def scales_lo(st=st):
                 prog.emit(f"v_mov_b32 v{SPREV}, v{SC0 + 7}")
@@ -374,7 +385,7 @@ def gen_prologue(block, lay):
     L = ["s_nop 7"]
     for k in range(128):
         L.append(f"v_mov_b32 v{ACC0 + k}, 0")
-    if lay.A[-1] - lay.A[0] + 8 * 2048 > DS_OFFSET_MAX:
+    if lay.A[-1] - lay.A[0] + 8 * lay.frag > DS_OFFSET_MAX:
         L.append(f"v_add_u32 v{RDA_HI}, 0x10000, %[rdA]")
     if block:
         for k in range(24):
@@ -396,9 +407,9 @@ def gen_prologue(block, lay):
     prog.emit("s_barrier")
     # leave S_DK on block S - 1: the first step re-issues the tail of that copy
     for i in range(4):
-        frag_read(prog, None, fw(0, i), "rdW", i * 2048)
+        frag_read(prog, None, fw(0, i), "rdW", i * lay.frag)
     frag_read(prog, None, fa(0), "rdA", 0)
-    frag_read(prog, None, fa(1), "rdA", 2048)
+    frag_read(prog, None, fa(1), "rdA", lay.frag)
     if block:
         prog.wait_all_lds()
         scale_reads(prog, None, 0, 0)
@@ -559,6 +570,7 @@ def main(path=OUT):
     for nw in SHAPES:
         lay = Layout(nw, STAGES[nw])
         out.append(f"#define FP8_PREFILL_W{nw}_STAGES {lay.stages}")
+        out.append(f"#define FP8_PREFILL_W{nw}_LDS_UNIT {lay.unit}")
         out.append(f"#define FP8_PREFILL_W{nw}_LDS_BYTES {lay.bytes}")
         out.append(f"#define FP8_PREFILL_W{nw}_LDS_W {lay.W[0]}")
         out.append(f"#define FP8_PREFILL_W{nw}_LDS_SA {lay.SA[0]}")

@@ -36,7 +36,7 @@ def test_fixed_registers_and_lds_fit():
         lay = g.Layout(nw, g.STAGES[nw])
         assert lay.bytes <= 160 * 1024
         # stages, then the scale groups and the table, none overlapping
-        assert lay.A[-1] + 256 * 128 <= lay.W[0] and lay.W[-1] + 32 * nw * 128 <= lay.SA[0]
+        assert lay.A[-1] + 32 * lay.unit <= lay.W[0] and lay.W[-1] + 4 * nw * lay.unit <= lay.SA[0]
     for nw, block in [(nw, b) for nw in g.SHAPES for b in (True, False)]:
         lines, max_out = g.gen(block, nw)
         assert max_out <= 15
@@ -74,3 +74,59 @@ def test_barriers_wait_for_the_next_block():
             assert set(loop) == {0}
         else:
             assert set(loop) <= {n, n + 1} and waits[0] == (g.STAGES[nw] - 1) * n
+
+
+def _bank_groups(addrs):
+    """16-byte bank groups (of the 16 in 64 four-byte banks) of 16 lanes'
+    16-byte accesses."""
+    return [(a // 16) % 16 for a in addrs]
+
+
+def test_fragment_reads_are_conflict_free():
+    # the LDS serves a ds_read_b128 16 lanes at a time from 64 four-byte
+    # banks; each lane of a 16-lane group reads one 16-byte chunk of its own
+    # row, and the 16 chunks must fall on 16 distinct bank groups.  Lane
+    # (r16, kg) of a wave reads row 16 j + r16 of its rows, chunks 2 kg and
+    # 2 kg + 1, stored at positions XOR-swizzled by 2 ((row >> 1) & 3).
+    g = _gen()
+
+    def swz_pair(r):
+        return 2 * ((r >> 1) & 3)
+
+    for nw in g.SHAPES:
+        lay = g.Layout(nw, g.STAGES[nw])
+        for j in range(8):                                   # fragment of the wave
+            for half in range(2):                            # first or second ds_read_b128
+                for kg in range(4):                          # 16-lane group
+                    addrs = []
+                    for r16 in range(16):
+                        row = 16 * j + r16
+                        pos = (2 * kg) ^ swz_pair(r16)
+                        addrs.append((row // 8) * lay.unit + (row % 8) * 128 + pos * 16 + 16 * half)
+                    assert len(set(_bank_groups(addrs))) == 16, (nw, j, half, kg)
+        # the unpadded layout meets every bank twice
+        flat = g.Layout(nw, g.STAGES[nw], pad=0)
+        addrs = [(r // 8) * flat.unit + (r % 8) * 128 + swz_pair(r) * 16 for r in range(16)]
+        assert len(set(_bank_groups(addrs))) == 8
+
+
+def test_copies_land_where_fragments_are_read():
+    # copy t of wave w writes tile rows 8 (w + NW t) .. + 7 as one 1 KiB unit
+    # at stage + (w + NW t) * unit; fragment j of wave row wm starts at unit
+    # 16 wm + 2 j: the two addressings agree for every row
+    g = _gen()
+    for nw in g.SHAPES:
+        lay = g.Layout(nw, g.STAGES[nw])
+        seen = set()
+        for w in range(nw):
+            for t in range(32 // nw):
+                u = w + nw * t
+                for r in range(8):
+                    row = 8 * u + r
+                    wm, j, r16 = row // 128, (row % 128) // 16, row % 16
+                    by_read = wm * 16 * lay.unit + j * lay.frag + (r16 // 8) * lay.unit + (r16 % 8) * 128
+                    by_copy = u * lay.unit + r * 128
+                    assert by_read == by_copy
+                    seen.add(row)
+        assert seen == set(range(256))
+        assert lay.A[1] - lay.A[0] == 32 * lay.unit and lay.W[0] == lay.stages * 32 * lay.unit
