@@ -232,8 +232,12 @@ def quant_weight_block(w, scale_mode="block", block_n=128, block_k=128, workspac
     return q, scales
 
 
-def block_gemm(a_q, a_s, w_q, w_s, scale_mode="block", out=None):
-    """out[M, N] bf16 = A . W^T from FP8 codes and their scales."""
+def block_gemm(a_q, a_s, w_q, w_s, scale_mode="block", out=None, workspace=None, split=True):
+    """out[M, N] bf16 = A . W^T from FP8 codes and their scales.
+
+    Shapes that split K in two (fp8_workspace_bytes(FP8_OP_GEMM) > 0) get a
+    workspace (allocated here unless given); split=False passes none, so the
+    call runs unsplit."""
     mode = _mode(scale_mode)
     M, K, ld_a = _rows(a_q, torch.uint8, "a_q")
     N, K2, ld_w = _rows(w_q, torch.uint8, "w_q")
@@ -256,9 +260,16 @@ def block_gemm(a_q, a_s, w_q, w_s, scale_mode="block", out=None):
             out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
         _device_tensor(out, "out", torch.bfloat16, a_q.device, (M, N))
         ld_out = _rows(out, torch.bfloat16, "out")[2]
+        ws_ptr, ws_len = None, 0
+        if split:
+            nws = workspace_bytes(OP_GEMM, M, N, K, mode)
+            if nws and workspace is None:
+                workspace = torch.empty(nws, dtype=torch.uint8, device=a_q.device)
+            if workspace is not None:
+                ws_ptr, ws_len = _workspace(workspace, a_q.device)
         _check(lib().fp8_block_gemm(a_q.data_ptr(), ld_a, a_s.data_ptr(), ld_as, w_q.data_ptr(),
                                     ld_w, w_s.data_ptr(), ld_ws, out.data_ptr(), ld_out,
-                                    M, N, K, mode, None, 0, _stream(a_q)))
+                                    M, N, K, mode, ws_ptr, ws_len, _stream(a_q)))
     return out
 
 

@@ -152,11 +152,11 @@ fp8_status launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LA
 // one float), then the per-tensor partials.  Every piece starts 256-byte
 // aligned.
 struct LinearLayout {
-  size_t codes, scales, partials, total;
+  size_t codes, scales, partials, gemm, gemm_bytes, total;
   int64_t ld_q;
 };
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
-LinearLayout linear_layout(int64_t M, int64_t K, int scale_mode) {
+LinearLayout linear_layout(int64_t M, int64_t N, int64_t K, int scale_mode) {
   LinearLayout l;
   l.ld_q = (K + 15) / 16 * 16;
   l.codes = 0;
@@ -165,9 +165,12 @@ LinearLayout linear_layout(int64_t M, int64_t K, int scale_mode) {
                          : scale_mode == FP8_SCALE_ROW  ? (size_t)M
                                                         : 1;
   l.partials = align256(l.scales + nscales * sizeof(float));
-  l.total = scale_mode == FP8_SCALE_TENSOR
-                ? l.partials + (size_t)fp8k::kTensorPartials * sizeof(uint32_t)
-                : l.partials;
+  l.gemm = scale_mode == FP8_SCALE_TENSOR
+               ? align256(l.partials + (size_t)fp8k::kTensorPartials * sizeof(uint32_t))
+               : l.partials;
+  // the GEMM's split-K workspace, when the shape splits
+  l.gemm_bytes = fp8k::gemm_split_bytes(M, N, K, scale_mode != FP8_SCALE_BLOCK);
+  l.total = l.gemm + l.gemm_bytes;
   return l;
 }
 
@@ -205,13 +208,17 @@ const char* fp8_status_str(fp8_status s) {
 }
 
 size_t fp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int scale_mode) {
-  (void)N;
+  if (op == FP8_OP_GEMM) {
+    if (!mode_ok(scale_mode) || M <= 0 || M >= kMaxDim || !shape_ok_kn(K) || !shape_ok_kn(N))
+      return 0;
+    return fp8k::gemm_split_bytes(M, N, K, scale_mode != FP8_SCALE_BLOCK);
+  }
   if ((op == FP8_OP_QUANT_ACT || op == FP8_OP_QUANT_WEIGHT) && scale_mode == FP8_SCALE_TENSOR)
     return (size_t)fp8k::kTensorPartials * sizeof(uint32_t);
   if (op == FP8_OP_LINEAR) {
     if (scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, K)) return 0;
     if (M <= 0 || K <= 0) return 0;
-    return linear_layout(M, K, scale_mode).total;
+    return linear_layout(M, N, K, scale_mode).total;
   }
   return 0;
 }
@@ -280,16 +287,37 @@ fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, in
                           const uint8_t* w_q, int64_t ld_w, const float* w_s, int64_t ld_ws,
                           uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
                           int scale_mode, void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace; (void)ws_bytes;
   fp8_status st = validate_gemm(a_q, ld_a, a_s, ld_as, w_q, ld_w, w_s, ld_ws, out, ld_out, M, N,
                                 K, scale_mode);
   if (st != FP8_OK || M == 0) return st;
+  // the workspace is optional; one that is used must be aligned and apart
+  // from every tensor of the call
+  size_t need = 0;
+  if (workspace && ws_bytes > 0 &&
+      (need = fp8k::gemm_split_bytes(M, N, K, scale_mode != FP8_SCALE_BLOCK)) > 0 &&
+      ws_bytes >= need) {
+    if (!aligned(workspace, 16)) return FP8_ERR_ALIGN;
+    const int64_t KB = K / 128;
+    Range r = {(uintptr_t)workspace, (uintptr_t)workspace + need};
+    Range ras = scale_mode == FP8_SCALE_BLOCK ? range_of(a_s, M, KB, ld_as, 4)
+                : scale_mode == FP8_SCALE_ROW ? row_scales(a_s, M, ld_as)
+                                              : range_of(a_s, 1, 1, 1, 4);
+    Range rws = scale_mode == FP8_SCALE_BLOCK ? range_of(w_s, N / 128, KB, ld_ws, 4)
+                : scale_mode == FP8_SCALE_ROW ? row_scales(w_s, N, ld_ws)
+                                              : range_of(w_s, 1, 1, 1, 4);
+    if (overlap(r, range_of(out, M, N, ld_out, 2)) || overlap(r, range_of(a_q, M, K, ld_a, 1)) ||
+        overlap(r, range_of(w_q, N, K, ld_w, 1)) || overlap(r, ras) || overlap(r, rws))
+      return FP8_ERR_ALIAS;
+  } else {
+    workspace = nullptr;
+    ws_bytes = 0;
+  }
   if ((st = check_device()) != FP8_OK) return st;
   const bool kconst = scale_mode != FP8_SCALE_BLOCK;
   const bool tensor = scale_mode == FP8_SCALE_TENSOR;
   return launched(fp8k::launch_gemm(a_q, ld_a, a_s, tensor ? 0 : ld_as, w_q, ld_w, w_s,
-                                    tensor ? 0 : ld_ws, out, ld_out, M, N, K, kconst,
-                                    (hipStream_t)stream));
+                                    tensor ? 0 : ld_ws, out, ld_out, M, N, K, kconst, workspace,
+                                    ws_bytes, (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -326,7 +354,7 @@ fp8_status validate_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, 
                                             : range_of(w_s, 1, 1, 1, 4);
   if (overlap(ro, rx) || overlap(ro, rw) || overlap(ro, rws)) return FP8_ERR_ALIAS;
   fused = scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, K);
-  lay = linear_layout(M, K, scale_mode);
+  lay = linear_layout(M, N, K, scale_mode);
   return FP8_OK;
 }
 
@@ -370,7 +398,8 @@ fp8_status run_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
   const int64_t lsa = scale_mode == FP8_SCALE_BLOCK ? KB : scale_mode == FP8_SCALE_ROW ? 1 : 0;
   const int64_t lsw = scale_mode == FP8_SCALE_TENSOR ? 0 : ld_ws;
   return launched(fp8k::launch_gemm(q, lay.ld_q, sa, lsa, w_q, ld_w, w_s, lsw, out, ld_out, M, N,
-                                    K, scale_mode != FP8_SCALE_BLOCK, s));
+                                    K, scale_mode != FP8_SCALE_BLOCK, ws8 + lay.gemm,
+                                    lay.gemm_bytes, s));
 }
 
 // Scratch of fp8_linear_noalloc: a file-scope device array, one copy per

@@ -767,6 +767,22 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // distinct groups and the read takes one pass instead of two.
 __device__ __forceinline__ int swz_pair(int r) { return 2 * ((r >> 1) & 3); }
 
+// Workspace of a split-K launch (two workgroups per 256 x 256 tile, each
+// half of the K blocks): one slot per (tile, wave), kSplitSlotBytes apart.
+// A slot holds the fp32 partial of one wave (128 x 64 accumulators,
+// lane-major) and then four 32-bit words: arrival counter, ready flag, and
+// the XCD records of the two halves.  The words are zeroed before every
+// launch; the partials need no initial value.
+constexpr uint32_t kSplitPartBytes = 128 * 64 * 4;
+constexpr uint32_t kSplitSlotBytes = kSplitPartBytes + 256;
+struct SplitLayout {
+  uint64_t slots, total;
+  __host__ __device__ SplitLayout(int64_t tiles, int nw) {
+    slots = (uint64_t)tiles * (uint64_t)nw;
+    total = slots * kSplitSlotBytes;
+  }
+};
+
 // the scalar operands of the assembly must sit in SGPRs: every one passes
 // through readfirstlane (the values are wave-uniform by construction)
 __device__ __forceinline__ int pf_uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -853,7 +869,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
     const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
     uint16_t* __restrict__ out, int64_t ld_out, int64_t M_all, int N, int KB, int tiles_m,
-    int tiles_n, const int64_t* __restrict__ offsets, int E, int64_t w_es, int64_t sw_es) {
+    int tiles_n, const int64_t* __restrict__ offsets, int E, int64_t w_es, int64_t sw_es,
+    uint8_t* __restrict__ ws, int nsplit) {
   constexpr int kTN = 32 * NW;                 // tile width (weight rows)
   constexpr int kWN = NW / 2;                  // waves along N
   using Lay = PfLayout<NW>;
@@ -867,7 +884,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   const int r16 = lane & 15;
   const int kg = lane >> 4;
 
-  int tm, tn;
+  int tm, tn, split = 0, tile = 0;
   int M = (int)M_all;
   if (E > 0) {
     // gridDim.x is a multiple of 8: consecutive tiles share an XCD
@@ -883,15 +900,32 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
     sw += (int64_t)e * sw_es;
     M = (int)(hi - lo);
   } else {
-    // workgroup id -> tile, as gemm_prefill_kernel
-    const int tiles = tiles_m * tiles_n;
+    // workgroup id -> tile, as gemm_prefill_kernel; with a split K the two
+    // halves of a tile are consecutive after the remap (one XCD, one L2)
+    const int G = (int)gridDim.x;
     int lin = blockIdx.x;
-    if (tiles % 8 == 0) lin = (lin % 8) * (tiles / 8) + lin / 8;
+    if (G % 8 == 0) lin = (lin % 8) * (G / 8) + lin / 8;
+    if (nsplit) {
+      split = lin & 1;
+      lin >>= 1;
+    }
+    tile = lin;
     const int group = lin / (kGroupM * tiles_n);
     const int first_m = group * kGroupM;
     const int gsize = min(tiles_m - first_m, kGroupM);
     tm = first_m + (lin % (kGroupM * tiles_n)) % gsize;
     tn = (lin % (kGroupM * tiles_n)) / gsize;
+  }
+  // split K: this workgroup takes K blocks kb0 .. kb0 + KB - 1 of its tile
+  // (the launch passes half of them as KB); operand and scale bases move to
+  // kb0 and every descriptor still ends where the whole matrix does
+  const int kb0 = split * KB;
+  const int64_t ksh = (int64_t)kb0 * 128;
+  a += ksh;
+  w += ksh;
+  if (!KCONST) {
+    sa += kb0;
+    sw += kb0;
   }
   const int64_t m0 = (int64_t)tm * kPM;
   const int64_t n0 = (int64_t)tn * kTN;
@@ -906,8 +940,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   const int cchunk = (lane & 7) ^ swz_pair(8 * (wave & 1) + crow);
   const uint32_t offA = (uint32_t)((8 * wave + crow) * ld_a + cchunk * 16);
   const uint32_t offW = (uint32_t)((8 * wave + crow) * ld_w + cchunk * 16);
-  const v4i dA = pf_desc(a + m0 * ld_a, ((int64_t)M - m0) * ld_a);
-  const v4i dW = pf_desc(w + n0 * ld_w, ((int64_t)N - n0) * ld_w);
+  const v4i dA = pf_desc(a + m0 * ld_a, ((int64_t)M - m0) * ld_a - ksh);
+  const v4i dW = pf_desc(w + n0 * ld_w, ((int64_t)N - n0) * ld_w - ksh);
   const uint32_t rsA = pf_uni((uint32_t)(NW * 8 * ld_a));
   const uint32_t rsW = pf_uni((uint32_t)(NW * 8 * ld_w));
   // operand rows sit in units of 8 (Lay::unit bytes: 1 KiB and a pad); copy
@@ -927,7 +961,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   // 16 r + 4 u; lane r16 of wave row wm reads rows 128 wm + 16 j + r16,
   // fragments 0-3 from scL and 4-7 from scH (1 KiB above)
   const uint32_t offSa = (uint32_t)((64 * (wave & 3) + lane) * ld_sa * 4);
-  const v4i dSa = pf_desc(sa + m0 * ld_sa, ((int64_t)M - m0) * ld_sa * 4);
+  const v4i dSa = pf_desc(sa + m0 * ld_sa, (((int64_t)M - m0) * ld_sa - kb0) * 4);
   const int wsa = pf_uni(wave < 4 ? 1 : 0);
   const uint32_t sam0 = pf_uni(lds0 + (uint32_t)(Lay::sa + (wave & 3) * 1024));
   const uint32_t scL0 = lds0 + (uint32_t)(Lay::sa + (wm * kPWM + r16) * 16);
@@ -965,6 +999,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   const int wave_s = pf_uni(wave);
   const uint32_t ldsb = pf_uni(lds0);
 
+  // split-K hand-over slots of this wave: its fp32 partial, arrival counter
+  // and ready flag (SplitLayout)
+  const SplitLayout spl(tiles_m * tiles_n, NW);
+  const uint32_t slot = (uint32_t)(tile * NW + wave);
+  const v4i dWs = pf_desc(ws, nsplit ? (int64_t)spl.total : 0);
+  const uint32_t wsPart = pf_uni(slot * kSplitSlotBytes);
+  // 1 | half << 8 for a split launch (the generated code reads the XCD)
+  const uint32_t xinfo = pf_uni(nsplit ? 1u | ((uint32_t)split << 8) : 0u);
+
 #define FP8_PF_COMMON_OPERANDS                                                                  \
   [rdA] "v"(rdA), [rdW] "v"(rdW), [offA] "v"(offA), [offW] "v"(offW), [dA] "s"(dA),            \
       [dW] "s"(dW), [rsA] "s"(rsA), [rsW] "s"(rsW), [dOut] "s"(dOut), [wave1k] "s"(wave1k),     \
@@ -973,6 +1016,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
 #define FP8_PF_KCONST_OPERANDS                                                                  \
   [offSaR] "v"(offSaR), [offSwR] "v"(offSwR), [dSaR] "s"(dSaR), [dSwR] "s"(dSwR),               \
       [sjA] "s"(sjA), [siW] "s"(siW), [srW] "s"(srW)
+#define FP8_PF_SPLIT_OPERANDS                                                                   \
+  [dWs] "s"(dWs), [wsPart] "s"(wsPart), [xinfo] "s"(xinfo)
 #define FP8_PF_BLOCK_OPERANDS                                                                   \
   [offSa] "v"(offSa), [scL0] "v"(scL0), [scH0] "v"(scH0), [scL1] "v"(scL1), [scH1] "v"(scH1),  \
       [offSw] "v"(offSw), [dSa] "s"(dSa), [dSw] "s"(dSw), [sam0] "s"(sam0), [wsa] "s"(wsa),     \
@@ -981,7 +1026,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
     if (NW == 8)
       asm volatile(FP8_PREFILL_ASM_TENSOR_W8
                    : [swrd] "+v"(swrd)
-                   : FP8_PF_COMMON_OPERANDS, FP8_PF_KCONST_OPERANDS
+                   : FP8_PF_COMMON_OPERANDS, FP8_PF_KCONST_OPERANDS, FP8_PF_SPLIT_OPERANDS
                    : FP8_PREFILL_ASM_CLOBBERS);
     else
       asm volatile(FP8_PREFILL_ASM_TENSOR_W4
@@ -992,7 +1037,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
     if (NW == 8)
       asm volatile(FP8_PREFILL_ASM_BLOCK_W8
                    : [swrd] "+v"(swrd)
-                   : FP8_PF_COMMON_OPERANDS, FP8_PF_BLOCK_OPERANDS
+                   : FP8_PF_COMMON_OPERANDS, FP8_PF_BLOCK_OPERANDS, FP8_PF_SPLIT_OPERANDS
                    : FP8_PREFILL_ASM_CLOBBERS);
     else
       asm volatile(FP8_PREFILL_ASM_BLOCK_W4
@@ -1003,24 +1048,42 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
 #undef FP8_PF_COMMON_OPERANDS
 #undef FP8_PF_KCONST_OPERANDS
 #undef FP8_PF_BLOCK_OPERANDS
+#undef FP8_PF_SPLIT_OPERANDS
 }
 
+// zeroes the four words of every split-K slot (no memset node, so the
+// launch sequence stays capturable)
+__global__ __launch_bounds__(256) void zero_split_words_kernel(uint8_t* __restrict__ ws, int64_t slots) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < slots * 4; i += (int64_t)gridDim.x * 256)
+    ((uint32_t*)(ws + (i >> 2) * kSplitSlotBytes + kSplitPartBytes))[i & 3] = 0u;
+}
+
+// ws != nullptr: split K in two (NW = 8 only; ws holds SplitLayout's bytes
+// for this grid and KB is even)
 template <int NW>
 hipError_t launch_prefill_asm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                               const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
                               uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int KB,
-                              bool kconst, hipStream_t st) {
+                              bool kconst, uint8_t* ws, hipStream_t st) {
   const int tiles_m = (int)((M + kPM - 1) / kPM);
   const int tiles_n = (int)((N + 32 * NW - 1) / (32 * NW));
-  dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n);
+  const int nsplit = ws ? 1 : 0;
+  dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n * (nsplit ? 2u : 1u));
+  if (nsplit) {
+    const SplitLayout spl((int64_t)tiles_m * tiles_n, NW);
+    const int64_t blocks = ((int64_t)spl.slots * 4 + 255) / 256;
+    hipLaunchKernelGGL(zero_split_words_kernel, dim3((uint32_t)(blocks < 64 ? blocks : 64)),
+                       dim3(256), 0, st, ws, (int64_t)spl.slots);
+    KB /= 2;
+  }
   if (kconst)
     hipLaunchKernelGGL((gemm_prefill_asm_kernel<true, NW>), grid, dim3(64 * NW), 0, st, a,
                        ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, (int)N, KB, tiles_m,
-                       tiles_n, nullptr, 0, (int64_t)0, (int64_t)0);
+                       tiles_n, nullptr, 0, (int64_t)0, (int64_t)0, ws, nsplit);
   else
     hipLaunchKernelGGL((gemm_prefill_asm_kernel<false, NW>), grid, dim3(64 * NW), 0, st, a,
                        ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, (int)N, KB, tiles_m,
-                       tiles_n, nullptr, 0, (int64_t)0, (int64_t)0);
+                       tiles_n, nullptr, 0, (int64_t)0, (int64_t)0, ws, nsplit);
   return hipGetLastError();
 }
 
@@ -1039,7 +1102,7 @@ hipError_t launch_prefill_asm_grouped(const uint8_t* a, int64_t ld_a, const floa
   if (g == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_prefill_asm_kernel<false, NW>), dim3((uint32_t)g), dim3(64 * NW),
                      0, st, a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, (int)N, KB,
-                     (int)tiles_m, (int)tiles_n, offsets, (int)E, w_es, sw_es);
+                     (int)tiles_m, (int)tiles_n, offsets, (int)E, w_es, sw_es, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -1233,10 +1296,35 @@ uint64_t linear_decode_items(int64_t N) { return (uint64_t)(N / 16) * 64u * FP8_
 // the grouped prefill path is taken only when its own grid fits.
 uint64_t grouped_items(int64_t N) { return (uint64_t)(N / 16) * 64u * FP8_DECODE_KSPLIT; }
 
+// The hand-scheduled prefill kernel takes the call (strides within its
+// 32-bit offsets, K a multiple of 4 blocks).
+bool prefill_asm_ok(int64_t M, int64_t KB, bool kconst, int64_t ld_a, int64_t ld_sa,
+                    int64_t ld_w, int64_t ld_sw, int64_t ld_out) {
+  return FP8_PREFILL_ASM && M > 64 && KB % kPfKbGroup == 0 && KB <= kPrefillMaxKB &&
+         (!kconst || ld_sw < kPrefillMaxLd / 4) && ld_a < kPrefillMaxLd &&
+         ld_w < kPrefillMaxLd && ld_out < kPrefillMaxLd / 2 && ld_sa < kPrefillMaxLd / 4 &&
+         ld_sw < kPrefillMaxLd;
+}
+
+// Block-scaled calls whose 256 x 256 tiles would occupy at most half of the
+// CUs: split K in two (each half a multiple of 4 blocks) when a workspace is
+// given, else 256 x 128 tiles.  0 when the call does not split.  (Scales
+// constant along K keep the 256 x 128 tiles: without the per-block fold that
+// loop is as fast as the split one plus its hand-over.)
+size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K, bool kconst) {
+  const int64_t KB = K / 128;
+  if (kconst || !FP8_PREFILL_ASM || M <= 64 || KB % (2 * kPfKbGroup) != 0 || KB > kPrefillMaxKB)
+    return 0;
+  if (M <= FP8_DECODE_MAX_M && KB <= kDecodeMaxKB) return 0;
+  const int64_t tiles256 = ((M + kPM - 1) / kPM) * ((N + kPN - 1) / kPN);
+  if (2 * tiles256 > device_cus()) return 0;
+  return (size_t)SplitLayout(tiles256, 8).total;
+}
+
 hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                        const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
                        uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
-                       bool kconst, hipStream_t st) {
+                       bool kconst, void* ws, size_t ws_bytes, hipStream_t st) {
   const int KB = (int)(K / 128);
   if (M <= FP8_DECODE_MAX_M && KB <= kDecodeMaxKB) {
     constexpr int KSPLIT = FP8_DECODE_KSPLIT, KBW = FP8_DECODE_KBW;
@@ -1260,18 +1348,21 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
     }
     return hipGetLastError();
   }
-  if (FP8_PREFILL_ASM && M > 64 && KB % kPfKbGroup == 0 && KB <= kPrefillMaxKB &&
-      (!kconst || ld_sw < kPrefillMaxLd / 4) && ld_a < kPrefillMaxLd &&
-      ld_w < kPrefillMaxLd && ld_out < kPrefillMaxLd / 2 && ld_sa < kPrefillMaxLd / 4 &&
-      ld_sw < kPrefillMaxLd) {
+  if (prefill_asm_ok(M, KB, kconst, ld_a, ld_sa, ld_w, ld_sw, ld_out)) {
     // 256 x 256 tiles unless they would occupy at most half of the CUs: then
-    // 256 x 128 tiles (twice the workgroups, one wave per SIMD)
+    // K split in two over twice the workgroups (two waves per SIMD) when the
+    // caller gave the workspace, else 256 x 128 tiles (one wave per SIMD)
     const int64_t tiles256 = ((M + kPM - 1) / kPM) * ((N + kPN - 1) / kPN);
-    if (2 * tiles256 <= device_cus())
+    if (2 * tiles256 <= device_cus()) {
+      const size_t need = gemm_split_bytes(M, N, K, kconst);
+      if (need && ws && ws_bytes >= need)
+        return launch_prefill_asm<8>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N,
+                                     KB, kconst, (uint8_t*)ws, st);
       return launch_prefill_asm<4>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N, KB,
-                                   kconst, st);
+                                   kconst, nullptr, st);
+    }
     return launch_prefill_asm<8>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N, KB,
-                                 kconst, st);
+                                 kconst, nullptr, st);
   }
   if (M > 64 && ld_a < kPrefillMaxLd && ld_w < kPrefillMaxLd) {
     const int tiles_m = (int)((M + kPM - 1) / kPM);

@@ -378,11 +378,33 @@ def gen_loop(block, lay):
     return chunks, prog.max_out
 
 
-def gen_prologue(block, lay):
+def gen_split_record(tag):
+    """Split-K launches: one lane records this half's XCD (+1) in the wave's
+    workspace slot, word 2 + half, for the partner wave's hand-over."""
+    skip = f"fp8pf_norec_{tag}_%="
+    return ["s_cmp_eq_u32 %[xinfo], 0", f"s_cbranch_scc1 {skip}",
+            "s_lshr_b32 s87, %[xinfo], 8",
+            "s_lshl_b32 s87, s87, 2",
+            "s_add_u32 s87, s87, 8",
+            f"v_mov_b32 v{P0 + 1}, s87",
+            XCC_READ,
+            "s_add_u32 s86, s86, 1",
+            f"v_mov_b32 v{P0}, s86",
+            f"s_add_u32 s88, %[wsPart], {SPLIT_PART_BYTES}",
+            "s_mov_b64 s[84:85], exec",
+            "s_mov_b64 exec, 1",
+            f"buffer_store_dword v{P0}, v{P0 + 1}, %[dWs], s88 offen sc0 sc1",
+            "s_mov_b64 exec, s[84:85]",
+            f"{skip}:"]
+
+
+def gen_prologue(block, lay, tag="", split=False):
     nw, S = lay.nw, lay.stages
     # some scalar operands were just written by v_readfirstlane; VMEM reads of
     # an SGPR written by the VALU need wait states
     L = ["s_nop 7"]
+    if split:
+        L += gen_split_record(tag)
     for k in range(128):
         L.append(f"v_mov_b32 v{ACC0 + k}, 0")
     if lay.A[-1] - lay.A[0] + 8 * lay.frag > DS_OFFSET_MAX:
@@ -423,7 +445,120 @@ EP_PITCH = 144                    # bytes per staged output row (64 bf16 + 16 B 
 EP_HALF = 64 * EP_PITCH           # one wave's staging area: 64 rows
 
 
-def gen_epilogue(block, tag, nw):
+SPLIT_PART_BYTES = 128 * 64 * 4    # one wave's fp32 accumulators
+XCC_READ = "s_getreg_b32 s86, hwreg(HW_REG_XCC_ID, 0, 4)"   # this wave's XCD
+SPIN_LIMIT = 1 << 22              # polls of the partner's flag (64-clock sleeps) before giving up
+
+
+def gen_split_exchange(tag):
+    """Hand-over of a tile split in two along K (two workgroups, each half of
+    the K blocks; a wave of one and the same wave of the other own the same
+    128 x 64 outputs and share one workspace slot: the fp32 partial, then
+    four words -- arrival counter, flag, and the XCD records of the two
+    halves).  Each wave bumps the counter (one lane, an atomic add that
+    returns the old count).  The first to arrive stores its accumulators
+    (lane-major: quad q of lane l at 1024 q + 16 l) and then writes the flag;
+    the second polls the flag, adds the stored partial to its own and goes on
+    to the bf16 stores.  fp32 addition commutes, so the sum does not depend
+    on which of the two arrives first.
+
+    Where the partial travels: every wave records its XCD (+1) when it
+    starts (gen_split_record).  If the first finds its partner recorded on its own XCD, the two
+    share an L2: the partial is stored plainly (the L1 writes through) and
+    read back past the reader's L1 (sc0), flag 2.  Otherwise (partner on
+    another XCD, or not started yet) it is written through and read past both
+    L2s (sc0 sc1), flag 1.  The atomic, the records and the flag are
+    system-coherent (sc0 sc1) and the partial's stores have completed
+    (vmcnt 0) before the flag is written, so no cache is written back or
+    invalidated as a whole.
+
+    The first waits for nothing; the second waits only for a wave that has
+    already finished its K loop, so the poll always ends (its limit only
+    guards against words that were not cleared before the launch).
+    %[xinfo] = 1 | (half << 8), or 0 when the launch does not split."""
+    vt, vo, vl16 = P0, P0 + 1, P0 + 2
+    tmp = FW0                          # 64 VGPRs: 16 quads of the partner's partial
+    lab = {n: f"fp8pf_{n}_{tag}_%=" for n in
+           ("done", "last", "spin", "ready", "nosplit", "fl2", "fflag", "l2h0", "l2h1", "addh0", "addh1")}
+    words = f"s_add_u32 s88, %[wsPart], {SPLIT_PART_BYTES}"
+
+    def one_lane(*ops):
+        return ["s_mov_b64 exec, 1", *ops, "s_waitcnt vmcnt(0)", "s_mov_b64 exec, s[84:85]", "s_nop 1",
+                f"v_readfirstlane_b32 s86, v{vt}", "s_nop 1"]
+
+    def stores(bits):
+        L = []
+        for q in range(32):
+            if q % 4 == 0:
+                L.append(f"s_add_u32 s88, %[wsPart], {4096 * (q // 4)}")
+            L.append(f"buffer_store_dwordx4 {vr(ACC0 + 4 * q, 4)}, v{vl16}, %[dWs], s88 offen "
+                     f"offset:{1024 * (q % 4)}{bits}")
+        return L
+
+    def loads(h, bits):
+        L = []
+        for q in range(16 * h, 16 * h + 16):
+            if q % 4 == 0:
+                L.append(f"s_add_u32 s88, %[wsPart], {4096 * (q // 4)}")
+            L.append(f"buffer_load_dwordx4 {vr(tmp + 4 * (q % 16), 4)}, v{vl16}, %[dWs], s88 offen "
+                     f"offset:{1024 * (q % 4)}{bits}")
+        return L
+
+    L = ["s_cmp_eq_u32 %[xinfo], 0", f"s_cbranch_scc1 {lab['nosplit']}",
+         f"v_mbcnt_lo_u32_b32 v{vl16}, -1, 0",
+         f"v_mbcnt_hi_u32_b32 v{vl16}, -1, v{vl16}",
+         f"v_lshlrev_b32 v{vl16}, 4, v{vl16}",
+         f"v_mov_b32 v{vo}, 0",
+         "s_mov_b64 s[84:85], exec",
+         words]
+    L += one_lane(f"v_mov_b32 v{vt}, 1",
+                  f"buffer_atomic_add v{vt}, v{vo}, %[dWs], s88 offen sc0 sc1")
+    L += ["s_cmp_eq_u32 s86, 0", f"s_cbranch_scc0 {lab['last']}"]
+    # first to arrive: the partner's record sits at 12 - 4 half
+    L += ["s_lshr_b32 s87, %[xinfo], 8",
+          "s_lshl_b32 s87, s87, 2",
+          "s_sub_u32 s87, 12, s87",
+          f"v_mov_b32 v{vo}, s87"]
+    L += one_lane(f"buffer_load_dword v{vt}, v{vo}, %[dWs], s88 offen sc0 sc1")
+    L += [f"v_mov_b32 v{vo}, 0",
+          XCC_READ.replace("s86", "s87"),
+          "s_add_u32 s87, s87, 1",
+          "s_cmp_eq_u32 s86, s87", f"s_cbranch_scc1 {lab['fl2']}"]
+    L += stores(" sc0 sc1")
+    L += ["s_mov_b32 s87, 1", f"s_branch {lab['fflag']}", f"{lab['fl2']}:"]
+    L += stores("")
+    L += ["s_mov_b32 s87, 2", f"{lab['fflag']}:",
+          words,
+          "s_waitcnt vmcnt(0)",
+          "s_mov_b64 exec, 1",
+          f"v_mov_b32 v{vt}, s87",
+          f"buffer_store_dword v{vt}, v{vo}, %[dWs], s88 offen offset:4 sc0 sc1",
+          "s_waitcnt vmcnt(0)",
+          "s_mov_b64 exec, s[84:85]",
+          f"s_branch {lab['done']}"]
+    # second to arrive: wait for the flag, then add the partial
+    L += [f"{lab['last']}:", f"s_mov_b32 s87, {SPIN_LIMIT}", f"{lab['spin']}:"]
+    L += one_lane(f"buffer_load_dword v{vt}, v{vo}, %[dWs], s88 offen offset:4 sc0 sc1")
+    L += ["s_cmp_lg_u32 s86, 0", f"s_cbranch_scc1 {lab['ready']}",
+          "s_sleep 1",
+          "s_sub_u32 s87, s87, 1",
+          "s_cmp_eq_u32 s87, 0",
+          f"s_cbranch_scc0 {lab['spin']}",
+          f"{lab['ready']}:"]
+    for h in range(2):
+        L += ["s_cmp_eq_u32 s86, 2", f"s_cbranch_scc1 {lab['l2h%d' % h]}"]
+        L += loads(h, " sc0 sc1")
+        L += [f"s_branch {lab['addh%d' % h]}", f"{lab['l2h%d' % h]}:"]
+        L += loads(h, " sc0")
+        L += [f"{lab['addh%d' % h]}:", "s_waitcnt vmcnt(0)"]
+        for q in range(16 * h, 16 * h + 16):
+            for r in range(4):
+                L.append(f"v_add_f32_e32 v{ACC0 + 4 * q + r}, v{ACC0 + 4 * q + r}, v{tmp + 4 * (q % 16) + r}")
+    L.append(f"{lab['nosplit']}:")
+    return L
+
+
+def gen_epilogue(block, tag, nw, split=False):
     """Fold the last fragment, round to bf16 and store.  The wave's 128 x 64
     outputs go out in two halves of 64 rows, each staged through LDS so that
     a lane stores 16 contiguous bytes and an instruction covers eight whole
@@ -472,6 +607,8 @@ def gen_epilogue(block, tag, nw):
     # every wave's copies and fragment reads are done: the stages are free
     L += ["s_waitcnt vmcnt(0) lgkmcnt(0)", "s_barrier",
           "s_cmp_eq_u32 %[colok], 0", f"s_cbranch_scc1 fp8pf_done_{tag}_%="]
+    if split:
+        L += gen_split_exchange(tag)
     vl, vt, vk, vw, vrd, vo = (FW0 + k for k in range(6))
     buf = FW0 + 8                      # 32 VGPRs of read-back data
     s_reg, s_ldo2, s_uni, s_step = S_KB, S_DK, S_DK4, S_T
@@ -535,7 +672,7 @@ def gen(block, nw=8):
     _label[0] = 0
     lay = Layout(nw, STAGES[nw])
     chunks, max_out = gen_loop(block, lay)
-    L = gen_prologue(block, lay)
+    L = gen_prologue(block, lay, tag, split=nw == 8)
     L.append(f"fp8pf_loop_{tag}_%=:")
     for c, chunk in enumerate(chunks):
         L += chunk
@@ -543,7 +680,7 @@ def gen(block, nw=8):
             L += [f"s_cmp_eq_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_tail_{tag}_%="]
     L += [f"s_cmp_lt_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_loop_{tag}_%="]
     L.append(f"fp8pf_tail_{tag}_%=:")
-    L += gen_epilogue(block, tag, nw)
+    L += gen_epilogue(block, tag, nw, split=nw == 8)
     return L, max_out
 
 

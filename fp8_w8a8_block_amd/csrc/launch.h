@@ -45,11 +45,16 @@ hipError_t launch_encode_f32(const float* x, int64_t n, uint8_t* codes, hipStrea
 // out = A . W^T.  kconst = false: block scales sa[m * ld_sa + kb],
 // sw[(n / 128) * ld_sw + kb].  kconst = true: scales constant along K,
 // out[m, n] = (sa[m * ld_sa] * sw[n * ld_sw]) * acc; ld_sa = ld_sw = 0 is the
-// per-tensor case.
+// per-tensor case.  ws: device workspace of ws_bytes (may be null); a call
+// for which gemm_split_bytes is nonzero splits K in two when ws_bytes is at
+// least that (16-byte aligned, contents not needed), else runs unsplit.
 hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                        const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
                        uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
-                       bool kconst, hipStream_t st);
+                       bool kconst, void* ws, size_t ws_bytes, hipStream_t st);
+// Workspace bytes of launch_gemm's split-K path on the current device for
+// this shape and scale form (0: the call never splits).
+size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K, bool kconst);
 
 // Fused decode linear: dynamic 1x128 quantization of x inside the decode GEMM
 // (block scales).  Dispatched for 1 <= M <= 4 and K <= 16384; the result is

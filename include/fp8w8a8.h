@@ -91,8 +91,12 @@ const char* fp8_status_str(fp8_status s);
 
 /* Bytes of device workspace a call needs (0 if none).  For op
  * FP8_OP_QUANT_ACT the shape is (M, K); for FP8_OP_QUANT_WEIGHT it is (N, K)
- * passed as (rows = M argument, K); FP8_OP_GEMM needs none; FP8_OP_LINEAR
- * takes (M, N, K) and needs none on its fused path. */
+ * passed as (rows = M argument, K); FP8_OP_LINEAR takes (M, N, K) and needs
+ * none on its fused path.  FP8_OP_GEMM takes (M, N, K): the bytes with which
+ * fp8_block_gemm splits K in two on the current device (nonzero only for
+ * FP8_SCALE_BLOCK shapes with M > 64 whose 256 x 256 output tiles would
+ * occupy at most half of the device's compute units and whose K is a
+ * multiple of 1024); the call works without them. */
 size_t fp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int scale_mode);
 
 /* fp8_quant_act -- dynamic activation quantization.
@@ -153,7 +157,16 @@ fp8_status fp8_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64
  *     out[m,n] = bf16_RNE( (a_s[m] * w_s[n]) * sum_k dec(a_q) * dec(w_q) ),
  *     the scale product in fp32, the sum accumulated in fp32.
  *   Mixing a per-tensor activation scale with block weights (or the reverse)
- *   is not a mode (FP8_ERR_SCHEME).  No workspace is used. */
+ *   is not a mode (FP8_ERR_SCHEME).
+ *   workspace (optional, may be NULL): with at least
+ *   fp8_workspace_bytes(FP8_OP_GEMM, M, N, K, scale_mode) bytes (16-byte
+ *   aligned, apart from every tensor of the call, contents not needed and
+ *   not read afterwards) a shape for which that is nonzero runs as two
+ *   workgroups per output tile, each over half of the K blocks, and adds the
+ *   two fp32 partial sums before rounding to bf16 -- the same arithmetic
+ *   with the K-block sum split in two, so the result can differ from the
+ *   unsplit call's in the last bits.  A smaller or NULL workspace runs the
+ *   call unsplit.  The result of a given call does not depend on timing. */
 fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, int64_t ld_as,
                           const uint8_t* w_q, int64_t ld_w, const float* w_s, int64_t ld_ws,
                           uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
@@ -174,7 +187,10 @@ fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, in
  *   launch (quantization inside the decode GEMM) and needs no workspace.
  *   Any other call quantizes into the workspace and then multiplies; it
  *   needs fp8_workspace_bytes(FP8_OP_LINEAR, M, N, K, scale_mode) bytes of
- *   device memory (16-byte aligned, not initialized, not read afterwards). */
+ *   device memory (16-byte aligned, not initialized, not read afterwards),
+ *   which include the GEMM's split-K bytes (fp8_block_gemm) when the shape
+ *   splits: the result equals fp8_quant_act followed by fp8_block_gemm
+ *   given that workspace. */
 fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
                       const float* w_s, int64_t ld_ws, uint16_t* out, int64_t ld_out,
                       int64_t M, int64_t N, int64_t K, int scale_mode, void* workspace,
@@ -196,7 +212,7 @@ fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
  *   streams, or threads without ordering) race and are the caller's to
  *   order.  No byte of it needs to start at any value (each call writes
  *   everything it reads). */
-#define FP8_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define FP8_NOALLOC_SCRATCH_BYTES (64u << 20)
 fp8_status fp8_linear_noalloc(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
                               const float* w_s, int64_t ld_ws, uint16_t* out, int64_t ld_out,
                               int64_t M, int64_t N, int64_t K, int scale_mode, void* stream);

@@ -452,6 +452,93 @@ def test_gemm_large_stratified():
                   f"large rows {lo}.. x cols")
 
 
+# ---------------------------------------------------------------------------
+# split K: shapes whose 256 x 256 tiles would fill at most half of the CUs
+# run as two workgroups per tile, each over half of the K blocks, when the
+# call has the workspace
+
+def _split_case(M, N, K, mode, seed):
+    rng = np.random.default_rng(seed)
+    a = synth.f32_to_bf16_bits((rng.standard_normal((M, K)) * 2).astype(np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.03).astype(np.float32))
+    qmode = "row" if mode == "row" else mode
+    wq, ws = fp8.quant_weight_block(dev_bf16(w), qmode)
+    aq, as_ = fp8.quant_act(dev_bf16(a), qmode)
+    return a, w, aq, as_, wq, ws
+
+
+def _oracle_mode(a, w, mode):
+    if mode == "row":
+        aq, sa = quant.quant_rows_ref(a)
+        wq, sw = quant.quant_rows_ref(w)
+        return oracle_refs.rows(aq, sa, wq, sw)
+    return oracle_gemm(a, w, mode)
+
+
+@pytest.mark.parametrize("M,N,K,mode", [(512, 512, 2048, "block"), (300, 384, 1024, "block"),
+                                        (65, 256, 1024, "block"), (257, 1024, 3072, "block"),
+                                        (1000, 640, 2048, "block"), (1024, 2048, 8192, "block")])
+def test_gemm_split_k(M, N, K, mode):
+    # both forms against the oracle; the split form again with a workspace
+    # full of garbage (counters are cleared by the call) and once more
+    # reusing that workspace: the same bits every time
+    nws = fp8.workspace_bytes(fp8._lib.OP_GEMM, M, N, K, mode)
+    assert nws > 0, (M, N, K)
+    a, w, aq, as_, wq, ws = _split_case(M, N, K, mode, [M, N, K, 3])
+    log("gemm split K", (M, N, K, mode), nws)
+    out_split = host_u16(fp8.block_gemm(aq, as_, wq, ws, mode))
+    out_plain = host_u16(fp8.block_gemm(aq, as_, wq, ws, mode, split=False))
+    junk = torch.full((nws,), 0xA5, dtype=torch.uint8, device="cuda")
+    out_junk = host_u16(fp8.block_gemm(aq, as_, wq, ws, mode, workspace=junk))
+    out_again = host_u16(fp8.block_gemm(aq, as_, wq, ws, mode, workspace=junk))
+    torch.cuda.synchronize()
+    assert np.array_equal(out_split, out_junk) and np.array_equal(out_split, out_again)
+    ref = _oracle_mode(a, w, mode)
+    check_out(out_split, ref, f"split {mode} {M}x{N}x{K}")
+    check_out(out_plain, ref, f"unsplit {mode} {M}x{N}x{K}")
+
+
+def test_gemm_split_k_small_workspace_runs_unsplit():
+    M, N, K = 300, 512, 2048
+    nws = fp8.workspace_bytes(fp8._lib.OP_GEMM, M, N, K, "block")
+    a, w, aq, as_, wq, ws = _split_case(M, N, K, "block", 17)
+    short = torch.zeros((nws - 256,), dtype=torch.uint8, device="cuda")
+    out_short = host_u16(fp8.block_gemm(aq, as_, wq, ws, "block", workspace=short))
+    out_plain = host_u16(fp8.block_gemm(aq, as_, wq, ws, "block", split=False))
+    assert np.array_equal(out_short, out_plain)
+    assert torch.all(short == 0)                 # an unused workspace is not touched
+
+
+def test_linear_split_k_matches_two_calls():
+    # fp8_linear's workspace holds the GEMM's split-K bytes: the result equals
+    # quant_act followed by block_gemm with its workspace
+    M, N, K = 512, 1024, 4096
+    rng = np.random.default_rng(71)
+    a = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    assert fp8.workspace_bytes(fp8._lib.OP_LINEAR, M, N, K, "block") >= \
+        M * K + fp8.workspace_bytes(fp8._lib.OP_GEMM, M, N, K, "block")
+    wq, ws = fp8.quant_weight_block(dev_bf16(w))
+    x = dev_bf16(a)
+    got = host_u16(fp8.linear(x, wq, ws))
+    assert np.array_equal(got, _two_call(x, wq, ws, "block"))
+    check_out(got, oracle_gemm(a, w), "linear split K")
+
+
+@pytest.mark.parametrize("mode", ["tensor", "row"])
+def test_gemm_constant_scales_do_not_split(mode):
+    # scales constant along K keep the unsplit kernel: no workspace, and a
+    # workspace given anyway changes nothing
+    M, N, K = 512, 512, 2048
+    assert fp8.workspace_bytes(fp8._lib.OP_GEMM, M, N, K, mode) == 0
+    a, w, aq, as_, wq, ws = _split_case(M, N, K, mode, 29)
+    junk = torch.full((1 << 20,), 0xA5, dtype=torch.uint8, device="cuda")
+    o1 = host_u16(fp8.block_gemm(aq, as_, wq, ws, mode))
+    o2 = host_u16(fp8.block_gemm(aq, as_, wq, ws, mode, workspace=junk))
+    assert np.array_equal(o1, o2)
+    check_out(o1, _oracle_mode(a, w, mode), f"{mode} {M}x{N}x{K}")
+
+
 def test_gemm_small_integers_exact():
     """Codes are small integers, unit scales: every partial is exact, so the
     bf16 output must equal the exact result bit for bit."""

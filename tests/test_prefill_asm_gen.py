@@ -130,3 +130,31 @@ def test_copies_land_where_fragments_are_read():
                     seen.add(row)
         assert seen == set(range(256))
         assert lay.A[1] - lay.A[0] == 32 * lay.unit and lay.W[0] == lay.stages * 32 * lay.unit
+
+
+def test_split_handover_stays_in_its_slot():
+    # every workspace access of the split-K hand-over lies inside the wave's
+    # slot: the 32 KiB partial (quad q of lane l at 1024 q + 16 l) and the
+    # four words after it; the 256 x 128 shape has no hand-over
+    g = _gen()
+    for block in (True, False):
+        lines, _ = g.gen(block, 8)
+        base = None
+        seen = 0
+        for l in lines:
+            m = re.fullmatch(r"s_add_u32 s88, %\[wsPart\], (\d+)", l)
+            if m:
+                base = int(m.group(1))
+                assert base % 4096 == 0 and base <= g.SPLIT_PART_BYTES
+            if "%[dWs]" in l:
+                seen += 1
+                off = int(re.search(r"offset:(\d+)", l).group(1)) if "offset:" in l else 0
+                assert "s88" in l and base is not None
+                if base == g.SPLIT_PART_BYTES:               # the words (voffset 0 or 8 / 12)
+                    assert off in (0, 4)
+                else:                                        # a 16-byte quad, lane offset <= 1008
+                    assert l.startswith(("buffer_load_dwordx4", "buffer_store_dwordx4"))
+                    assert base + off + 1008 + 16 <= g.SPLIT_PART_BYTES
+        assert seen == 1 + 1 + 1 + 2 * 32 + 1 + 1 + 2 * 32      # record, atomic, partner, stores, flag, poll, loads
+        for l in g.gen(block, 4)[0]:
+            assert "%[dWs]" not in l

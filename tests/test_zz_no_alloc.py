@@ -34,6 +34,7 @@ def operands(seed, M, N, K, mode):
     ("tensor", [(257, 256, 1024), (3, 256, 1024)]),       # per-tensor partials in scratch
     ("row", [(64, 512, 512), (17, 512, 512)]),
     ("block", [(4, 512, 1024), (1, 512, 1024)]),          # fused path: no scratch
+    ("block", [(512, 1024, 4096), (300, 512, 2048)]),     # GEMM split in K: its slots in scratch
 ])
 def test_noalloc_matches_linear(mode, shapes):
     for i, (M, N, K) in enumerate(shapes):
@@ -47,14 +48,14 @@ def test_noalloc_matches_linear(mode, shapes):
 
 
 def test_noalloc_refuses_calls_beyond_its_scratch():
-    # 8192 x 4096 block activations need 32 MiB of codes plus scales: more than
-    # the 32 MiB scratch; refused before anything is enqueued
-    M, N, K = 8192, 256, 4096
+    # 16384 x 4096 block activations need 64 MiB of codes plus scales: more
+    # than the 64 MiB scratch; refused before anything is enqueued
+    M, N, K = 16384, 256, 4096
     x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
     wq = torch.zeros((N, K), dtype=torch.uint8, device="cuda")
     ws = torch.ones((N // 128, K // 128), dtype=torch.float32, device="cuda")
     out = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
-    assert fp8.workspace_bytes(3, M, N, K, "block") > (32 << 20)
+    assert fp8.workspace_bytes(3, M, N, K, "block") > (64 << 20)
     with pytest.raises(ValueError, match="scratch"):
         fp8.linear_noalloc(x, wq, ws, out)
     torch.cuda.synchronize()
