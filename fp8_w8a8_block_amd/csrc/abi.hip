@@ -387,8 +387,12 @@ fp8_status run_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
   uint8_t* q = ws8 + lay.codes;
   float* sa = (float*)(ws8 + lay.scales);
   hipError_t e;
+  // block scales: the quantizer also clears the GEMM's split-K slot words
+  const uint32_t nzero =
+      scale_mode == FP8_SCALE_BLOCK && lay.gemm_bytes ? fp8k::gemm_split_words(M, N, K, false) : 0;
   if (scale_mode == FP8_SCALE_BLOCK)
-    e = fp8k::launch_quant_act_block(x, M, K, ld_x, q, lay.ld_q, sa, KB, s);
+    e = fp8k::launch_quant_act_block(x, M, K, ld_x, q, lay.ld_q, sa, KB, s,
+                                     (uint32_t*)(ws8 + lay.gemm), nzero);
   else if (scale_mode == FP8_SCALE_ROW)
     e = fp8k::launch_quant_rows(x, M, K, ld_x, q, lay.ld_q, sa, 1, s);
   else
@@ -399,7 +403,7 @@ fp8_status run_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
   const int64_t lsw = scale_mode == FP8_SCALE_TENSOR ? 0 : ld_ws;
   return launched(fp8k::launch_gemm(q, lay.ld_q, sa, lsa, w_q, ld_w, w_s, lsw, out, ld_out, M, N,
                                     K, scale_mode != FP8_SCALE_BLOCK, ws8 + lay.gemm,
-                                    lay.gemm_bytes, s));
+                                    lay.gemm_bytes, s, nzero > 0));
 }
 
 // Scratch of fp8_linear_noalloc: a file-scope device array, one copy per

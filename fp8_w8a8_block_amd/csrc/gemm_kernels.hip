@@ -768,18 +768,19 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int swz_pair(int r) { return 2 * ((r >> 1) & 3); }
 
 // Workspace of a split-K launch (two workgroups per 256 x 256 tile, each
-// half of the K blocks): one slot per (tile, wave), kSplitSlotBytes apart.
-// A slot holds the fp32 partial of one wave (128 x 64 accumulators,
-// lane-major) and then four 32-bit words: arrival counter, ready flag, and
-// the XCD records of the two halves.  The words are zeroed before every
-// launch; the partials need no initial value.
+// half of the K blocks), one slot per (tile, wave): four 32-bit words at
+// 16 slot (arrival counter, ready flag, the XCD records of the two halves),
+// zeroed before every launch, and from kSplitWordsBytes on the fp32
+// partials, 32 KiB per slot (128 x 64 accumulators, lane-major), which need
+// no initial value.
 constexpr uint32_t kSplitPartBytes = 128 * 64 * 4;
-constexpr uint32_t kSplitSlotBytes = kSplitPartBytes + 256;
+constexpr uint32_t kSplitWordsBytes = 65536;
+constexpr uint64_t kSplitMaxSlots = kSplitWordsBytes / 16;
 struct SplitLayout {
   uint64_t slots, total;
   __host__ __device__ SplitLayout(int64_t tiles, int nw) {
     slots = (uint64_t)tiles * (uint64_t)nw;
-    total = slots * kSplitSlotBytes;
+    total = kSplitWordsBytes + slots * kSplitPartBytes;
   }
 };
 
@@ -1004,7 +1005,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   const SplitLayout spl(tiles_m * tiles_n, NW);
   const uint32_t slot = (uint32_t)(tile * NW + wave);
   const v4i dWs = pf_desc(ws, nsplit ? (int64_t)spl.total : 0);
-  const uint32_t wsPart = pf_uni(slot * kSplitSlotBytes);
+  const uint32_t wsPart = pf_uni(kSplitWordsBytes + slot * kSplitPartBytes);
   // 1 | half << 8 for a split launch (the generated code reads the XCD)
   const uint32_t xinfo = pf_uni(nsplit ? 1u | ((uint32_t)split << 8) : 0u);
 
@@ -1051,11 +1052,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
 #undef FP8_PF_SPLIT_OPERANDS
 }
 
-// zeroes the four words of every split-K slot (no memset node, so the
-// launch sequence stays capturable)
-__global__ __launch_bounds__(256) void zero_split_words_kernel(uint8_t* __restrict__ ws, int64_t slots) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < slots * 4; i += (int64_t)gridDim.x * 256)
-    ((uint32_t*)(ws + (i >> 2) * kSplitSlotBytes + kSplitPartBytes))[i & 3] = 0u;
+// zeroes n 32-bit words (the split-K slot words) without a memset node, so
+// the launch sequence stays capturable
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0u;
 }
 
 // ws != nullptr: split K in two (NW = 8 only; ws holds SplitLayout's bytes
@@ -1064,16 +1065,18 @@ template <int NW>
 hipError_t launch_prefill_asm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                               const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
                               uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int KB,
-                              bool kconst, uint8_t* ws, hipStream_t st) {
+                              bool kconst, uint8_t* ws, hipStream_t st, bool words_zero = false) {
   const int tiles_m = (int)((M + kPM - 1) / kPM);
   const int tiles_n = (int)((N + 32 * NW - 1) / (32 * NW));
   const int nsplit = ws ? 1 : 0;
   dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n * (nsplit ? 2u : 1u));
   if (nsplit) {
     const SplitLayout spl((int64_t)tiles_m * tiles_n, NW);
-    const int64_t blocks = ((int64_t)spl.slots * 4 + 255) / 256;
-    hipLaunchKernelGGL(zero_split_words_kernel, dim3((uint32_t)(blocks < 64 ? blocks : 64)),
-                       dim3(256), 0, st, ws, (int64_t)spl.slots);
+    const int64_t words = (int64_t)spl.slots * 4;
+    const int64_t blocks = (words + 255) / 256;
+    if (!words_zero)
+      hipLaunchKernelGGL(zero_words_kernel, dim3((uint32_t)(blocks < 64 ? blocks : 64)),
+                         dim3(256), 0, st, (uint32_t*)ws, words);
     KB /= 2;
   }
   if (kconst)
@@ -1317,14 +1320,19 @@ size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K, bool kconst) {
     return 0;
   if (M <= FP8_DECODE_MAX_M && KB <= kDecodeMaxKB) return 0;
   const int64_t tiles256 = ((M + kPM - 1) / kPM) * ((N + kPN - 1) / kPN);
-  if (2 * tiles256 > device_cus()) return 0;
+  if (2 * tiles256 > device_cus() || (uint64_t)tiles256 * 8 > kSplitMaxSlots) return 0;
   return (size_t)SplitLayout(tiles256, 8).total;
+}
+
+uint32_t gemm_split_words(int64_t M, int64_t N, int64_t K, bool kconst) {
+  if (!gemm_split_bytes(M, N, K, kconst)) return 0;
+  return (uint32_t)(SplitLayout(((M + kPM - 1) / kPM) * ((N + kPN - 1) / kPN), 8).slots * 4);
 }
 
 hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                        const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
                        uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
-                       bool kconst, void* ws, size_t ws_bytes, hipStream_t st) {
+                       bool kconst, void* ws, size_t ws_bytes, hipStream_t st, bool words_zero) {
   const int KB = (int)(K / 128);
   if (M <= FP8_DECODE_MAX_M && KB <= kDecodeMaxKB) {
     constexpr int KSPLIT = FP8_DECODE_KSPLIT, KBW = FP8_DECODE_KBW;
@@ -1357,7 +1365,7 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
       const size_t need = gemm_split_bytes(M, N, K, kconst);
       if (need && ws && ws_bytes >= need)
         return launch_prefill_asm<8>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N,
-                                     KB, kconst, (uint8_t*)ws, st);
+                                     KB, kconst, (uint8_t*)ws, st, words_zero);
       return launch_prefill_asm<4>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N, KB,
                                    kconst, nullptr, st);
     }

@@ -378,6 +378,12 @@ def gen_loop(block, lay):
     return chunks, prog.max_out
 
 
+def slot_words():
+    """s88 = byte offset of this wave's slot words: %[wsPart] is
+    SPLIT_WORDS_BYTES + 32 KiB slot, the words sit at 16 slot."""
+    return [f"s_sub_u32 s88, %[wsPart], {SPLIT_WORDS_BYTES}", "s_lshr_b32 s88, s88, 11"]
+
+
 def gen_split_record(tag):
     """Split-K launches: one lane records this half's XCD (+1) in the wave's
     workspace slot, word 2 + half, for the partner wave's hand-over."""
@@ -390,7 +396,7 @@ def gen_split_record(tag):
             XCC_READ,
             "s_add_u32 s86, s86, 1",
             f"v_mov_b32 v{P0}, s86",
-            f"s_add_u32 s88, %[wsPart], {SPLIT_PART_BYTES}",
+            *slot_words(),
             "s_mov_b64 s[84:85], exec",
             "s_mov_b64 exec, 1",
             f"buffer_store_dword v{P0}, v{P0 + 1}, %[dWs], s88 offen sc0 sc1",
@@ -446,6 +452,7 @@ EP_HALF = 64 * EP_PITCH           # one wave's staging area: 64 rows
 
 
 SPLIT_PART_BYTES = 128 * 64 * 4    # one wave's fp32 accumulators
+SPLIT_WORDS_BYTES = 65536         # the slots' words come first: 16 bytes per slot
 XCC_READ = "s_getreg_b32 s86, hwreg(HW_REG_XCC_ID, 0, 4)"   # this wave's XCD
 SPIN_LIMIT = 1 << 22              # polls of the partner's flag (64-clock sleeps) before giving up
 
@@ -453,9 +460,9 @@ SPIN_LIMIT = 1 << 22              # polls of the partner's flag (64-clock sleeps
 def gen_split_exchange(tag):
     """Hand-over of a tile split in two along K (two workgroups, each half of
     the K blocks; a wave of one and the same wave of the other own the same
-    128 x 64 outputs and share one workspace slot: the fp32 partial, then
-    four words -- arrival counter, flag, and the XCD records of the two
-    halves).  Each wave bumps the counter (one lane, an atomic add that
+    128 x 64 outputs and share one workspace slot: four words -- arrival
+    counter, flag, and the XCD records of the two halves -- and a 32 KiB fp32
+    partial).  Each wave bumps the counter (one lane, an atomic add that
     returns the old count).  The first to arrive stores its accumulators
     (lane-major: quad q of lane l at 1024 q + 16 l) and then writes the flag;
     the second polls the flag, adds the stored partial to its own and goes on
@@ -480,7 +487,7 @@ def gen_split_exchange(tag):
     tmp = FW0                          # 64 VGPRs: 16 quads of the partner's partial
     lab = {n: f"fp8pf_{n}_{tag}_%=" for n in
            ("done", "last", "spin", "ready", "nosplit", "fl2", "fflag", "l2h0", "l2h1", "addh0", "addh1")}
-    words = f"s_add_u32 s88, %[wsPart], {SPLIT_PART_BYTES}"
+    words = slot_words()
 
     def one_lane(*ops):
         return ["s_mov_b64 exec, 1", *ops, "s_waitcnt vmcnt(0)", "s_mov_b64 exec, s[84:85]", "s_nop 1",
@@ -510,7 +517,7 @@ def gen_split_exchange(tag):
          f"v_lshlrev_b32 v{vl16}, 4, v{vl16}",
          f"v_mov_b32 v{vo}, 0",
          "s_mov_b64 s[84:85], exec",
-         words]
+         *words]
     L += one_lane(f"v_mov_b32 v{vt}, 1",
                   f"buffer_atomic_add v{vt}, v{vo}, %[dWs], s88 offen sc0 sc1")
     L += ["s_cmp_eq_u32 s86, 0", f"s_cbranch_scc0 {lab['last']}"]
@@ -528,7 +535,7 @@ def gen_split_exchange(tag):
     L += ["s_mov_b32 s87, 1", f"s_branch {lab['fflag']}", f"{lab['fl2']}:"]
     L += stores("")
     L += ["s_mov_b32 s87, 2", f"{lab['fflag']}:",
-          words,
+          *words,
           "s_waitcnt vmcnt(0)",
           "s_mov_b64 exec, 1",
           f"v_mov_b32 v{vt}, s87",

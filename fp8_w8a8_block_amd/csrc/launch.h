@@ -27,9 +27,11 @@ uint64_t gemm_items(int64_t M, int64_t N, int64_t K);
 uint64_t grouped_items(int64_t N);
 uint64_t linear_decode_items(int64_t N);
 
+// zero / zero_n: words the launch also sets to 0 (the next GEMM's split-K
+// slot words, so that GEMM needs no clearing launch of its own)
 hipError_t launch_quant_act_block(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                                   uint8_t* q, int64_t ld_q, float* s, int64_t ld_s,
-                                  hipStream_t st);
+                                  hipStream_t st, uint32_t* zero = nullptr, uint32_t zero_n = 0);
 hipError_t launch_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
                                      uint8_t* q, int64_t ld_q, float* s, int64_t ld_s,
                                      hipStream_t st);
@@ -48,13 +50,18 @@ hipError_t launch_encode_f32(const float* x, int64_t n, uint8_t* codes, hipStrea
 // per-tensor case.  ws: device workspace of ws_bytes (may be null); a call
 // for which gemm_split_bytes is nonzero splits K in two when ws_bytes is at
 // least that (16-byte aligned, contents not needed), else runs unsplit.
+// words_zero: the split-K slot words (the first gemm_split_words 32-bit
+// words of ws) are already 0, so the launch skips clearing them.
 hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                        const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
                        uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int64_t K,
-                       bool kconst, void* ws, size_t ws_bytes, hipStream_t st);
+                       bool kconst, void* ws, size_t ws_bytes, hipStream_t st,
+                       bool words_zero = false);
 // Workspace bytes of launch_gemm's split-K path on the current device for
-// this shape and scale form (0: the call never splits).
+// this shape and scale form (0: the call never splits), and how many 32-bit
+// words at its start must be 0 when the launch begins.
 size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K, bool kconst);
+uint32_t gemm_split_words(int64_t M, int64_t N, int64_t K, bool kconst);
 
 // Fused decode linear: dynamic 1x128 quantization of x inside the decode GEMM
 // (block scales).  Dispatched for 1 <= M <= 4 and K <= 16384; the result is

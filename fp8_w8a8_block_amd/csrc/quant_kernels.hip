@@ -26,7 +26,10 @@ namespace {
 template <int GPT>
 __global__ __launch_bounds__(256) void quant_act_block_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
-    float* __restrict__ s, int64_t ld_s, uint32_t groups_per_row, uint32_t blocks_per_row) {
+    float* __restrict__ s, int64_t ld_s, uint32_t groups_per_row, uint32_t blocks_per_row,
+    uint32_t* __restrict__ zero, uint32_t zero_n) {
+  if (blockIdx.x == 0)
+    for (uint32_t i = threadIdx.x; i < zero_n; i += 256) zero[i] = 0u;
   const uint32_t row = blockIdx.x / blocks_per_row;
   const uint32_t blk = blockIdx.x - row * blocks_per_row;
   const uint32_t lane16 = threadIdx.x & 15u;
@@ -63,7 +66,10 @@ __global__ __launch_bounds__(256) void quant_act_block_kernel(
 template <int GPT>
 __global__ __launch_bounds__(256) void quant_act_flat_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
-    float* __restrict__ s, int64_t ld_s, uint32_t groups_per_row, uint32_t total_groups) {
+    float* __restrict__ s, int64_t ld_s, uint32_t groups_per_row, uint32_t total_groups,
+    uint32_t* __restrict__ zero, uint32_t zero_n) {
+  if (blockIdx.x == 0)
+    for (uint32_t i = threadIdx.x; i < zero_n; i += 256) zero[i] = 0u;
   const uint32_t lane16 = threadIdx.x & 15u;
   const uint32_t slot = threadIdx.x >> 4;
   uint4 v[GPT];
@@ -268,7 +274,7 @@ uint64_t encode_items(int64_t n) { return ((uint64_t)n + 255) / 256 * 256u; }
 
 hipError_t launch_quant_act_block(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                                   uint8_t* q, int64_t ld_q, float* s, int64_t ld_s,
-                                  hipStream_t st) {
+                                  hipStream_t st, uint32_t* zero, uint32_t zero_n) {
   constexpr int GPT = kActGPT;
   const uint32_t groups = (uint32_t)(K / kGroup);
   const uint64_t total = (uint64_t)M * groups;
@@ -278,14 +284,14 @@ hipError_t launch_quant_act_block(const uint16_t* x, int64_t M, int64_t K, int64
   if (act_flat(groups, total)) {
     const uint64_t grid = (total + 16u * GPT - 1) / (16u * GPT);
     hipLaunchKernelGGL(quant_act_flat_kernel<GPT>, dim3((uint32_t)grid), dim3(256), 0, st, x,
-                       ld_x, q, ld_q, s, ld_s, groups, (uint32_t)total);
+                       ld_x, q, ld_q, s, ld_s, groups, (uint32_t)total, zero, zero_n);
     return hipGetLastError();
   }
   const uint32_t per_block = 16u * GPT;
   const uint32_t bpr = (groups + per_block - 1) / per_block;
   const uint64_t grid = (uint64_t)bpr * (uint64_t)M;
   hipLaunchKernelGGL(quant_act_block_kernel<GPT>, dim3((uint32_t)grid), dim3(256), 0, st, x,
-                     ld_x, q, ld_q, s, ld_s, groups, bpr);
+                     ld_x, q, ld_q, s, ld_s, groups, bpr, zero, zero_n);
   return hipGetLastError();
 }
 

@@ -134,23 +134,26 @@ def test_copies_land_where_fragments_are_read():
 
 def test_split_handover_stays_in_its_slot():
     # every workspace access of the split-K hand-over lies inside the wave's
-    # slot: the 32 KiB partial (quad q of lane l at 1024 q + 16 l) and the
-    # four words after it; the 256 x 128 shape has no hand-over
+    # slot: its four words (16 bytes at 16 slot) and its 32 KiB partial (quad
+    # q of lane l at 1024 q + 16 l); the 256 x 128 shape has no hand-over
     g = _gen()
     for block in (True, False):
         lines, _ = g.gen(block, 8)
         base = None
         seen = 0
-        for l in lines:
+        for l, nxt in zip(lines, lines[1:] + [""]):
             m = re.fullmatch(r"s_add_u32 s88, %\[wsPart\], (\d+)", l)
             if m:
                 base = int(m.group(1))
-                assert base % 4096 == 0 and base <= g.SPLIT_PART_BYTES
+                assert base % 4096 == 0 and base < g.SPLIT_PART_BYTES
+            if l == f"s_sub_u32 s88, %[wsPart], {g.SPLIT_WORDS_BYTES}":
+                assert nxt == "s_lshr_b32 s88, s88, 11"      # 16 bytes per 32 KiB slot
+                base = "words"
             if "%[dWs]" in l:
                 seen += 1
                 off = int(re.search(r"offset:(\d+)", l).group(1)) if "offset:" in l else 0
                 assert "s88" in l and base is not None
-                if base == g.SPLIT_PART_BYTES:               # the words (voffset 0 or 8 / 12)
+                if base == "words":                          # the words (voffset 0 or 8 / 12)
                     assert off in (0, 4)
                 else:                                        # a 16-byte quad, lane offset <= 1008
                     assert l.startswith(("buffer_load_dwordx4", "buffer_store_dwordx4"))
