@@ -1052,11 +1052,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
 #undef FP8_PF_SPLIT_OPERANDS
 }
 
-// zeroes n 32-bit words (the split-K slot words) without a memset node, so
-// the launch sequence stays capturable
+// zeroes n 32-bit words (the split-K slot words), one per thread, without a
+// memset node, so the launch sequence stays capturable
 __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    p[i] = 0u;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 // ws != nullptr: split K in two (NW = 8 only; ws holds SplitLayout's bytes
@@ -1075,8 +1075,8 @@ hipError_t launch_prefill_asm(const uint8_t* a, int64_t ld_a, const float* sa, i
     const int64_t words = (int64_t)spl.slots * 4;
     const int64_t blocks = (words + 255) / 256;
     if (!words_zero)
-      hipLaunchKernelGGL(zero_words_kernel, dim3((uint32_t)(blocks < 64 ? blocks : 64)),
-                         dim3(256), 0, st, (uint32_t*)ws, words);
+      hipLaunchKernelGGL(zero_words_kernel, dim3((uint32_t)blocks), dim3(256), 0, st,
+                         (uint32_t*)ws, words);
     KB /= 2;
   }
   if (kconst)
