@@ -328,24 +328,50 @@ def secondary_gemm(name, n_launches=None):
 
 
 def hbm_reference(nbytes=1 << 30, n=10):
-    """Timed HBM reference beside the kernels: torch's device copy of
-    a 1 GiB buffer (2 GiB moved per launch) and torch's sum over it (a pure
-    1 GiB read), each n back-to-back launches timed like the kernels."""
+    """Timed HBM references beside the kernels, each n back-to-back
+    launches timed like the kernels: torch's device copy of a 1 GiB buffer
+    (2 GiB moved per launch), and a plain streaming read (hbm_probe.hip, its
+    own library) of the same 1 GiB and of 45.1 MB -- the decode weight's
+    bytes, rotating over eight such buffers so the Infinity Cache holds none
+    of them."""
+    import ctypes
     import torch
+    path = os.path.join(ROOT, "fp8_w8a8_block_amd", "libhbmprobe.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m fp8_w8a8_block_amd.build`")
+    probe = ctypes.CDLL(path)
+    probe.hbm_read_probe.restype = ctypes.c_int
+    probe.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                     ctypes.c_void_p]
+    grid = 2048
+    sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     src.fill_(1)
     dst = torch.empty_like(src)
-    acc = torch.empty((), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     c_ms = time_launches(lambda i: dst.copy_(src), n)
-    r_ms = time_launches(lambda i: torch.sum(src.view(torch.float32), dim=0, out=acc), n)
-    del src, dst
+
+    def read(buf):
+        st = torch.cuda.current_stream().cuda_stream
+        rc = probe.hbm_read_probe(buf.data_ptr(), buf.numel(), sink.data_ptr(), grid, st)
+        if rc != 0:
+            raise RuntimeError(f"hbm_read_probe failed: {rc}")
+    r_ms = time_launches(lambda i: read(src), n)
+    del dst
+    small = 11008 * 4096
+    bufs = [src[i * small:(i + 1) * small] for i in range(8)]
+    s_ms = time_launches(lambda i: read(bufs[i % 8]), 4 * n)
+    del src, bufs
     torch.cuda.empty_cache()
     return {"copy": {"bytes_moved": 2 * nbytes, "avg_launch_us": c_ms * 1e3,
                      "GB/s": 2 * nbytes / (c_ms * 1e-3) / 1e9},
-            "read_sum": {"bytes_read": nbytes, "avg_launch_us": r_ms * 1e3,
-                         "GB/s": nbytes / (r_ms * 1e-3) / 1e9},
-            "note": "torch.Tensor.copy_ and torch.sum over a 1 GiB device buffer"}
+            "read_stream": {"bytes_read": nbytes, "avg_launch_us": r_ms * 1e3,
+                            "GB/s": nbytes / (r_ms * 1e-3) / 1e9},
+            "read_stream_decode_bytes": {"bytes_read": small, "avg_launch_us": s_ms * 1e3,
+                                         "GB/s": small / (s_ms * 1e-3) / 1e9},
+            "note": ("torch.Tensor.copy_ over a 1 GiB device buffer; hbm_read_kernel "
+                     "(fp8_w8a8_block_amd/csrc/hbm_probe.hip) reading 1 GiB, and 45.1 MB "
+                     "(one decode weight) rotating over 8 buffers")}
 
 
 def cpu_model():

@@ -1,4 +1,5 @@
-"""Build libfp8w8a8.so in-tree with hipcc for gfx950.
+"""Build libfp8w8a8.so (and bench.py's libhbmprobe.so) in-tree with hipcc
+for gfx950.
 
     python -m fp8_w8a8_block_amd.build        # or fp8_w8a8_block_amd.build.build()
 
@@ -21,6 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8w8a8.so")
 SOURCES = ["abi.hip", "quant_kernels.hip", "gemm_kernels.hip", "kv_kernels.hip"]
+PROBE_SOURCE = "hbm_probe.hip"                 # bench.py's HBM read reference
+PROBE_LIB = os.path.join(PKG, "libhbmprobe.so")
 ARCH = "gfx950"
 
 
@@ -69,6 +72,14 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # bench.py's HBM read reference, a library of its own
+    probe = _compile(PROBE_SOURCE, verbose)
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, probe,
+                        "-Wl,-rpath,/opt/rocm/lib"], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -93,7 +93,8 @@ def test_decode_line_fields():
     assert abs(roof["achieved"] - b / (us * 1e-6) / 1e9) < 1e-6 * roof["achieved"]
     assert "traffic" in roof
     ref = line["hbm_reference"]
-    assert ref["copy"]["GB/s"] > 0 and ref["read_sum"]["GB/s"] > 0
+    assert ref["copy"]["GB/s"] > 0 and ref["read_stream"]["GB/s"] > 0
+    assert ref["read_stream_decode_bytes"]["bytes_read"] == 11008 * 4096
     cpu = line["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1
     assert isinstance(cpu["sample"], str) and cpu["unit"] == "GB/s"
