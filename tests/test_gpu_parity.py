@@ -525,6 +525,46 @@ def test_linear_split_k_matches_two_calls():
     check_out(got, oracle_gemm(a, w), "linear split K")
 
 
+def test_split_k_replays_from_a_hip_graph():
+    # the split launch clears its words with a kernel, not a memset node, so
+    # it can be captured: three replays of a captured fp8_block_gemm and of a
+    # captured fp8_linear, with eager work and synchronizations between them,
+    # each equal to the eager result bit for bit
+    M, N, K = 512, 1024, 4096
+    rng = np.random.default_rng(83)
+    a = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    wq, ws = fp8.quant_weight_block(dev_bf16(w))
+    x = dev_bf16(a)
+    aq, as_ = fp8.quant_act(x)
+    gws = torch.empty(fp8.workspace_bytes(fp8._lib.OP_GEMM, M, N, K, "block"), dtype=torch.uint8,
+                      device="cuda")
+    lws = torch.empty(fp8.workspace_bytes(fp8._lib.OP_LINEAR, M, N, K, "block"), dtype=torch.uint8,
+                      device="cuda")
+    assert gws.numel() > 0
+    want_g = host_u16(fp8.block_gemm(aq, as_, wq, ws, workspace=gws))
+    want_l = host_u16(fp8.linear(x, wq, ws, workspace=lws))
+    out_g = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    out_l = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fp8.block_gemm(aq, as_, wq, ws, out=out_g, workspace=gws)
+        fp8.linear(x, wq, ws, out=out_l, workspace=lws)
+    for r in range(3):
+        out_g.zero_()
+        out_l.zero_()
+        gws.fill_(0xA5)                       # garbage in the words between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u16(out_g), want_g), r
+        assert np.array_equal(host_u16(out_l), want_l), r
+        fp8.block_gemm(aq, as_, wq, ws, workspace=gws)      # eager work between replays
+    check_out(want_l, oracle_gemm(a, w), "split K from a graph")
+
+
 @pytest.mark.parametrize("mode", ["tensor", "row"])
 def test_gemm_constant_scales_do_not_split(mode):
     # scales constant along K keep the unsplit kernel: no workspace, and a
