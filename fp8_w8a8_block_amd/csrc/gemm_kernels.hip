@@ -857,6 +857,10 @@ __device__ __forceinline__ bool grouped_tile(const int64_t* __restrict__ offsets
 // NW = 8: 256 x 256 tiles, two waves per SIMD.  NW = 4: 256 x 128 tiles, one
 // wave per SIMD, for grids that would otherwise leave CUs idle (the same
 // 128 x 64 wave tile, so the K loop is the same schedule).
+// nsplit = 1 (NW = 8, E = 0): two workgroups per tile, consecutive after the
+// XCD remap, each over half of the K blocks (the launch passes that half as
+// KB); the generated epilogue hands the first half's fp32 accumulators to the
+// second through the workspace ws (SplitLayout) before the bf16 stores.
 // E > 0: the grouped (MoE) form, chosen at run time so the K loop's code
 // exists once per variant.  The grid enumerates the tiles of all experts
 // (rounded up to a multiple of 8; workgroups past the last tile exit at
