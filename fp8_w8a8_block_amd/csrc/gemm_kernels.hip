@@ -18,6 +18,7 @@
 // w[n, k] whatever order the unit walks the 32 bytes in.  The 16x16 fp32
 // result sits in lane n + 16 (m / 4), register m % 4.
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -679,35 +680,38 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Prefill shape, hand-scheduled: the same tile, wave grid and MFMA roles as
-// gemm_prefill_kernel, with the K loop as generated gfx950 assembly
-// (prefill_asm.inc, written by gen_prefill_asm.py).  C++ below only sets up
-// the operands; the assembly issues every copy, fragment read, MFMA and
-// scale fold in a fixed order:
+// Prefill shape, hand-scheduled: the MFMA roles of gemm_prefill_kernel
+// (its 256 x 256 tile and wave grid, or 128 x 256 tiles of 8 waves of
+// 64 x 64), with the K loop as generated gfx950 assembly (prefill_asm.inc,
+// written by gen_prefill_asm.py).  C++ below only sets up the operands; the
+// assembly issues every copy, fragment read, MFMA and scale fold in a fixed
+// order:
 //
-//  * one K step = 32 MFMA slots; the activation fragment of slot group j + 1
-//    is read while group j multiplies, each partial product is folded four
-//    MFMAs after it was issued (six partial-product slots in rotation);
+//  * one K step = 4 MFMA slots per activation fragment of the wave (32 for
+//    128 x 64 wave tiles, 16 for 64 x 64); the activation fragment of slot
+//    group j + 1 is read while group j multiplies, each partial product is
+//    folded four MFMAs after it was issued (six partial-product slots in
+//    rotation);
 //  * the weight fragments are double-buffered in registers, so the next
 //    step's fragments are read as soon as its copy is visible, and the
 //    barrier that releases a stage sits before the last fragment group's
 //    MFMAs rather than after them (the matrix unit does not drain on it);
 //  * the copies of K block kb + S (and its activation scales) go out one per
 //    slot after that barrier, S the number of LDS stages (2 for 256 x 256
-//    tiles, 3 for 256 x 128 tiles, whose one wave per SIMD has no other wave
-//    to cover a wait: its copies get two K steps to land); each barrier waits
-//    only for the copies of the next block.  The block index is clamped to
-//    the last block, so no copy ever addresses past the operands' K extent.
+//    tiles, 3 for 128 x 256 tiles, whose copies get two K steps to land);
+//    each barrier waits only for the copies of the next block.  The block
+//    index is clamped to the last block, so no copy ever addresses past the
+//    operands' K extent.
 //
 // Activation scales travel by DMA too, four K blocks at a time: every fourth
-// step waves 0-3 copy sa[m0 + row, g .. g + 3] (16 bytes per row, one row per
-// lane) into one of two group buffers; per step each lane gathers its eight
-// fragments' scales with two ds_read2 pairs.  (One float per row per step
-// costs a cache line per row per step.)  The K loop therefore runs on K
+// step waves 0 .. tm / 64 - 1 copy sa[m0 + row, g .. g + 3] (16 bytes per
+// row, one row per lane) into one of two group buffers; per step each lane
+// gathers its fragments' scales with ds_read2 pairs.  (One float per row per
+// step costs a cache line per row per step.)  The K loop therefore runs on K
 // blocks in multiples of four (K % 512 == 0); other K take the C++ kernel.
-// The two weight blocks' scales for every K block are copied into an LDS
+// The tile's weight blocks' scales for every K block are copied into an LDS
 // table once.  Per step the lane
-// multiplies its eight activation scales by its weight block's scale
+// multiplies its activation scales by its weight block's scale
 // (fp32), then folds acc = fma(scale, partial, acc): the arithmetic of the
 // C++ kernel, operation for operation.
 //
@@ -719,42 +723,52 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(
 // past N skips its stores.
 #include "prefill_asm.inc"
 
-// LDS layout of each workgroup shape (the offsets of gen_prefill_asm.py):
-// `stages` activation stages (256 rows x 128 B), `stages` weight stages
-// (32 NW rows x 128 B), two activation-scale group buffers, the weight-scale
-// table.  The 256 x 256 shape has two stages, the 256 x 128 shape three.
+// Workgroup shapes of the generated loop, by tag (gen_prefill_asm.py): nw
+// waves on a tm x tn tile, tn / 64 waves along N, each wave 64 columns and
+// tm / (nw / (tn / 64)) rows; its LDS layout: `stages` activation stages (tm
+// rows x 128 B), `stages` weight stages (tn rows x 128 B), two
+// activation-scale group buffers, the weight-scale table.
+//   W8:  256 x 256, 8 waves of 128 x 64, two stages;
+//   W8M: 128 x 256, 8 waves of 64 x 64, three stages (and the split-K form).
 constexpr int kPfKbGroup = FP8_PREFILL_KB_GROUP;   // K blocks per activation-scale copy
 constexpr int kPrefillMaxKB = 256;            // weight-scale table rows: K <= 32768
 
-template <int NW>
-struct PfLayout;
-template <>
-struct PfLayout<8> {
-  static constexpr int stages = FP8_PREFILL_W8_STAGES, unit = FP8_PREFILL_W8_LDS_UNIT,
-                       bytes = FP8_PREFILL_W8_LDS_BYTES,
-                       w = FP8_PREFILL_W8_LDS_W, sa = FP8_PREFILL_W8_LDS_SA,
-                       sa_group = FP8_PREFILL_W8_LDS_SA_GROUP_BYTES, sw = FP8_PREFILL_W8_LDS_SW;
-};
-template <>
-struct PfLayout<4> {
-  static constexpr int stages = FP8_PREFILL_W4_STAGES, unit = FP8_PREFILL_W4_LDS_UNIT,
-                       bytes = FP8_PREFILL_W4_LDS_BYTES,
-                       w = FP8_PREFILL_W4_LDS_W, sa = FP8_PREFILL_W4_LDS_SA,
-                       sa_group = FP8_PREFILL_W4_LDS_SA_GROUP_BYTES, sw = FP8_PREFILL_W4_LDS_SW;
-};
+#define FP8_PF_SHAPE(TAG)                                                                       \
+  struct Pf##TAG {                                                                              \
+    static constexpr int nw = FP8_PREFILL_##TAG##_WAVES, tm = FP8_PREFILL_##TAG##_TM,           \
+                         tn = FP8_PREFILL_##TAG##_TN, stages = FP8_PREFILL_##TAG##_STAGES,      \
+                         unit = FP8_PREFILL_##TAG##_LDS_UNIT,                                   \
+                         bytes = FP8_PREFILL_##TAG##_LDS_BYTES, w = FP8_PREFILL_##TAG##_LDS_W,  \
+                         sa = FP8_PREFILL_##TAG##_LDS_SA,                                       \
+                         sa_group = FP8_PREFILL_##TAG##_LDS_SA_GROUP_BYTES,                     \
+                         sw = FP8_PREFILL_##TAG##_LDS_SW;                                       \
+  };
+FP8_PF_SHAPE(W8)
+FP8_PF_SHAPE(W8M)
+#undef FP8_PF_SHAPE
 
-template <int NW>
+template <class L>
 constexpr bool pf_layout_ok() {
-  using L = PfLayout<NW>;
   return L::unit >= 1024 && L::unit % 16 == 0 &&           // 8 rows of 128 B, then a pad
-         L::w == L::stages * (kPM / 8) * L::unit &&         // activation stages first
-         L::sa == L::w + L::stages * 4 * NW * L::unit &&    // then the weight stages
-         L::sa_group == kPM * kPfKbGroup * 4 &&             // a group: 4 K blocks of 256 rows
+         L::tn % 64 == 0 && L::nw % (L::tn / 64) == 0 &&    // whole 64-column waves
+         L::tm % (16 * (L::nw / (L::tn / 64))) == 0 &&      // whole 16-row fragments
+         L::nw % 2 == 0 && L::nw >= 4 &&                    // copy rows, scale-table waves
+         L::tm % 64 == 0 && L::tm / 64 <= L::nw &&          // activation-scale copy waves
+         L::tn <= 32 * L::nw && L::tn <= 256 &&             // weight-scale table rows
+         L::w == L::stages * (L::tm / 8) * L::unit &&       // activation stages first
+         L::sa == L::w + L::stages * (L::tn / 8) * L::unit &&   // then the weight stages
+         L::sa_group == L::tm * kPfKbGroup * 4 &&           // a group: 4 K blocks of tm rows
          L::sw == L::sa + 2 * L::sa_group &&                // two groups, then the table
          L::bytes == L::sw + 2 * kPrefillMaxKB * 4 &&       // which ends the layout
          L::bytes <= 160 * 1024;                            // LDS of one CU
 }
-static_assert(pf_layout_ok<8>() && pf_layout_ok<4>(), "LDS layout of the generated loop");
+static_assert(pf_layout_ok<PfW8>() && pf_layout_ok<PfW8M>(), "LDS layout of the generated loop");
+
+// tiles of an M x N output in shape S
+template <class S>
+int64_t pf_tiles(int64_t M, int64_t N) {
+  return ((M + S::tm - 1) / S::tm) * ((N + S::tn - 1) / S::tn);
+}
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -767,14 +781,16 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // distinct groups and the read takes one pass instead of two.
 __device__ __forceinline__ int swz_pair(int r) { return 2 * ((r >> 1) & 3); }
 
-// Workspace of a split-K launch (two workgroups per 256 x 256 tile, each
+// Workspace of a split-K launch (two W8M workgroups per 128 x 256 tile, each
 // half of the K blocks), one slot per (tile, wave): four 32-bit words at
 // 16 slot (arrival counter, ready flag, the XCD records of the two halves),
 // zeroed before every launch, and from kSplitWordsBytes on the fp32
-// partials, 32 KiB per slot (128 x 64 accumulators, lane-major), which need
+// partials, 16 KiB per slot (64 x 64 accumulators, lane-major), which need
 // no initial value.
-constexpr uint32_t kSplitPartBytes = 128 * 64 * 4;
-constexpr uint32_t kSplitWordsBytes = 65536;
+constexpr uint32_t kSplitPartBytes = FP8_PREFILL_SPLIT_PART_BYTES;
+constexpr uint32_t kSplitWordsBytes = FP8_PREFILL_SPLIT_WORDS_BYTES;
+static_assert(kSplitPartBytes == PfW8M::tm / (PfW8M::nw / (PfW8M::tn / 64)) * 64 * 4,
+              "one wave's accumulators per slot");
 constexpr uint64_t kSplitMaxSlots = kSplitWordsBytes / 16;
 struct SplitLayout {
   uint64_t slots, total;
@@ -804,14 +820,14 @@ __device__ __forceinline__ v4i pf_desc(const void* base, int64_t bytes) {
 }
 
 // Grouped (MoE) tile lookup.  Tile numbers run expert by expert; within
-// expert e (t_e = ceil(rows_e / 256) M tiles) the M tile varies fastest, so
+// expert e (t_e = ceil(rows_e / rows) M tiles) the M tile varies fastest, so
 // the t_e tiles that read one weight slab (same expert, same N tile) are
 // neighbours: they land on one XCD together and share the slab in its L2.
 // Every wave runs the same scan (64 experts per step, a wave prefix sum of
 // t_e * tiles_n), so the result is uniform over the workgroup.  Returns
 // false when the tile lies past the last expert's tiles.
 __device__ __forceinline__ bool grouped_tile(const int64_t* __restrict__ offsets, int E,
-                                             int64_t M, int tile, int tiles_n, int& e_out,
+                                             int64_t M, int tile, int tiles_n, int rows, int& e_out,
                                              int& tm_out, int& tn_out, int64_t& lo_out,
                                              int64_t& hi_out) {
   const int lane = threadIdx.x & 63;
@@ -823,7 +839,7 @@ __device__ __forceinline__ bool grouped_tile(const int64_t* __restrict__ offsets
     if (e < E) {
       int64_t lo, hi;
       expert_rows(offsets, e, M, lo, hi);
-      t = (hi - lo + kPM - 1) / kPM * tiles_n;
+      t = (hi - lo + rows - 1) / rows * tiles_n;
     }
     long long incl = t;
 #pragma unroll
@@ -839,7 +855,7 @@ __device__ __forceinline__ bool grouped_tile(const int64_t* __restrict__ offsets
       const long long local = (long long)tile - base - __shfl(excl, l, 64);
       int64_t lo, hi;
       expert_rows(offsets, e_own, M, lo, hi);
-      const long long te = (hi - lo + kPM - 1) / kPM;
+      const long long te = (hi - lo + rows - 1) / rows;
       // 0 <= local < te * tiles_n by construction; checked anyway
       if (te <= 0 || local < 0 || local >= te * tiles_n) return false;
       e_out = e_own;
@@ -854,10 +870,9 @@ __device__ __forceinline__ bool grouped_tile(const int64_t* __restrict__ offsets
   return false;
 }
 
-// NW = 8: 256 x 256 tiles, two waves per SIMD.  NW = 4: 256 x 128 tiles, one
-// wave per SIMD, for grids that would otherwise leave CUs idle (the same
-// 128 x 64 wave tile, so the K loop is the same schedule).
-// nsplit = 1 (NW = 8, E = 0): two workgroups per tile, consecutive after the
+// S: the workgroup shape (PfW8, PfW8M).  W8 is the default; W8M serves grids
+// whose 256 x 256 tiles would leave CUs idle.
+// nsplit = 1 (W8M only, E = 0): two workgroups per tile, consecutive after the
 // XCD remap, each over half of the K blocks (the launch passes that half as
 // KB); the generated epilogue hands the first half's fp32 accumulators to the
 // second through the workspace ws (SplitLayout) before the bf16 stores.
@@ -869,16 +884,19 @@ __device__ __forceinline__ bool grouped_tile(const int64_t* __restrict__ offsets
 // output rebased to the expert's first row, M = its row count) and weight
 // (w + e * w_es, sw + e * sw_es).  The range-checked descriptors end at the expert's last row,
 // so the next expert's rows are neither read nor written.
-template <bool KCONST, int NW>
-__global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
+template <bool KCONST, class S>
+__global__ __launch_bounds__(64 * S::nw) void gemm_prefill_asm_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ sa, int64_t ld_sa,
     const uint8_t* __restrict__ w, int64_t ld_w, const float* __restrict__ sw, int64_t ld_sw,
     uint16_t* __restrict__ out, int64_t ld_out, int64_t M_all, int N, int KB, int tiles_m,
     int tiles_n, const int64_t* __restrict__ offsets, int E, int64_t w_es, int64_t sw_es,
     uint8_t* __restrict__ ws, int nsplit) {
-  constexpr int kTN = 32 * NW;                 // tile width (weight rows)
-  constexpr int kWN = NW / 2;                  // waves along N
-  using Lay = PfLayout<NW>;
+  using Lay = S;
+  constexpr int NW = S::nw;
+  constexpr int kTM = S::tm, kTN = S::tn;      // tile height and width
+  constexpr int kWN = kTN / kPWN;              // waves along N
+  constexpr int kWR = kTM / (NW / kWN);        // rows per wave
+  constexpr int kSaWaves = kTM / 64;           // waves that copy activation scales
   __shared__ __attribute__((aligned(1024))) uint8_t lds[Lay::bytes];
 
   const int tid = threadIdx.x;
@@ -897,7 +915,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
     const int lin = (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8);
     int e;
     int64_t lo, hi;
-    if (!grouped_tile(offsets, E, M_all, lin, tiles_n, e, tm, tn, lo, hi)) return;
+    if (!grouped_tile(offsets, E, M_all, lin, tiles_n, kTM, e, tm, tn, lo, hi)) return;
     a += lo * ld_a;
     sa += lo * ld_sa;
     out += lo * ld_out;
@@ -932,7 +950,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
     sa += kb0;
     sw += kb0;
   }
-  const int64_t m0 = (int64_t)tm * kPM;
+  const int64_t m0 = (int64_t)tm * kTM;
   const int64_t n0 = (int64_t)tn * kTN;
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
@@ -957,19 +975,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   // (2 kg) ^ swz_pair(r16) and the next one
   const int p0 = (2 * kg) ^ swz_pair(r16);
   const int rd_row = (r16 >> 3) * Lay::unit + (r16 & 7) * 128 + p0 * 16;
-  const uint32_t rdA = lds0 + (uint32_t)(wm * (kPWM / 8) * Lay::unit + rd_row);
+  const uint32_t rdA = lds0 + (uint32_t)(wm * (kWR / 8) * Lay::unit + rd_row);
   const uint32_t rdW = lds0 + (uint32_t)(Lay::w + wn * (kPWN / 8) * Lay::unit + rd_row);
 
-  // activation scales, copied by waves 0..3 every four K blocks: lane
-  // r = 64 wave + lane copies the 16 bytes sa[m0 + r, g .. g + 3] to 16 r of a
-  // group buffer, so the scale of tile row r for block g + u sits at
-  // 16 r + 4 u; lane r16 of wave row wm reads rows 128 wm + 16 j + r16,
-  // fragments 0-3 from scL and 4-7 from scH (1 KiB above)
-  const uint32_t offSa = (uint32_t)((64 * (wave & 3) + lane) * ld_sa * 4);
+  // activation scales, copied by waves 0 .. tm / 64 - 1 every four K blocks:
+  // lane r = 64 wave + lane copies the 16 bytes sa[m0 + r, g .. g + 3] to 16 r
+  // of a group buffer, so the scale of tile row r for block g + u sits at
+  // 16 r + 4 u; lane r16 of wave row wm reads rows kWR wm + 16 j + r16,
+  // fragments 0-3 from scL and 4-7 (if the wave has them) from scH (1 KiB
+  // above)
+  const uint32_t offSa = (uint32_t)((64 * (wave % kSaWaves) + lane) * ld_sa * 4);
   const v4i dSa = pf_desc(sa + m0 * ld_sa, (((int64_t)M - m0) * ld_sa - kb0) * 4);
-  const int wsa = pf_uni(wave < 4 ? 1 : 0);
-  const uint32_t sam0 = pf_uni(lds0 + (uint32_t)(Lay::sa + (wave & 3) * 1024));
-  const uint32_t scL0 = lds0 + (uint32_t)(Lay::sa + (wm * kPWM + r16) * 16);
+  const int wsa = pf_uni(wave < kSaWaves ? 1 : 0);
+  const uint32_t sam0 = pf_uni(lds0 + (uint32_t)(Lay::sa + (wave % kSaWaves) * 1024));
+  const uint32_t scL0 = lds0 + (uint32_t)(Lay::sa + (wm * kWR + r16) * 16);
   const uint32_t scH0 = scL0 + 4u * 16u * 16u;
   const uint32_t scL1 = scL0 + (uint32_t)Lay::sa_group;
   const uint32_t scH1 = scH0 + (uint32_t)Lay::sa_group;
@@ -990,10 +1009,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   const int colok = pf_uni((n0 + wn * kPWN < N) ? 1 : 0);
   // scales constant along K: row scale sa[m * ld_sa], column scale
   // sw[n * ld_sw] (strides 0: one scale each); the lane's rows are
-  // 128 wm + 16 j + r16, its columns 64 wn + 16 i + 4 kg + r
+  // kWR wm + 16 j + r16, its columns 64 wn + 16 i + 4 kg + r
   const v4i dSaR = pf_desc(sa + m0 * ld_sa, (((int64_t)M - m0 - 1) * ld_sa + 1) * 4);
   const v4i dSwR = pf_desc(sw + n0 * ld_sw, (((int64_t)N - n0 - 1) * ld_sw + 1) * 4);
-  const uint32_t offSaR = (uint32_t)((wm * kPWM + r16) * ld_sa * 4);
+  const uint32_t offSaR = (uint32_t)((wm * kWR + r16) * ld_sa * 4);
   const uint32_t offSwR = (uint32_t)((wn * kPWN + 4 * kg) * ld_sw * 4);
   const uint32_t sjA = pf_uni((uint32_t)(16 * ld_sa * 4));
   const uint32_t siW = pf_uni((uint32_t)(16 * ld_sw * 4));
@@ -1027,29 +1046,31 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_asm_kernel(
   [offSa] "v"(offSa), [scL0] "v"(scL0), [scH0] "v"(scH0), [scL1] "v"(scL1), [scH1] "v"(scH1),  \
       [offSw] "v"(offSw), [dSa] "s"(dSa), [dSw] "s"(dSw), [sam0] "s"(sam0), [wsa] "s"(wsa),     \
       [swm0] "s"(swm0), [kbm4] "s"(kbm4)
-  if (KCONST) {
-    if (NW == 8)
-      asm volatile(FP8_PREFILL_ASM_TENSOR_W8
-                   : [swrd] "+v"(swrd)
-                   : FP8_PF_COMMON_OPERANDS, FP8_PF_KCONST_OPERANDS, FP8_PF_SPLIT_OPERANDS
-                   : FP8_PREFILL_ASM_CLOBBERS);
+  // the shapes with four activation fragments per wave read no scH
+#define FP8_PF_BLOCK4_OPERANDS                                                                  \
+  [offSa] "v"(offSa), [scL0] "v"(scL0), [scL1] "v"(scL1), [offSw] "v"(offSw), [dSa] "s"(dSa),   \
+      [dSw] "s"(dSw), [sam0] "s"(sam0), [wsa] "s"(wsa), [swm0] "s"(swm0), [kbm4] "s"(kbm4)
+#define FP8_PF_ASM(TEXT, ...) \
+  asm volatile(TEXT : [swrd] "+v"(swrd) : __VA_ARGS__ : FP8_PREFILL_ASM_CLOBBERS)
+  if constexpr (KCONST) {
+    if constexpr (std::is_same<S, PfW8>::value)
+      FP8_PF_ASM(FP8_PREFILL_ASM_TENSOR_W8, FP8_PF_COMMON_OPERANDS, FP8_PF_KCONST_OPERANDS);
+    else if constexpr (std::is_same<S, PfW8M>::value)
+      FP8_PF_ASM(FP8_PREFILL_ASM_TENSOR_W8M, FP8_PF_COMMON_OPERANDS, FP8_PF_KCONST_OPERANDS,
+                 FP8_PF_SPLIT_OPERANDS);
     else
-      asm volatile(FP8_PREFILL_ASM_TENSOR_W4
-                   : [swrd] "+v"(swrd)
-                   : FP8_PF_COMMON_OPERANDS, FP8_PF_KCONST_OPERANDS
-                   : FP8_PREFILL_ASM_CLOBBERS);
+      static_assert(sizeof(S) == 0, "no generated loop for this shape");
   } else {
-    if (NW == 8)
-      asm volatile(FP8_PREFILL_ASM_BLOCK_W8
-                   : [swrd] "+v"(swrd)
-                   : FP8_PF_COMMON_OPERANDS, FP8_PF_BLOCK_OPERANDS, FP8_PF_SPLIT_OPERANDS
-                   : FP8_PREFILL_ASM_CLOBBERS);
+    if constexpr (std::is_same<S, PfW8>::value)
+      FP8_PF_ASM(FP8_PREFILL_ASM_BLOCK_W8, FP8_PF_COMMON_OPERANDS, FP8_PF_BLOCK_OPERANDS);
+    else if constexpr (std::is_same<S, PfW8M>::value)
+      FP8_PF_ASM(FP8_PREFILL_ASM_BLOCK_W8M, FP8_PF_COMMON_OPERANDS, FP8_PF_BLOCK4_OPERANDS,
+                 FP8_PF_SPLIT_OPERANDS);
     else
-      asm volatile(FP8_PREFILL_ASM_BLOCK_W4
-                   : [swrd] "+v"(swrd)
-                   : FP8_PF_COMMON_OPERANDS, FP8_PF_BLOCK_OPERANDS
-                   : FP8_PREFILL_ASM_CLOBBERS);
+      static_assert(sizeof(S) == 0, "no generated loop for this shape");
   }
+#undef FP8_PF_ASM
+#undef FP8_PF_BLOCK4_OPERANDS
 #undef FP8_PF_COMMON_OPERANDS
 #undef FP8_PF_KCONST_OPERANDS
 #undef FP8_PF_BLOCK_OPERANDS
@@ -1063,19 +1084,20 @@ __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ 
   if (i < n) p[i] = 0u;
 }
 
-// ws != nullptr: split K in two (NW = 8 only; ws holds SplitLayout's bytes
-// for this grid and KB is even)
-template <int NW>
+// ws != nullptr: split K in two (W8M only; ws holds SplitLayout's bytes for
+// this grid and KB is a multiple of 8)
+template <class S>
 hipError_t launch_prefill_asm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                               const uint8_t* w, int64_t ld_w, const float* sw, int64_t ld_sw,
                               uint16_t* out, int64_t ld_out, int64_t M, int64_t N, int KB,
                               bool kconst, uint8_t* ws, hipStream_t st, bool words_zero = false) {
-  const int tiles_m = (int)((M + kPM - 1) / kPM);
-  const int tiles_n = (int)((N + 32 * NW - 1) / (32 * NW));
+  const int tiles_m = (int)((M + S::tm - 1) / S::tm);
+  const int tiles_n = (int)((N + S::tn - 1) / S::tn);
   const int nsplit = ws ? 1 : 0;
+  if (nsplit && !std::is_same<S, PfW8M>::value) return hipErrorInvalidValue;
   dim3 grid((uint32_t)tiles_m * (uint32_t)tiles_n * (nsplit ? 2u : 1u));
   if (nsplit) {
-    const SplitLayout spl((int64_t)tiles_m * tiles_n, NW);
+    const SplitLayout spl((int64_t)tiles_m * tiles_n, S::nw);
     const int64_t words = (int64_t)spl.slots * 4;
     const int64_t blocks = (words + 255) / 256;
     if (!words_zero)
@@ -1084,30 +1106,30 @@ hipError_t launch_prefill_asm(const uint8_t* a, int64_t ld_a, const float* sa, i
     KB /= 2;
   }
   if (kconst)
-    hipLaunchKernelGGL((gemm_prefill_asm_kernel<true, NW>), grid, dim3(64 * NW), 0, st, a,
+    hipLaunchKernelGGL((gemm_prefill_asm_kernel<true, S>), grid, dim3(64 * S::nw), 0, st, a,
                        ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, (int)N, KB, tiles_m,
                        tiles_n, nullptr, 0, (int64_t)0, (int64_t)0, ws, nsplit);
   else
-    hipLaunchKernelGGL((gemm_prefill_asm_kernel<false, NW>), grid, dim3(64 * NW), 0, st, a,
+    hipLaunchKernelGGL((gemm_prefill_asm_kernel<false, S>), grid, dim3(64 * S::nw), 0, st, a,
                        ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, (int)N, KB, tiles_m,
                        tiles_n, nullptr, 0, (int64_t)0, (int64_t)0, ws, nsplit);
   return hipGetLastError();
 }
 
-// Grouped launch: at most floor((M + 255 E) / 256) M tiles over all experts
-// (each expert's last tile may be partial), times the N tiles, rounded up to
-// a multiple of 8.
-template <int NW>
+// Grouped launch: at most floor((M + (tm - 1) E) / tm) M tiles over all
+// experts (each expert's last tile may be partial), times the N tiles,
+// rounded up to a multiple of 8.
+template <class S>
 hipError_t launch_prefill_asm_grouped(const uint8_t* a, int64_t ld_a, const float* sa,
                                       int64_t ld_sa, const uint8_t* w, int64_t ld_w, int64_t w_es,
                                       const float* sw, int64_t ld_sw, int64_t sw_es,
                                       uint16_t* out, int64_t ld_out, const int64_t* offsets,
                                       int64_t E, int64_t M, int64_t N, int KB, hipStream_t st) {
-  const int64_t tiles_m = (M + (kPM - 1) * E) / kPM;
-  const int64_t tiles_n = (N + 32 * NW - 1) / (32 * NW);
+  const int64_t tiles_m = (M + (S::tm - 1) * E) / S::tm;
+  const int64_t tiles_n = (N + S::tn - 1) / S::tn;
   const int64_t g = (tiles_m * tiles_n + 7) / 8 * 8;
   if (g == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_prefill_asm_kernel<false, NW>), dim3((uint32_t)g), dim3(64 * NW),
+  hipLaunchKernelGGL((gemm_prefill_asm_kernel<false, S>), dim3((uint32_t)g), dim3(64 * S::nw),
                      0, st, a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, (int)N, KB,
                      (int)tiles_m, (int)tiles_n, offsets, (int)E, w_es, sw_es, nullptr, 0);
   return hipGetLastError();
@@ -1290,7 +1312,8 @@ bool linear_decode_supported(int64_t M, int64_t K) {
 // Work-items of the grid a GEMM launches: the decode tile (16 columns per
 // 64 * KSPLIT-thread workgroup) up to 64 rows, otherwise at most the
 // 128 x 128 tile kernel's (256 threads per 128 x 128 tile), which bounds the
-// prefill kernels' 256 x 128 and 256 x 256 tiles too.
+// prefill kernels' 256 x 256 and 128 x 256 tiles too (a split-K launch has
+// at most as many workgroups as the device has CUs).
 uint64_t gemm_items(int64_t M, int64_t N, int64_t K) {
   if (M <= FP8_DECODE_MAX_M && K / 128 <= kDecodeMaxKB)
     return (uint64_t)(N / 16) * 64u * FP8_DECODE_KSPLIT;
@@ -1313,24 +1336,23 @@ bool prefill_asm_ok(int64_t M, int64_t KB, bool kconst, int64_t ld_a, int64_t ld
          ld_sw < kPrefillMaxLd;
 }
 
-// Block-scaled calls whose 256 x 256 tiles would occupy at most half of the
-// CUs: split K in two (each half a multiple of 4 blocks) when a workspace is
-// given, else 256 x 128 tiles.  0 when the call does not split.  (Scales
-// constant along K keep the 256 x 128 tiles: without the per-block fold that
-// loop is as fast as the split one plus its hand-over.)
+// Block-scaled calls whose 128 x 256 tiles would occupy at most half of the
+// CUs: K split in two (each half a multiple of 4 blocks) when a workspace is
+// given.  0 when the call does not split.  (Scales constant along K do not
+// split.)
 size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K, bool kconst) {
   const int64_t KB = K / 128;
   if (kconst || !FP8_PREFILL_ASM || M <= 64 || KB % (2 * kPfKbGroup) != 0 || KB > kPrefillMaxKB)
     return 0;
   if (M <= FP8_DECODE_MAX_M && KB <= kDecodeMaxKB) return 0;
-  const int64_t tiles256 = ((M + kPM - 1) / kPM) * ((N + kPN - 1) / kPN);
-  if (2 * tiles256 > device_cus() || (uint64_t)tiles256 * 8 > kSplitMaxSlots) return 0;
-  return (size_t)SplitLayout(tiles256, 8).total;
+  const int64_t tiles = pf_tiles<PfW8M>(M, N);
+  if (2 * tiles > device_cus() || (uint64_t)tiles * PfW8M::nw > kSplitMaxSlots) return 0;
+  return (size_t)SplitLayout(tiles, PfW8M::nw).total;
 }
 
 uint32_t gemm_split_words(int64_t M, int64_t N, int64_t K, bool kconst) {
   if (!gemm_split_bytes(M, N, K, kconst)) return 0;
-  return (uint32_t)(SplitLayout(((M + kPM - 1) / kPM) * ((N + kPN - 1) / kPN), 8).slots * 4);
+  return (uint32_t)(SplitLayout(pf_tiles<PfW8M>(M, N), PfW8M::nw).slots * 4);
 }
 
 hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
@@ -1362,19 +1384,18 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
   }
   if (prefill_asm_ok(M, KB, kconst, ld_a, ld_sa, ld_w, ld_sw, ld_out)) {
     // 256 x 256 tiles unless they would occupy at most half of the CUs: then
-    // K split in two over twice the workgroups (two waves per SIMD) when the
-    // caller gave the workspace, else 256 x 128 tiles (one wave per SIMD)
-    const int64_t tiles256 = ((M + kPM - 1) / kPM) * ((N + kPN - 1) / kPN);
-    if (2 * tiles256 <= device_cus()) {
-      const size_t need = gemm_split_bytes(M, N, K, kconst);
-      if (need && ws && ws_bytes >= need)
-        return launch_prefill_asm<8>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N,
-                                     KB, kconst, (uint8_t*)ws, st, words_zero);
-      return launch_prefill_asm<4>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N, KB,
-                                   kconst, nullptr, st);
-    }
-    return launch_prefill_asm<8>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N, KB,
-                                 kconst, nullptr, st);
+    // 128 x 256 tiles (three LDS stages), and with block scales K split in
+    // two over twice the workgroups when those too would occupy at most half
+    // of the CUs and the caller gave the workspace
+    if (2 * pf_tiles<PfW8>(M, N) > device_cus())
+      return launch_prefill_asm<PfW8>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N,
+                                      KB, kconst, nullptr, st);
+    const size_t need = gemm_split_bytes(M, N, K, kconst);
+    if (need && ws && ws_bytes >= need)
+      return launch_prefill_asm<PfW8M>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N,
+                                       KB, kconst, (uint8_t*)ws, st, words_zero);
+    return launch_prefill_asm<PfW8M>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N, KB,
+                                     kconst, nullptr, st);
   }
   if (M > 64 && ld_a < kPrefillMaxLd && ld_w < kPrefillMaxLd) {
     const int tiles_m = (int)((M + kPM - 1) / kPM);
@@ -1414,15 +1435,17 @@ static_assert(kGroupedMaxKB <= kDecodeMaxKB, "grouped calls must fit the decode 
 bool grouped_prefill_ok(int64_t M, int64_t E, int64_t N, int64_t K, int64_t ld_a, int64_t ld_w,
                         int64_t ld_sa, int64_t ld_sw, int64_t ld_out) {
   const int64_t KB = K / 128;
-  // grid: at most (M + 255 E) / 256 M tiles times the N tiles of either tile
-  // shape, rounded up to a multiple of 8 workgroups
-  const uint64_t tm = (uint64_t)((M + (kPM - 1) * E) / kPM);
-  const uint64_t g8 = (tm * (uint64_t)((N + 255) / 256) + 7) / 8 * 8 * 512u;
-  const uint64_t g4 = (tm * (uint64_t)(N / 128) + 7) / 8 * 8 * 256u;
+  // grid: at most (M + (tm - 1) E) / tm M tiles times the N tiles of either
+  // tile shape, rounded up to a multiple of 8 workgroups
+  const uint64_t tn = (uint64_t)((N + 255) / 256);
+  const uint64_t t8 = (uint64_t)((M + (PfW8::tm - 1) * E) / PfW8::tm);
+  const uint64_t tM = (uint64_t)((M + (PfW8M::tm - 1) * E) / PfW8M::tm);
+  const uint64_t g8 = (t8 * tn + 7) / 8 * 8 * 512u;
+  const uint64_t gM = (tM * tn + 7) / 8 * 8 * 512u;
   return FP8_PREFILL_ASM && M > FP8_GROUPED_DECODE_MAX_AVG * E && KB % kPfKbGroup == 0 &&
          KB <= kPrefillMaxKB && ld_a < kPrefillMaxLd && ld_w < kPrefillMaxLd &&
          ld_out < kPrefillMaxLd / 2 && ld_sa < kPrefillMaxLd / 4 && ld_sw < kPrefillMaxLd &&
-         g8 < kMaxGridItems && g4 < kMaxGridItems;
+         g8 < kMaxGridItems && gM < kMaxGridItems;
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
@@ -1433,12 +1456,14 @@ hipError_t launch_grouped_gemm(const uint8_t* a, int64_t ld_a, const float* sa, 
   const int64_t w_es = N * ld_w;                   // expert strides
   const int64_t sw_es = (N / 128) * ld_sw;
   if (grouped_prefill_ok(M, E, N, K, ld_a, ld_w, ld_sa, ld_sw, ld_out)) {
-    const int64_t tiles256 = ((M + (kPM - 1) * E) / kPM) * ((N + kPN - 1) / kPN);
-    if (2 * tiles256 <= device_cus())
-      return launch_prefill_asm_grouped<4>(a, ld_a, sa, ld_sa, w, ld_w, w_es, sw, ld_sw, sw_es,
-                                           out, ld_out, offsets, E, M, N, KB, st);
-    return launch_prefill_asm_grouped<8>(a, ld_a, sa, ld_sa, w, ld_w, w_es, sw, ld_sw, sw_es, out,
-                                         ld_out, offsets, E, M, N, KB, st);
+    // 128-row tiles while the experts average at most 512 rows: they waste
+    // fewer padded rows, and their three LDS stages keep more weight bytes
+    // in flight
+    if (M <= 512 * E)
+      return launch_prefill_asm_grouped<PfW8M>(a, ld_a, sa, ld_sa, w, ld_w, w_es, sw, ld_sw,
+                                               sw_es, out, ld_out, offsets, E, M, N, KB, st);
+    return launch_prefill_asm_grouped<PfW8>(a, ld_a, sa, ld_sa, w, ld_w, w_es, sw, ld_sw, sw_es,
+                                            out, ld_out, offsets, E, M, N, KB, st);
   }
   constexpr int KSPLIT = FP8_DECODE_KSPLIT, KBW = FP8_DECODE_KBW;
   dim3 grid((uint32_t)(N / 16), (uint32_t)E);

@@ -36,12 +36,19 @@ OUT = os.path.join(HERE, "prefill_asm.inc")
 # below and static_asserts the ones it derives itself.
 KB_GROUP = 4                      # K blocks per activation-scale copy
 ROW_PAD = 16                      # bytes after every 8 operand rows
+EP_PITCH = 144                    # bytes per staged output row (64 bf16 + 16 B pad)
+EP_HALF = 64 * EP_PITCH           # one wave's staging area: 64 rows
 
 
 class Layout:
-    """Operand stages (activation 256 rows x 128 B, weight 32 NW rows x 128
-    B, `stages` of each), then the two activation-scale group buffers
-    (4 K blocks x 256 rows each), then the weight-scale table [2][256].
+    """One workgroup shape: nw waves on a tm x tn tile, wn = tn / 64 waves
+    along N and wm = nw / wn along M, so a wave owns tm / wm rows (fa
+    activation fragments) x 64 columns (4 weight fragments) and a K step is
+    4 fa MFMA slots.
+
+    LDS: operand stages (activation tm rows x 128 B, weight tn rows x 128 B,
+    `stages` of each), then the two activation-scale group buffers (4 K
+    blocks x tm rows each), then the weight-scale table [2][256].
 
     Operand rows are stored in units of 8 (1 KiB, what one copy instruction
     writes) followed by ROW_PAD bytes.  A fragment read takes one 16-byte
@@ -51,19 +58,30 @@ class Layout:
     chunks adjacent) cannot separate them, so every read took two cycles; the
     16-byte shift of the second unit puts them on different banks."""
 
-    def __init__(self, nw, stages, pad=ROW_PAD):
-        self.nw, self.stages = nw, stages
+    def __init__(self, nw, stages, tn=None, tm=256, pad=ROW_PAD, tag=""):
+        self.nw, self.stages, self.tag = nw, stages, tag
+        self.tm = tm                      # tile height (activation rows)
+        self.tn = tn or 32 * nw           # tile width (weight rows)
+        self.wn = self.tn // 64           # waves along N
+        self.wm = nw // self.wn           # waves along M
+        self.fa = tm // (16 * self.wm)    # activation fragments per wave
+        self.q = 4 * self.fa              # MFMA slots per K step
+        self.a_units, self.w_units = tm // 8, self.tn // 8
+        self.sa_waves = tm // 64          # waves that copy the activation scales
+        assert self.wm * self.wn == nw and self.fa in (4, 8) and nw % 2 == 0
+        assert self.a_units % nw == 0 and self.w_units % nw == 0 and self.sa_waves <= nw
         self.unit = 1024 + pad            # 8 rows and the pad
         self.frag = 2 * self.unit         # 16 rows: one MFMA operand fragment
-        a_bytes, w_bytes = 32 * self.unit, 4 * nw * self.unit
+        a_bytes, w_bytes = self.a_units * self.unit, self.w_units * self.unit
         self.A = tuple(i * a_bytes for i in range(stages))
         w0 = stages * a_bytes
         self.W = tuple(w0 + i * w_bytes for i in range(stages))
         sa0 = w0 + stages * w_bytes
-        self.SA = (sa0, sa0 + 256 * KB_GROUP * 4)
-        self.SW = self.SA[1] + 256 * KB_GROUP * 4
+        self.SA = (sa0, sa0 + tm * KB_GROUP * 4)
+        self.SW = self.SA[1] + tm * KB_GROUP * 4
         self.bytes = self.SW + 2 * 256 * 4
         assert self.bytes <= 160 * 1024
+        assert nw * EP_HALF <= self.bytes     # the epilogue's staging areas
 
 
 # ---------------------------------------------------------------------------
@@ -78,43 +96,53 @@ SPREV = 240                       # scale of fragment 7 of the previous K step
 SWN = 241                         # weight scale of the next K step
 VCOPY = (242, 243)                # per-copy source offsets (alternating)
 RDA_HI = 244                      # fragment-read base 64 KiB above rdA (a third stage)
+# the same for rdW, in shapes with four activation fragments per wave (their
+# accumulators leave acc(0, 4) .. unused)
+RDW_HI = ACC0 + (0 * 8 + 4) * 4
 NUM_FIXED_VGPR = 245
 DS_OFFSET_MAX = 65535             # ds_read immediate offsets are 16-bit
 # scalar scratch
 S_KB, S_DK, S_DK4, S_T, S_R = "s84", "s85", "s86", "s87", "s88"
 CLOBBER_SGPR = (84, 89)
 
-# Workgroup shapes: NW waves in a 2 x (NW / 2) grid of 128 x 64 wave tiles,
-# so the workgroup tile is 256 x (32 NW).  Copy t of wave w carries tile rows
-# 8 (w + NW t) .. + 7; the activation tile takes 32 / NW copies per wave, the
-# weight tile 4.  The 256 x 256 shape (two waves per SIMD) fills the LDS with
-# two stages; the 256 x 128 shape (one wave per SIMD, nothing to cover a wave
-# that waits) has room for three, so its copies run two K steps ahead.
-SHAPES = (8, 4)
-STAGES = {8: 2, 4: 3}
+# Workgroup shapes, by tag: (waves, LDS stages, tile width, tile height).
+# Copy t of wave w carries tile rows 8 (w + nw t) .. + 7; the activation tile
+# takes tm / (8 nw) copies per wave, the weight tile tn / (8 nw).
+#   W8:  256 x 256, 8 waves of 128 x 64 (two per SIMD), two stages (the LDS
+#        holds no third);
+#   W8M: 128 x 256, 8 waves of 64 x 64 (two per SIMD), three stages, so the
+#        copies run two K steps ahead; it alone carries the split-K hand-over.
+SHAPES = {"W8": (8, 2, 256, 256), "W8M": (8, 3, 256, 128)}
+SPLIT_SHAPE = "W8M"
 
 
-def copies(nw):
+def layout(tag):
+    return Layout(*SHAPES[tag], tag=tag)
+
+
+def copies(lay):
     """Order of one K block's copies: activation and weight interleaved."""
-    na = 32 // nw
+    na, nb = lay.a_units // lay.nw, lay.w_units // lay.nw
     a = [("A", t) for t in range(na)]
-    w = [("W", t) for t in range(4)]
+    w = [("W", t) for t in range(nb)]
     out = []
-    for k in range(max(na, 4)):
+    for k in range(max(na, nb)):
         if k < na:
             out.append(a[k])
-        if k < 4:
+        if k < nb:
             out.append(w[k])
     return out
 
 # partial-product slot of MFMA q (0..31) of a K step: every 5 consecutive
 # MFMAs (cyclically, across K steps) use distinct slots, so a partial is
 # folded 4 MFMAs after it was issued and its slot is free again by then.
-SLOT_SEQ = [0, 1, 2, 3, 4] * 5 + [0, 5, 1, 2, 3, 4, 5]
+SLOT_SEQS = {32: [0, 1, 2, 3, 4] * 5 + [0, 5, 1, 2, 3, 4, 5],
+             16: [0, 1, 2, 3, 4] * 3 + [5]}
 FOLD_LAG = 4
-assert len(SLOT_SEQ) == 32
-_cyc = SLOT_SEQ + SLOT_SEQ[:FOLD_LAG]
-assert all(len(set(_cyc[q:q + FOLD_LAG + 1])) == FOLD_LAG + 1 for q in range(32))
+for _q, _seq in SLOT_SEQS.items():
+    assert len(_seq) == _q
+    _cyc = _seq + _seq[:FOLD_LAG]
+    assert all(len(set(_cyc[q:q + FOLD_LAG + 1])) == FOLD_LAG + 1 for q in range(_q))
 
 LGKM_MAX = 15                     # 4-bit counter on gfx9
 
@@ -135,8 +163,8 @@ def fa(buf):
     return FA0 + 8 * buf
 
 
-def pslot(q):
-    return P0 + 4 * SLOT_SEQ[q % 32]
+def pslot(q, nq=32):
+    return P0 + 4 * SLOT_SEQS[nq][q % nq]
 
 
 class Program:
@@ -195,11 +223,11 @@ class Program:
 
 # ---------------------------------------------------------------------------
 def frag_read(prog, key, dst, base, off):
-    """The two 16-byte reads of a fragment at base operand + off; activation
-    offsets past the 16-bit field go through RDA_HI (rdA + 64 KiB)."""
+    """The two 16-byte reads of a fragment at base operand + off; offsets
+    past the 16-bit field go through RDA_HI / RDW_HI (64 KiB above the base)."""
     reg = f"%[{base}]"
-    if base == "rdA" and off + 16 > DS_OFFSET_MAX:
-        reg, off = f"v{RDA_HI}", off - 65536
+    if off + 16 > DS_OFFSET_MAX:
+        reg, off = f"v{RDA_HI if base == 'rdA' else RDW_HI}", off - 65536
     assert 0 <= off and off + 16 <= DS_OFFSET_MAX
     prog.lds(key, f"ds_read_b128 {vr(dst, 4)}, {reg} offset:{off}",
              f"ds_read_b128 {vr(dst + 4, 4)}, {reg} offset:{off + 16}")
@@ -226,9 +254,9 @@ _label = [0]
 
 
 def dma_scale_group(prog, lay, buf, tag, first=None):
-    """Waves 0-3: each lane copies the 16 bytes sa[row, g .. g + 3] of its row,
-    g = min(first K block of the next group, KB - 4) (or `first`), into group
-    buffer `buf`.  Waves 4-7 branch around."""
+    """Waves 0 .. tm / 64 - 1: each lane copies the 16 bytes sa[row, g .. g + 3]
+    of its row, g = min(first K block of the next group, KB - 4) (or `first`),
+    into group buffer `buf`.  The other waves branch around."""
     _label[0] += 1
     skip = f"fp8pf_sa_{tag}_{_label[0]}_%="
     prog.emit("s_cmp_eq_u32 %[wsa], 0", f"s_cbranch_scc1 {skip}")
@@ -241,7 +269,7 @@ def dma_scale_group(prog, lay, buf, tag, first=None):
         prog.emit(f"s_mov_b32 {S_T}, {4 * first}")
     prog.emit(f"s_add_u32 m0, %[sam0], {lay.SA[buf] - lay.SA[0]}", "s_nop 0")
     prog.vm(("sa", buf), f"buffer_load_dwordx4 %[offSa], %[dSa], {S_T} offen lds",
-            every_wave=lay.nw == 4)
+            every_wave=lay.sa_waves == lay.nw)
     prog.emit(f"{skip}:")
 
 
@@ -249,7 +277,7 @@ def scale_reads(prog, key, kb_next, half):
     """ds_read2 of the lane's activation scales of K block kb_next: fragments
     4 half .. 4 half + 3 into SC0 + 4 half .. .  Entry (tile row r, block u)
     of a group buffer sits at 16 r + 4 u; the lane's rows are
-    128 wm + 16 j + r16, so fragment j is 64 j + u dwords above the lane's
+    16 fa wm + 16 j + r16, so fragment j is 64 j + u dwords above the lane's
     base (one base per buffer and half: the read2 offsets are 8-bit), and the
     16 rows of a fragment fall on 16 distinct banks."""
     buf = (kb_next // KB_GROUP) % 2
@@ -284,7 +312,7 @@ def gen_loop(block, lay):
     steps (loop_period) as chunks of KB_GROUP steps, taken from the middle of
     a longer run so that the counter waits see the operations the previous
     steps left in flight."""
-    nw, S = lay.nw, lay.stages
+    nw, S, Q, FA = lay.nw, lay.stages, lay.q, lay.fa
     prog = Program()
     sched = {}
 
@@ -293,15 +321,17 @@ def gen_loop(block, lay):
 
     P = loop_period(S)
     nsteps = 3 * P
-    bar_slot = 26
+    # the barrier follows the last fragment read of the step's stage; the
+    # next step's first reads follow it, five slots before their first use
+    bar_slot = Q - 6
     for st in range(nsteps):
         p = st % S                   # LDS stage of this step
         q = (st + 1) % S             # LDS stage of the next step
         rq = (st + 1) % 2            # weight-fragment register set of the next step
-        base = 32 * st
-        # activation fragment j (1..7) of this step: after the last MFMA of
-        # fragment j - 2 (same buffer), five slots before its first use
-        for j in range(1, 8):
+        base = Q * st
+        # activation fragment j (1 .. FA - 1) of this step: after the last
+        # MFMA of fragment j - 2 (same buffer), five slots before its first use
+        for j in range(1, FA):
             at(base + 4 * j - 5, lambda st=st, j=j, p=p: frag_read(
                 prog, ("fa", st, j), fa(j % 2), "rdA", lay.A[p] - lay.A[0] + j * lay.frag))
 
@@ -313,21 +343,29 @@ def gen_loop(block, lay):
             prog.emit("s_barrier")
             set_dk(prog, S)
         at(base + bar_slot, barrier)
-        at(base + 27, lambda st=st, q=q, rq=rq: (
+        at(base + Q - 5, lambda st=st, q=q, rq=rq: (
             frag_read(prog, ("fa", st + 1, 0), fa(0), "rdA", lay.A[q] - lay.A[0]),
             frag_read(prog, ("fw", st + 1, 0), fw(rq, 0), "rdW", lay.W[q] - lay.W[0])))
         for i in (1, 2, 3):
-            at(base + 27 + i, lambda st=st, q=q, rq=rq, i=i: frag_read(
+            at(base + Q - 5 + i, lambda st=st, q=q, rq=rq, i=i: frag_read(
                 prog, ("fw", st + 1, i), fw(rq, i), "rdW", lay.W[q] - lay.W[0] + lay.frag * i))
         if block:
+            # the next step's scales overwrite SC0 .. SC0 + 3.  With eight
+            # fragments the folds still to come in this step read SC0 + 6, so
+            # the reads go out at slot Q - 4; with four they read SC0 + 2
+            # until slot Q - 1, so the reads wait for it (and the multiply
+            # moves one slot later to give them the time).
+            sc_slot, mul_slot = (Q - 4, 2) if FA == 8 else (Q - 1, 3)
+
             def scales_lo(st=st):
-                prog.emit(f"v_mov_b32 v{SPREV}, v{SC0 + 7}")
+                prog.emit(f"v_mov_b32 v{SPREV}, v{SC0 + FA - 1}")
                 scale_reads(prog, ("salo", st + 1), st + 1, 0)
                 prog.emit("v_add_u32 %[swrd], 4, %[swrd]")
                 prog.lds(("swn", st + 1), f"ds_read_b32 v{SWN}, %[swrd]")
-            at(base + 28, scales_lo)
-            # the second half at slot 4 of the next step (needed from slot 20)
-            at(base + 32 + 4, lambda st=st: scale_reads(prog, ("sahi", st + 1), st + 1, 1))
+            at(base + sc_slot, scales_lo)
+            if FA == 8:
+                # the second half at slot 4 of the next step (needed from slot 20)
+                at(base + Q + 4, lambda st=st: scale_reads(prog, ("sahi", st + 1), st + 1, 1))
 
             def mul_lo(st=st):
                 prog.need(("salo", st), ("swn", st))
@@ -338,53 +376,67 @@ def gen_loop(block, lay):
                 prog.need(("sahi", st), ("swn", st))
                 for r in range(4, 8):
                     prog.emit(f"v_mul_f32_e32 v{SC0 + r}, v{SWN}, v{SC0 + r}")
-            at(base + 2, mul_lo)
-            at(base + 12, mul_hi)
+            at(base + mul_slot, mul_lo)
+            if FA == 8:
+                at(base + 12, mul_hi)
             if st % KB_GROUP == 1:
                 nbuf = (st // KB_GROUP + 1) % 2
-                at(base + 30, lambda nbuf=nbuf: dma_scale_group(prog, lay, nbuf, f"blk{nw}"))
+                at(base + Q - 2, lambda nbuf=nbuf: dma_scale_group(prog, lay, nbuf, f"blk{lay.tag}"))
         # copies of K block kb + S into this step's stage (released at the
-        # barrier), one per slot from slot 28 on
-        for k, (op, t) in enumerate(copies(nw)):
-            at(base + 28 + k, lambda st=st, op=op, t=t, p=p, k=k: dma_copy(
+        # barrier), one per slot from slot Q - 4 on
+        for k, (op, t) in enumerate(copies(lay)):
+            at(base + Q - 4 + k, lambda st=st, op=op, t=t, p=p, k=k: dma_copy(
                 prog, lay, op, t, p, k, st + S))
 
-    total = 32 * nsteps
+    total = Q * nsteps
     marks = {}
     for gs in range(total):
-        st, qq = divmod(gs, 32)
+        st, qq = divmod(gs, Q)
         if qq == 0:
             marks[st] = len(prog.lines)
         j, i = divmod(qq, 4)
         c = st % 2
         prog.need(("fa", st, j), ("fw", st, i))
         if block:
-            prog.emit(f"v_mfma_f32_16x16x128_f8f6f4 {vr(pslot(qq), 4)}, {vr(fw(c, i), 8)}, "
+            prog.emit(f"v_mfma_f32_16x16x128_f8f6f4 {vr(pslot(qq, Q), 4)}, {vr(fw(c, i), 8)}, "
                       f"{vr(fa(j % 2), 8)}, 0")
             pq = qq - FOLD_LAG
-            jj, ii = divmod(pq % 32, 4)
+            jj, ii = divmod(pq % Q, 4)
             s = f"v{SC0 + jj}" if pq >= 0 else f"v{SPREV}"
             for r in range(4):
-                prog.emit(f"v_fmac_f32_e32 v{acc(ii, jj, r)}, {s}, v{pslot(pq) + r}")
+                prog.emit(f"v_fmac_f32_e32 v{acc(ii, jj, r)}, {s}, v{pslot(pq, Q) + r}")
         else:
             prog.emit(f"v_mfma_f32_16x16x128_f8f6f4 {vr(acc(i, j), 4)}, {vr(fw(c, i), 8)}, "
                       f"{vr(fa(j % 2), 8)}, {vr(acc(i, j), 4)}")
         for fn in sched.get(gs, []):
             fn()
-        if qq == 31:
+        if qq == Q - 1:
             prog.emit(f"s_add_u32 {S_KB}, {S_KB}, 1")
     marks[nsteps] = len(prog.lines)
     chunks = [prog.lines[marks[P + c]:marks[P + c + KB_GROUP]] for c in range(0, P, KB_GROUP)]
     return chunks, prog.max_out
 
 
-def slot_words():
+def slot_words(lay):
     """s88 = byte offset of this wave's slot words: %[wsPart] is
-    SPLIT_WORDS_BYTES + 32 KiB slot, the words sit at 16 slot."""
-    return [f"s_sub_u32 s88, %[wsPart], {SPLIT_WORDS_BYTES}", "s_lshr_b32 s88, s88, 11"]
+    SPLIT_WORDS_BYTES + slot * split_part_bytes(lay), the words sit at
+    16 slot."""
+    shift = (split_part_bytes(lay) // 16).bit_length() - 1
+    return [f"s_sub_u32 s88, %[wsPart], {SPLIT_WORDS_BYTES}", f"s_lshr_b32 s88, s88, {shift}"]
 
 
-def gen_split_record(tag):
+def split_quads(lay):
+    """The wave's accumulator quads (4 VGPRs, acc(i, j)) in the order of its
+    partial in the workspace: quad k of lane l at 1024 k + 16 l."""
+    return [8 * i + j for i in range(4) for j in range(lay.fa)]
+
+
+def split_part_bytes(lay):
+    """One wave's fp32 partial: 16 fa x 64 accumulators."""
+    return len(split_quads(lay)) * 1024
+
+
+def gen_split_record(tag, lay):
     """Split-K launches: one lane records this half's XCD (+1) in the wave's
     workspace slot, word 2 + half, for the partner wave's hand-over."""
     skip = f"fp8pf_norec_{tag}_%="
@@ -396,7 +448,7 @@ def gen_split_record(tag):
             XCC_READ,
             "s_add_u32 s86, s86, 1",
             f"v_mov_b32 v{P0}, s86",
-            *slot_words(),
+            *slot_words(lay),
             "s_mov_b64 s[84:85], exec",
             "s_mov_b64 exec, 1",
             f"buffer_store_dword v{P0}, v{P0 + 1}, %[dWs], s88 offen sc0 sc1",
@@ -410,11 +462,15 @@ def gen_prologue(block, lay, tag="", split=False):
     # an SGPR written by the VALU need wait states
     L = ["s_nop 7"]
     if split:
-        L += gen_split_record(tag)
-    for k in range(128):
-        L.append(f"v_mov_b32 v{ACC0 + k}, 0")
-    if lay.A[-1] - lay.A[0] + 8 * lay.frag > DS_OFFSET_MAX:
+        L += gen_split_record(tag, lay)
+    for i in range(4):
+        for j in range(lay.fa):
+            L += [f"v_mov_b32 v{acc(i, j, r)}, 0" for r in range(4)]
+    if lay.A[-1] - lay.A[0] + lay.fa * lay.frag > DS_OFFSET_MAX:
         L.append(f"v_add_u32 v{RDA_HI}, 0x10000, %[rdA]")
+    if lay.W[-1] - lay.W[0] + 4 * lay.frag > DS_OFFSET_MAX:
+        assert lay.fa == 4
+        L.append(f"v_add_u32 v{RDW_HI}, 0x10000, %[rdW]")
     if block:
         for k in range(24):
             L.append(f"v_mov_b32 v{P0 + k}, 0")
@@ -425,11 +481,11 @@ def gen_prologue(block, lay, tag="", split=False):
     prog = Program()
     prog.emit(*L)
     if block:
-        dma_scale_group(prog, lay, 0, f"pro{nw}", first=0)
+        dma_scale_group(prog, lay, 0, f"pro{lay.tag}", first=0)
     # K blocks 0 .. S - 1 into stages 0 .. S - 1
     for stage in range(S):
         set_dk(prog, stage)
-        for k, (op, t) in enumerate(copies(nw)):
+        for k, (op, t) in enumerate(copies(lay)):
             dma_copy(prog, lay, op, t, stage, k, stage)
     prog.vm_wait_for(("blk", 0))
     prog.emit("s_barrier")
@@ -441,30 +497,29 @@ def gen_prologue(block, lay, tag="", split=False):
     if block:
         prog.wait_all_lds()
         scale_reads(prog, None, 0, 0)
-        scale_reads(prog, None, 0, 1)
+        if lay.fa == 8:
+            scale_reads(prog, None, 0, 1)
         prog.emit(f"ds_read_b32 v{SWN}, %[swrd]")
     prog.emit("s_waitcnt lgkmcnt(0)")
     return prog.lines
 
 
-EP_PITCH = 144                    # bytes per staged output row (64 bf16 + 16 B pad)
-EP_HALF = 64 * EP_PITCH           # one wave's staging area: 64 rows
 
 
-SPLIT_PART_BYTES = 128 * 64 * 4    # one wave's fp32 accumulators
 SPLIT_WORDS_BYTES = 65536         # the slots' words come first: 16 bytes per slot
 XCC_READ = "s_getreg_b32 s86, hwreg(HW_REG_XCC_ID, 0, 4)"   # this wave's XCD
 SPIN_LIMIT = 1 << 22              # polls of the partner's flag (64-clock sleeps) before giving up
 
 
-def gen_split_exchange(tag):
+def gen_split_exchange(tag, lay):
     """Hand-over of a tile split in two along K (two workgroups, each half of
     the K blocks; a wave of one and the same wave of the other own the same
-    128 x 64 outputs and share one workspace slot: four words -- arrival
-    counter, flag, and the XCD records of the two halves -- and a 32 KiB fp32
-    partial).  Each wave bumps the counter (one lane, an atomic add that
-    returns the old count).  The first to arrive stores its accumulators
-    (lane-major: quad q of lane l at 1024 q + 16 l) and then writes the flag;
+    (16 fa) x 64 outputs and share one workspace slot: four words -- arrival
+    counter, flag, and the XCD records of the two halves -- and a fp32
+    partial of 1 KiB per accumulator quad).  Each wave bumps the counter (one
+    lane, an atomic add that returns the old count).  The first to arrive
+    stores its accumulators (lane-major: quad k of lane l at 1024 k + 16 l,
+    split_quads) and then writes the flag;
     the second polls the flag, adds the stored partial to its own and goes on
     to the bf16 stores.  fp32 addition commutes, so the sum does not depend
     on which of the two arrives first.
@@ -487,7 +542,9 @@ def gen_split_exchange(tag):
     tmp = FW0                          # 64 VGPRs: 16 quads of the partner's partial
     lab = {n: f"fp8pf_{n}_{tag}_%=" for n in
            ("done", "last", "spin", "ready", "nosplit", "fl2", "fflag", "l2h0", "l2h1", "addh0", "addh1")}
-    words = slot_words()
+    words = slot_words(lay)
+    quads = split_quads(lay)
+    halves = [quads[h:h + 16] for h in range(0, len(quads), 16)]
 
     def one_lane(*ops):
         return ["s_mov_b64 exec, 1", *ops, "s_waitcnt vmcnt(0)", "s_mov_b64 exec, s[84:85]", "s_nop 1",
@@ -495,20 +552,20 @@ def gen_split_exchange(tag):
 
     def stores(bits):
         L = []
-        for q in range(32):
-            if q % 4 == 0:
-                L.append(f"s_add_u32 s88, %[wsPart], {4096 * (q // 4)}")
+        for k, q in enumerate(quads):
+            if k % 4 == 0:
+                L.append(f"s_add_u32 s88, %[wsPart], {4096 * (k // 4)}")
             L.append(f"buffer_store_dwordx4 {vr(ACC0 + 4 * q, 4)}, v{vl16}, %[dWs], s88 offen "
-                     f"offset:{1024 * (q % 4)}{bits}")
+                     f"offset:{1024 * (k % 4)}{bits}")
         return L
 
     def loads(h, bits):
         L = []
-        for q in range(16 * h, 16 * h + 16):
-            if q % 4 == 0:
-                L.append(f"s_add_u32 s88, %[wsPart], {4096 * (q // 4)}")
-            L.append(f"buffer_load_dwordx4 {vr(tmp + 4 * (q % 16), 4)}, v{vl16}, %[dWs], s88 offen "
-                     f"offset:{1024 * (q % 4)}{bits}")
+        for k in range(16 * h, 16 * h + len(halves[h])):
+            if k % 4 == 0:
+                L.append(f"s_add_u32 s88, %[wsPart], {4096 * (k // 4)}")
+            L.append(f"buffer_load_dwordx4 {vr(tmp + 4 * (k % 16), 4)}, v{vl16}, %[dWs], s88 offen "
+                     f"offset:{1024 * (k % 4)}{bits}")
         return L
 
     L = ["s_cmp_eq_u32 %[xinfo], 0", f"s_cbranch_scc1 {lab['nosplit']}",
@@ -552,42 +609,43 @@ def gen_split_exchange(tag):
           "s_cmp_eq_u32 s87, 0",
           f"s_cbranch_scc0 {lab['spin']}",
           f"{lab['ready']}:"]
-    for h in range(2):
+    for h in range(len(halves)):
         L += ["s_cmp_eq_u32 s86, 2", f"s_cbranch_scc1 {lab['l2h%d' % h]}"]
         L += loads(h, " sc0 sc1")
         L += [f"s_branch {lab['addh%d' % h]}", f"{lab['l2h%d' % h]}:"]
         L += loads(h, " sc0")
         L += [f"{lab['addh%d' % h]}:", "s_waitcnt vmcnt(0)"]
-        for q in range(16 * h, 16 * h + 16):
+        for k, q in enumerate(halves[h]):
             for r in range(4):
-                L.append(f"v_add_f32_e32 v{ACC0 + 4 * q + r}, v{ACC0 + 4 * q + r}, v{tmp + 4 * (q % 16) + r}")
+                L.append(f"v_add_f32_e32 v{ACC0 + 4 * q + r}, v{ACC0 + 4 * q + r}, v{tmp + 4 * k + r}")
     L.append(f"{lab['nosplit']}:")
     return L
 
 
-def gen_epilogue(block, tag, nw, split=False):
-    """Fold the last fragment, round to bf16 and store.  The wave's 128 x 64
-    outputs go out in two halves of 64 rows, each staged through LDS so that
+def gen_epilogue(block, tag, lay, split=False):
+    """Fold the last fragment, round to bf16 and store.  The wave's
+    (16 fa) x 64 outputs go out in halves of 64 rows, each staged through LDS so that
     a lane stores 16 contiguous bytes and an instruction covers eight whole
     128-byte row segments (the MFMA layout gives a lane 4 adjacent values,
     i.e. 8-byte pieces of 16 rows).  The staged rows are 144 bytes apart:
     16 lanes writing 8 bytes each to 16 rows hit 16 distinct bank pairs."""
     # the last MFMAs' results are read by the VALU below: drain first
+    nw, FA, Q = lay.nw, lay.fa, lay.q
     L = ["s_nop 7", "s_nop 7"]
     if block:
-        # fold fragment 7 of the last K step
-        for q in range(28, 32):
+        # fold the last fragment of the last K step
+        for q in range(Q - 4, Q):
             jj, ii = divmod(q, 4)
             for r in range(4):
-                L.append(f"v_fmac_f32_e32 v{acc(ii, jj, r)}, v{SPREV}, v{pslot(q) + r}")
+                L.append(f"v_fmac_f32_e32 v{acc(ii, jj, r)}, v{SPREV}, v{pslot(q, Q) + r}")
     else:
         # scales constant along K: out[m, n] = (sa[m] * sw[n]) * acc.  The
-        # lane's 8 row scales (rows 128 wm + 16 j + r16) and 16 column scales
-        # (columns 64 wn + 16 i + 4 kg + r) come through range-checked
+        # lane's FA row scales (rows 16 FA wm + 16 j + r16) and 16 column
+        # scales (columns 64 wn + 16 i + 4 kg + r) come through range-checked
         # descriptors (strides 0 give the per-tensor case).
         sa_r, sw_r, vt = P0, P0 + 8, (SC0, SC0 + 1)
         n = 0
-        for j in range(8):
+        for j in range(FA):
             t = vt[n % 2]
             n += 1
             if j == 0:
@@ -607,7 +665,7 @@ def gen_epilogue(block, tag, nw, split=False):
                 L.append(f"buffer_load_dword v{sw_r + 4 * i + r}, v{t}, %[dSwR], 0 offen")
         L.append("s_waitcnt vmcnt(0)")
         for i in range(4):
-            for j in range(8):
+            for j in range(FA):
                 for r in range(4):
                     L += [f"v_mul_f32_e32 v{vt[0]}, v{sa_r + j}, v{sw_r + 4 * i + r}",
                           f"v_mul_f32_e32 v{acc(i, j, r)}, v{vt[0]}, v{acc(i, j, r)}"]
@@ -615,7 +673,7 @@ def gen_epilogue(block, tag, nw, split=False):
     L += ["s_waitcnt vmcnt(0) lgkmcnt(0)", "s_barrier",
           "s_cmp_eq_u32 %[colok], 0", f"s_cbranch_scc1 fp8pf_done_{tag}_%="]
     if split:
-        L += gen_split_exchange(tag)
+        L += gen_split_exchange(tag, lay)
     vl, vt, vk, vw, vrd, vo = (FW0 + k for k in range(6))
     buf = FW0 + 8                      # 32 VGPRs of read-back data
     s_reg, s_ldo2, s_uni, s_step = S_KB, S_DK, S_DK4, S_T
@@ -636,12 +694,12 @@ def gen_epilogue(block, tag, nw, split=False):
           f"v_and_b32 v{vk}, 7, v{vl}",
           f"v_lshl_add_u32 v{vrd}, v{vk}, 4, v{vt}",
           f"v_add_u32 v{vrd}, {s_reg}, v{vrd}",
-          # store offset: row 128 wm + lane / 8, columns 64 wn + 8 (lane % 8)
+          # store offset: row 16 FA wm + lane / 8, columns 64 wn + 8 (lane % 8)
           f"s_lshr_b32 {s_ldo2}, %[ldo16], 4",
-          f"s_lshr_b32 {s_uni}, %[wave], {(nw // 2).bit_length() - 1}",
-          f"s_mul_i32 {s_uni}, {s_uni}, 128",
+          f"s_lshr_b32 {s_uni}, %[wave], {lay.wn.bit_length() - 1}",
+          f"s_mul_i32 {s_uni}, {s_uni}, {16 * FA}",
           f"s_mul_i32 {s_uni}, {s_uni}, {s_ldo2}",
-          f"s_and_b32 {s_step}, %[wave], {nw // 2 - 1}",
+          f"s_and_b32 {s_step}, %[wave], {lay.wn - 1}",
           f"s_lshl_b32 {s_step}, {s_step}, 7",
           f"s_add_u32 {s_uni}, {s_uni}, {s_step}",
           f"v_lshrrev_b32 v{vt}, 3, v{vl}",
@@ -651,7 +709,7 @@ def gen_epilogue(block, tag, nw, split=False):
           f"s_lshr_b32 {s_step}, %[ldo16], 1"]          # 8 rows
     tmp = P0
     n = 0
-    for h in range(2):
+    for h in range(FA // 4):
         for j in range(4 * h, 4 * h + 4):
             for i in range(4):
                 t = tmp + 2 * (n % 12)
@@ -673,13 +731,15 @@ def gen_epilogue(block, tag, nw, split=False):
     return L
 
 
-def gen(block, nw=8):
-    """KB must be a positive multiple of KB_GROUP (the caller checks)."""
-    tag = ("blk" if block else "pt") + str(nw)
+def gen(block, shape="W8"):
+    """KB must be a positive multiple of KB_GROUP (the caller checks).  Only
+    SPLIT_SHAPE carries the split-K hand-over."""
+    tag = ("blk" if block else "pt") + shape
     _label[0] = 0
-    lay = Layout(nw, STAGES[nw])
+    lay = layout(shape)
+    split = shape == SPLIT_SHAPE
     chunks, max_out = gen_loop(block, lay)
-    L = gen_prologue(block, lay, tag, split=nw == 8)
+    L = gen_prologue(block, lay, tag, split=split)
     L.append(f"fp8pf_loop_{tag}_%=:")
     for c, chunk in enumerate(chunks):
         L += chunk
@@ -687,7 +747,7 @@ def gen(block, nw=8):
             L += [f"s_cmp_eq_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_tail_{tag}_%="]
     L += [f"s_cmp_lt_u32 {S_KB}, %[kb]", f"s_cbranch_scc1 fp8pf_loop_{tag}_%="]
     L.append(f"fp8pf_tail_{tag}_%=:")
-    L += gen_epilogue(block, tag, nw, split=nw == 8)
+    L += gen_epilogue(block, tag, lay, split=split)
     return L, max_out
 
 
@@ -699,9 +759,9 @@ def main(path=OUT):
     out = ["// Generated by gen_prefill_asm.py; do not edit by hand.",
            "// K loop of gemm_prefill_kernel as gfx950 assembly (see that file).",
            "#pragma once", ""]
-    for nw, block in [(nw, b) for nw in SHAPES for b in (True, False)]:
-        lines, max_out = gen(block, nw)
-        name = ("FP8_PREFILL_ASM_BLOCK" if block else "FP8_PREFILL_ASM_TENSOR") + f"_W{nw}"
+    for shape, block in [(t, b) for t in SHAPES for b in (True, False)]:
+        lines, max_out = gen(block, shape)
+        name = ("FP8_PREFILL_ASM_BLOCK" if block else "FP8_PREFILL_ASM_TENSOR") + f"_{shape}"
         out.append(f"// {len(lines)} lines; at most {max_out} LDS reads in flight")
         out.append(f"#define {name} \\")
         out.append(c_string(lines).replace("\n", " \\\n"))
@@ -711,15 +771,20 @@ def main(path=OUT):
     out.append(f'#define FP8_PREFILL_ASM_CLOBBERS {vg}, {sg}, "m0", "scc", "memory"')
     out.append(f"#define FP8_PREFILL_ASM_FIXED_VGPRS {NUM_FIXED_VGPR}")
     out.append(f"#define FP8_PREFILL_KB_GROUP {KB_GROUP}")
-    for nw in SHAPES:
-        lay = Layout(nw, STAGES[nw])
-        out.append(f"#define FP8_PREFILL_W{nw}_STAGES {lay.stages}")
-        out.append(f"#define FP8_PREFILL_W{nw}_LDS_UNIT {lay.unit}")
-        out.append(f"#define FP8_PREFILL_W{nw}_LDS_BYTES {lay.bytes}")
-        out.append(f"#define FP8_PREFILL_W{nw}_LDS_W {lay.W[0]}")
-        out.append(f"#define FP8_PREFILL_W{nw}_LDS_SA {lay.SA[0]}")
-        out.append(f"#define FP8_PREFILL_W{nw}_LDS_SA_GROUP_BYTES {lay.SA[1] - lay.SA[0]}")
-        out.append(f"#define FP8_PREFILL_W{nw}_LDS_SW {lay.SW}")
+    out.append(f"#define FP8_PREFILL_SPLIT_WORDS_BYTES {SPLIT_WORDS_BYTES}")
+    out.append(f"#define FP8_PREFILL_SPLIT_PART_BYTES {split_part_bytes(layout(SPLIT_SHAPE))}")
+    for shape in SHAPES:
+        lay = layout(shape)
+        out.append(f"#define FP8_PREFILL_{shape}_WAVES {lay.nw}")
+        out.append(f"#define FP8_PREFILL_{shape}_TM {lay.tm}")
+        out.append(f"#define FP8_PREFILL_{shape}_TN {lay.tn}")
+        out.append(f"#define FP8_PREFILL_{shape}_STAGES {lay.stages}")
+        out.append(f"#define FP8_PREFILL_{shape}_LDS_UNIT {lay.unit}")
+        out.append(f"#define FP8_PREFILL_{shape}_LDS_BYTES {lay.bytes}")
+        out.append(f"#define FP8_PREFILL_{shape}_LDS_W {lay.W[0]}")
+        out.append(f"#define FP8_PREFILL_{shape}_LDS_SA {lay.SA[0]}")
+        out.append(f"#define FP8_PREFILL_{shape}_LDS_SA_GROUP_BYTES {lay.SA[1] - lay.SA[0]}")
+        out.append(f"#define FP8_PREFILL_{shape}_LDS_SW {lay.SW}")
     text = "\n".join(out) + "\n"
     if path is None:
         return text

@@ -49,21 +49,24 @@ def test_workspace_bytes():
     assert _lib.workspace_bytes(_lib.OP_QUANT_ACT, 16, 0, 4096, "tensor") == 4096
     assert _lib.workspace_bytes(_lib.OP_QUANT_WEIGHT, 4096, 0, 4096, "tensor") == 4096
     assert _lib.workspace_bytes(_lib.OP_GEMM, 16, 256, 4096, "tensor") == 0
-    # split K: 2048 x 4096 has 128 tiles of 256 x 256 (at most half of 256
+    # split K: 1024 x 4096 has 128 tiles of 128 x 256 (at most half of 256
     # CUs) and K / 128 = 112 is a multiple of 8: 64 KiB of slot words, then a
-    # 32 KiB fp32 partial per (tile, wave); block scales only
-    assert _lib.workspace_bytes(_lib.OP_GEMM, 2048, 4096, 14336, "block") == 65536 + 128 * 8 * 32768
-    assert _lib.workspace_bytes(_lib.OP_GEMM, 2048, 4096, 14336, "tensor") == 0
-    assert _lib.workspace_bytes(_lib.OP_GEMM, 2048, 4096, 14336, "row") == 0
-    assert _lib.workspace_bytes(_lib.OP_GEMM, 4096, 4096, 4096, "block") == 0    # 256 tiles
-    assert _lib.workspace_bytes(_lib.OP_GEMM, 2048, 4096, 14208, "block") == 0   # 111 K blocks
+    # 16 KiB fp32 partial per (tile, wave); block scales only
+    assert _lib.workspace_bytes(_lib.OP_GEMM, 1024, 4096, 14336, "block") == 65536 + 128 * 8 * 16384
+    assert _lib.workspace_bytes(_lib.OP_GEMM, 1024, 4096, 14336, "tensor") == 0
+    assert _lib.workspace_bytes(_lib.OP_GEMM, 1024, 4096, 14336, "row") == 0
+    assert _lib.workspace_bytes(_lib.OP_GEMM, 2048, 4096, 14336, "block") == 0   # 256 tiles
+    assert _lib.workspace_bytes(_lib.OP_GEMM, 4096, 4096, 4096, "block") == 0    # 256 x 256 tiles
+    assert _lib.workspace_bytes(_lib.OP_GEMM, 1024, 4096, 14208, "block") == 0   # 111 K blocks
     assert _lib.workspace_bytes(_lib.OP_GEMM, 64, 4096, 14336, "block") == 0     # decode shape
-    lin = _lib.workspace_bytes(_lib.OP_LINEAR, 2048, 4096, 14336, "block")
-    assert lin >= 2048 * 14336 + 2048 * 112 * 4 + 65536 + 128 * 8 * 32768
-    # ... and fits fp8_linear_noalloc's scratch (FP8_NOALLOC_SCRATCH_BYTES)
+    lin = _lib.workspace_bytes(_lib.OP_LINEAR, 1024, 4096, 14336, "block")
+    assert lin >= 1024 * 14336 + 1024 * 112 * 4 + 65536 + 128 * 8 * 16384
+    lin2 = _lib.workspace_bytes(_lib.OP_LINEAR, 2048, 4096, 14336, "block")
+    assert lin2 >= 2048 * 14336 + 2048 * 112 * 4
+    # ... and both fit fp8_linear_noalloc's scratch (FP8_NOALLOC_SCRATCH_BYTES)
     with open(os.path.join(ROOT, "include", "fp8w8a8.h")) as f:
         m = re.search(r"#define FP8_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
-    assert lin <= int(m.group(1)) << int(m.group(2))
+    assert max(lin, lin2) <= int(m.group(1)) << int(m.group(2))
     # fused decode linear needs none; other shapes hold codes + scales
     assert _lib.workspace_bytes(_lib.OP_LINEAR, 4, 11008, 4096, "block") == 0
     assert _lib.workspace_bytes(_lib.OP_LINEAR, 16, 11008, 4096, "block") >= 16 * 4096

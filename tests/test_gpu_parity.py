@@ -453,9 +453,9 @@ def test_gemm_large_stratified():
 
 
 # ---------------------------------------------------------------------------
-# split K: shapes whose 256 x 256 tiles would fill at most half of the CUs
-# run as two workgroups per tile, each over half of the K blocks, when the
-# call has the workspace
+# split K: block-scaled shapes whose 128 x 256 tiles would fill at most half
+# of the CUs run as two workgroups per tile, each over half of the K blocks,
+# when the call has the workspace
 
 def _split_case(M, N, K, mode, seed):
     rng = np.random.default_rng(seed)
