@@ -169,7 +169,7 @@ LinearLayout linear_layout(int64_t M, int64_t N, int64_t K, int scale_mode) {
                ? align256(l.partials + (size_t)fp8k::kTensorPartials * sizeof(uint32_t))
                : l.partials;
   // the GEMM's split-K workspace, when the shape splits
-  l.gemm_bytes = fp8k::gemm_split_bytes(M, N, K, scale_mode != FP8_SCALE_BLOCK);
+  l.gemm_bytes = fp8k::gemm_split_bytes(M, N, K);
   l.total = l.gemm + l.gemm_bytes;
   return l;
 }
@@ -211,7 +211,7 @@ size_t fp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int scale_mo
   if (op == FP8_OP_GEMM) {
     if (!mode_ok(scale_mode) || M <= 0 || M >= kMaxDim || !shape_ok_kn(K) || !shape_ok_kn(N))
       return 0;
-    return fp8k::gemm_split_bytes(M, N, K, scale_mode != FP8_SCALE_BLOCK);
+    return fp8k::gemm_split_bytes(M, N, K);
   }
   if ((op == FP8_OP_QUANT_ACT || op == FP8_OP_QUANT_WEIGHT) && scale_mode == FP8_SCALE_TENSOR)
     return (size_t)fp8k::kTensorPartials * sizeof(uint32_t);
@@ -294,7 +294,7 @@ fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, in
   // from every tensor of the call
   size_t need = 0;
   if (workspace && ws_bytes > 0 &&
-      (need = fp8k::gemm_split_bytes(M, N, K, scale_mode != FP8_SCALE_BLOCK)) > 0 &&
+      (need = fp8k::gemm_split_bytes(M, N, K)) > 0 &&
       ws_bytes >= need) {
     if (!aligned(workspace, 16)) return FP8_ERR_ALIGN;
     const int64_t KB = K / 128;
@@ -389,7 +389,7 @@ fp8_status run_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
   hipError_t e;
   // block scales: the quantizer also clears the GEMM's split-K slot words
   const uint32_t nzero =
-      scale_mode == FP8_SCALE_BLOCK && lay.gemm_bytes ? fp8k::gemm_split_words(M, N, K, false) : 0;
+      scale_mode == FP8_SCALE_BLOCK && lay.gemm_bytes ? fp8k::gemm_split_words(M, N, K) : 0;
   if (scale_mode == FP8_SCALE_BLOCK)
     e = fp8k::launch_quant_act_block(x, M, K, ld_x, q, lay.ld_q, sa, KB, s,
                                      (uint32_t*)(ws8 + lay.gemm), nzero);

@@ -1336,13 +1336,13 @@ bool prefill_asm_ok(int64_t M, int64_t KB, bool kconst, int64_t ld_a, int64_t ld
          ld_sw < kPrefillMaxLd;
 }
 
-// Block-scaled calls whose 128 x 256 tiles would occupy at most half of the
-// CUs: K split in two (each half a multiple of 4 blocks) when a workspace is
-// given.  0 when the call does not split.  (Scales constant along K do not
-// split.)
-size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K, bool kconst) {
+// Calls whose 128 x 256 tiles would occupy at most half of the CUs: K split
+// in two (each half a multiple of 4 blocks) when a workspace is given.  0
+// when the call does not split.  Scales constant along K are applied after
+// the hand-over, to the sum of the two halves.
+size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
   const int64_t KB = K / 128;
-  if (kconst || !FP8_PREFILL_ASM || M <= 64 || KB % (2 * kPfKbGroup) != 0 || KB > kPrefillMaxKB)
+  if (!FP8_PREFILL_ASM || M <= 64 || KB % (2 * kPfKbGroup) != 0 || KB > kPrefillMaxKB)
     return 0;
   if (M <= FP8_DECODE_MAX_M && KB <= kDecodeMaxKB) return 0;
   const int64_t tiles = pf_tiles<PfW8M>(M, N);
@@ -1350,8 +1350,8 @@ size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K, bool kconst) {
   return (size_t)SplitLayout(tiles, PfW8M::nw).total;
 }
 
-uint32_t gemm_split_words(int64_t M, int64_t N, int64_t K, bool kconst) {
-  if (!gemm_split_bytes(M, N, K, kconst)) return 0;
+uint32_t gemm_split_words(int64_t M, int64_t N, int64_t K) {
+  if (!gemm_split_bytes(M, N, K)) return 0;
   return (uint32_t)(SplitLayout(pf_tiles<PfW8M>(M, N), PfW8M::nw).slots * 4);
 }
 
@@ -1384,13 +1384,13 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
   }
   if (prefill_asm_ok(M, KB, kconst, ld_a, ld_sa, ld_w, ld_sw, ld_out)) {
     // 256 x 256 tiles unless they would occupy at most half of the CUs: then
-    // 128 x 256 tiles (three LDS stages), and with block scales K split in
-    // two over twice the workgroups when those too would occupy at most half
-    // of the CUs and the caller gave the workspace
+    // 128 x 256 tiles (three LDS stages), with K split in two over twice the
+    // workgroups when those too would occupy at most half of the CUs and the
+    // caller gave the workspace
     if (2 * pf_tiles<PfW8>(M, N) > device_cus())
       return launch_prefill_asm<PfW8>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N,
                                       KB, kconst, nullptr, st);
-    const size_t need = gemm_split_bytes(M, N, K, kconst);
+    const size_t need = gemm_split_bytes(M, N, K);
     if (need && ws && ws_bytes >= need)
       return launch_prefill_asm<PfW8M>(a, ld_a, sa, ld_sa, w, ld_w, sw, ld_sw, out, ld_out, M, N,
                                        KB, kconst, (uint8_t*)ws, st, words_zero);

@@ -139,6 +139,7 @@ def copies(lay):
 SLOT_SEQS = {32: [0, 1, 2, 3, 4] * 5 + [0, 5, 1, 2, 3, 4, 5],
              16: [0, 1, 2, 3, 4] * 3 + [5]}
 FOLD_LAG = 4
+FOLDS_BEFORE = 0                  # of a slot's four folds, how many precede its MFMA
 for _q, _seq in SLOT_SEQS.items():
     assert len(_seq) == _q
     _cyc = _seq + _seq[:FOLD_LAG]
@@ -396,16 +397,20 @@ def gen_loop(block, lay):
             marks[st] = len(prog.lines)
         j, i = divmod(qq, 4)
         c = st % 2
-        prog.need(("fa", st, j), ("fw", st, i))
         if block:
-            prog.emit(f"v_mfma_f32_16x16x128_f8f6f4 {vr(pslot(qq, Q), 4)}, {vr(fw(c, i), 8)}, "
-                      f"{vr(fa(j % 2), 8)}, 0")
             pq = qq - FOLD_LAG
             jj, ii = divmod(pq % Q, 4)
             s = f"v{SC0 + jj}" if pq >= 0 else f"v{SPREV}"
-            for r in range(4):
-                prog.emit(f"v_fmac_f32_e32 v{acc(ii, jj, r)}, {s}, v{pslot(pq, Q) + r}")
+            folds = [f"v_fmac_f32_e32 v{acc(ii, jj, r)}, {s}, v{pslot(pq, Q) + r}" for r in range(4)]
+            nb = FOLDS_BEFORE
+            # folds before the MFMA go out ahead of its fragment wait
+            prog.emit(*folds[:nb])
+            prog.need(("fa", st, j), ("fw", st, i))
+            prog.emit(f"v_mfma_f32_16x16x128_f8f6f4 {vr(pslot(qq, Q), 4)}, {vr(fw(c, i), 8)}, "
+                      f"{vr(fa(j % 2), 8)}, 0")
+            prog.emit(*folds[nb:])
         else:
+            prog.need(("fa", st, j), ("fw", st, i))
             prog.emit(f"v_mfma_f32_16x16x128_f8f6f4 {vr(acc(i, j), 4)}, {vr(fw(c, i), 8)}, "
                       f"{vr(fa(j % 2), 8)}, {vr(acc(i, j), 4)}")
         for fn in sched.get(gs, []):
@@ -622,8 +627,45 @@ def gen_split_exchange(tag, lay):
     return L
 
 
+def gen_const_scales(lay):
+    """Scales constant along K: out[m, n] = (sa[m] * sw[n]) * acc.  The
+    lane's FA row scales (rows 16 FA wm + 16 j + r16) and 16 column scales
+    (columns 64 wn + 16 i + 4 kg + r) come through range-checked descriptors
+    (strides 0 give the per-tensor case)."""
+    FA = lay.fa
+    L = []
+    sa_r, sw_r, vt = P0, P0 + 8, (SC0, SC0 + 1)
+    n = 0
+    for j in range(FA):
+        t = vt[n % 2]
+        n += 1
+        if j == 0:
+            L.append(f"v_mov_b32 v{t}, %[offSaR]")
+        else:
+            L += [f"s_mul_i32 {S_R}, %[sjA], {j}", f"v_add_u32 v{t}, {S_R}, %[offSaR]"]
+        L.append(f"buffer_load_dword v{sa_r + j}, v{t}, %[dSaR], 0 offen")
+    for i in range(4):
+        for r in range(4):
+            t = vt[n % 2]
+            n += 1
+            if i == 0 and r == 0:
+                L.append(f"v_mov_b32 v{t}, %[offSwR]")
+            else:
+                L += [f"s_mul_i32 {S_R}, %[siW], {i}", f"s_mul_i32 {S_T}, %[srW], {r}",
+                      f"s_add_u32 {S_R}, {S_R}, {S_T}", f"v_add_u32 v{t}, {S_R}, %[offSwR]"]
+            L.append(f"buffer_load_dword v{sw_r + 4 * i + r}, v{t}, %[dSwR], 0 offen")
+    L.append("s_waitcnt vmcnt(0)")
+    for i in range(4):
+        for j in range(FA):
+            for r in range(4):
+                L += [f"v_mul_f32_e32 v{vt[0]}, v{sa_r + j}, v{sw_r + 4 * i + r}",
+                      f"v_mul_f32_e32 v{acc(i, j, r)}, v{vt[0]}, v{acc(i, j, r)}"]
+    return L
+
+
 def gen_epilogue(block, tag, lay, split=False):
-    """Fold the last fragment, round to bf16 and store.  The wave's
+    """Fold the last fragment (block scales), hand over a split tile's
+    partial, apply scales constant along K, round to bf16 and store.  The wave's
     (16 fa) x 64 outputs go out in halves of 64 rows, each staged through LDS so that
     a lane stores 16 contiguous bytes and an instruction covers eight whole
     128-byte row segments (the MFMA layout gives a lane 4 adjacent values,
@@ -638,42 +680,15 @@ def gen_epilogue(block, tag, lay, split=False):
             jj, ii = divmod(q, 4)
             for r in range(4):
                 L.append(f"v_fmac_f32_e32 v{acc(ii, jj, r)}, v{SPREV}, v{pslot(q, Q) + r}")
-    else:
-        # scales constant along K: out[m, n] = (sa[m] * sw[n]) * acc.  The
-        # lane's FA row scales (rows 16 FA wm + 16 j + r16) and 16 column
-        # scales (columns 64 wn + 16 i + 4 kg + r) come through range-checked
-        # descriptors (strides 0 give the per-tensor case).
-        sa_r, sw_r, vt = P0, P0 + 8, (SC0, SC0 + 1)
-        n = 0
-        for j in range(FA):
-            t = vt[n % 2]
-            n += 1
-            if j == 0:
-                L.append(f"v_mov_b32 v{t}, %[offSaR]")
-            else:
-                L += [f"s_mul_i32 {S_R}, %[sjA], {j}", f"v_add_u32 v{t}, {S_R}, %[offSaR]"]
-            L.append(f"buffer_load_dword v{sa_r + j}, v{t}, %[dSaR], 0 offen")
-        for i in range(4):
-            for r in range(4):
-                t = vt[n % 2]
-                n += 1
-                if i == 0 and r == 0:
-                    L.append(f"v_mov_b32 v{t}, %[offSwR]")
-                else:
-                    L += [f"s_mul_i32 {S_R}, %[siW], {i}", f"s_mul_i32 {S_T}, %[srW], {r}",
-                          f"s_add_u32 {S_R}, {S_R}, {S_T}", f"v_add_u32 v{t}, {S_R}, %[offSwR]"]
-                L.append(f"buffer_load_dword v{sw_r + 4 * i + r}, v{t}, %[dSwR], 0 offen")
-        L.append("s_waitcnt vmcnt(0)")
-        for i in range(4):
-            for j in range(FA):
-                for r in range(4):
-                    L += [f"v_mul_f32_e32 v{vt[0]}, v{sa_r + j}, v{sw_r + 4 * i + r}",
-                          f"v_mul_f32_e32 v{acc(i, j, r)}, v{vt[0]}, v{acc(i, j, r)}"]
     # every wave's copies and fragment reads are done: the stages are free
     L += ["s_waitcnt vmcnt(0) lgkmcnt(0)", "s_barrier",
           "s_cmp_eq_u32 %[colok], 0", f"s_cbranch_scc1 fp8pf_done_{tag}_%="]
     if split:
         L += gen_split_exchange(tag, lay)
+    if not block:
+        # after the hand-over, so a split tile's two halves are scaled once
+        # as their sum, like an unsplit tile's accumulator
+        L += gen_const_scales(lay)
     vl, vt, vk, vw, vrd, vo = (FW0 + k for k in range(6))
     buf = FW0 + 8                      # 32 VGPRs of read-back data
     s_reg, s_ldo2, s_uni, s_step = S_KB, S_DK, S_DK4, S_T

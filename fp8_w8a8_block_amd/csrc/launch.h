@@ -58,10 +58,10 @@ hipError_t launch_gemm(const uint8_t* a, int64_t ld_a, const float* sa, int64_t 
                        bool kconst, void* ws, size_t ws_bytes, hipStream_t st,
                        bool words_zero = false);
 // Workspace bytes of launch_gemm's split-K path on the current device for
-// this shape and scale form (0: the call never splits), and how many 32-bit
+// this shape, any scale form (0: the call never splits), and how many 32-bit
 // words at its start must be 0 when the launch begins.
-size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K, bool kconst);
-uint32_t gemm_split_words(int64_t M, int64_t N, int64_t K, bool kconst);
+size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K);
+uint32_t gemm_split_words(int64_t M, int64_t N, int64_t K);
 
 // Fused decode linear: dynamic 1x128 quantization of x inside the decode GEMM
 // (block scales).  Dispatched for 1 <= M <= 4 and K <= 16384; the result is

@@ -94,9 +94,9 @@ const char* fp8_status_str(fp8_status s);
  * passed as (rows = M argument, K); FP8_OP_LINEAR takes (M, N, K) and needs
  * none on its fused path.  FP8_OP_GEMM takes (M, N, K): the bytes with which
  * fp8_block_gemm splits K in two on the current device (nonzero only for
- * FP8_SCALE_BLOCK shapes with M > 64 whose 128 x 256 output tiles would
- * occupy at most half of the device's compute units and whose K is a
- * multiple of 1024); the call works without them. */
+ * shapes with M > 64 whose 128 x 256 output tiles would occupy at most half
+ * of the device's compute units and whose K is a multiple of 1024, in every
+ * scale mode); the call works without them. */
 size_t fp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int scale_mode);
 
 /* fp8_quant_act -- dynamic activation quantization.

@@ -51,10 +51,9 @@ def test_workspace_bytes():
     assert _lib.workspace_bytes(_lib.OP_GEMM, 16, 256, 4096, "tensor") == 0
     # split K: 1024 x 4096 has 128 tiles of 128 x 256 (at most half of 256
     # CUs) and K / 128 = 112 is a multiple of 8: 64 KiB of slot words, then a
-    # 16 KiB fp32 partial per (tile, wave); block scales only
-    assert _lib.workspace_bytes(_lib.OP_GEMM, 1024, 4096, 14336, "block") == 65536 + 128 * 8 * 16384
-    assert _lib.workspace_bytes(_lib.OP_GEMM, 1024, 4096, 14336, "tensor") == 0
-    assert _lib.workspace_bytes(_lib.OP_GEMM, 1024, 4096, 14336, "row") == 0
+    # 16 KiB fp32 partial per (tile, wave); every scale form
+    for mode in ("block", "tensor", "row"):
+        assert _lib.workspace_bytes(_lib.OP_GEMM, 1024, 4096, 14336, mode) == 65536 + 128 * 8 * 16384
     assert _lib.workspace_bytes(_lib.OP_GEMM, 2048, 4096, 14336, "block") == 0   # 256 tiles
     assert _lib.workspace_bytes(_lib.OP_GEMM, 4096, 4096, 4096, "block") == 0    # 256 x 256 tiles
     assert _lib.workspace_bytes(_lib.OP_GEMM, 1024, 4096, 14208, "block") == 0   # 111 K blocks

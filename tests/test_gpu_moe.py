@@ -4,8 +4,9 @@ fp8_grouped_gemm through the C ABI against oracle.moe.grouped_gemm_ref on
 the same FP8 operands (quantized by the oracle on the host), through the
 tolerance gate of the block GEMM: both kernel paths (the decode tile for a
 few rows per expert, including its 16-row chunk loop, and the grouped
-hand-scheduled kernel in both tile shapes), empty experts, rows in no
-expert's range left untouched, ragged segments crossing 256-row tiles,
+hand-scheduled kernel in both tile shapes: 128-row tiles while experts
+average at most 512 rows, 256-row tiles above), empty experts, rows in no
+expert's range left untouched, ragged segments crossing 128- and 256-row tiles,
 clamped offsets, an activation stride past 32-bit buffer offsets, bit-identity with fp8_block_gemm for a single expert, and
 sampled rows of the two full MoE workloads.
 """
@@ -80,7 +81,7 @@ CASES = {
     "decode_small": (5, 256, 512, [3, 0, 17, 1, 40], 2, 3),
     "decode_chunks": (8, 256, 512, [100, 0, 0, 0, 0, 0, 0, 5], 0, 0),
     "decode_k640": (2, 256, 640, [150, 90], 1, 0),
-    "asm_w4": (3, 512, 1024, [300, 0, 530], 5, 7),
+    "asm_128row": (3, 512, 1024, [300, 0, 530], 5, 7),
     "asm_k512_edges": (4, 384, 512, [255, 256, 257, 1], 0, 2),
     # the longest K of a grouped call (128 K blocks) on both paths
     "decode_k16384": (3, 256, 16384, [5, 20, 0], 1, 0),
@@ -100,7 +101,8 @@ def test_grouped_small(case):
 
 
 def test_grouped_w8_sampled():
-    # enough tiles for the 256 x 256 shape; rows sampled at segment and tile edges
+    # 3000 rows per expert on average: the 256 x 256 shape; rows sampled at
+    # segment and tile edges
     E, N, K = 4, 1920, 1024                   # N % 256 = 128: a half-empty last tile
     sizes = [4000, 3000, 0, 5000]
     lead, tail = 3, 4

@@ -453,9 +453,10 @@ def test_gemm_large_stratified():
 
 
 # ---------------------------------------------------------------------------
-# split K: block-scaled shapes whose 128 x 256 tiles would fill at most half
-# of the CUs run as two workgroups per tile, each over half of the K blocks,
-# when the call has the workspace
+# split K: shapes whose 128 x 256 tiles would fill at most half of the CUs
+# run as two workgroups per tile, each over half of the K blocks, when the
+# call has the workspace (scales constant along K are applied to the sum of
+# the two halves)
 
 def _split_case(M, N, K, mode, seed):
     rng = np.random.default_rng(seed)
@@ -477,7 +478,9 @@ def _oracle_mode(a, w, mode):
 
 @pytest.mark.parametrize("M,N,K,mode", [(512, 512, 2048, "block"), (300, 384, 1024, "block"),
                                         (65, 256, 1024, "block"), (257, 1024, 3072, "block"),
-                                        (1000, 640, 2048, "block"), (1024, 2048, 8192, "block")])
+                                        (1000, 640, 2048, "block"), (1024, 2048, 8192, "block"),
+                                        (512, 512, 2048, "tensor"), (1000, 640, 2048, "tensor"),
+                                        (300, 384, 1024, "row"), (1024, 2048, 8192, "row")])
 def test_gemm_split_k(M, N, K, mode):
     # both forms against the oracle; the split form again with a workspace
     # full of garbage (counters are cleared by the call) and once more
@@ -509,20 +512,21 @@ def test_gemm_split_k_small_workspace_runs_unsplit():
     assert torch.all(short == 0)                 # an unused workspace is not touched
 
 
-def test_linear_split_k_matches_two_calls():
+@pytest.mark.parametrize("mode", ["block", "tensor", "row"])
+def test_linear_split_k_matches_two_calls(mode):
     # fp8_linear's workspace holds the GEMM's split-K bytes: the result equals
     # quant_act followed by block_gemm with its workspace
     M, N, K = 512, 1024, 4096
     rng = np.random.default_rng(71)
     a = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
     w = synth.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
-    assert fp8.workspace_bytes(fp8._lib.OP_LINEAR, M, N, K, "block") >= \
-        M * K + fp8.workspace_bytes(fp8._lib.OP_GEMM, M, N, K, "block")
-    wq, ws = fp8.quant_weight_block(dev_bf16(w))
+    nws = fp8.workspace_bytes(fp8._lib.OP_GEMM, M, N, K, mode)
+    assert nws > 0 and fp8.workspace_bytes(fp8._lib.OP_LINEAR, M, N, K, mode) >= M * K + nws
+    wq, ws = fp8.quant_weight_block(dev_bf16(w), mode)
     x = dev_bf16(a)
-    got = host_u16(fp8.linear(x, wq, ws))
-    assert np.array_equal(got, _two_call(x, wq, ws, "block"))
-    check_out(got, oracle_gemm(a, w), "linear split K")
+    got = host_u16(fp8.linear(x, wq, ws, mode))
+    assert np.array_equal(got, _two_call(x, wq, ws, mode))
+    check_out(got, _oracle_mode(a, w, mode), f"linear split K {mode}")
 
 
 def test_split_k_replays_from_a_hip_graph():
@@ -563,20 +567,6 @@ def test_split_k_replays_from_a_hip_graph():
         assert np.array_equal(host_u16(out_l), want_l), r
         fp8.block_gemm(aq, as_, wq, ws, workspace=gws)      # eager work between replays
     check_out(want_l, oracle_gemm(a, w), "split K from a graph")
-
-
-@pytest.mark.parametrize("mode", ["tensor", "row"])
-def test_gemm_constant_scales_do_not_split(mode):
-    # scales constant along K keep the unsplit kernel: no workspace, and a
-    # workspace given anyway changes nothing
-    M, N, K = 512, 512, 2048
-    assert fp8.workspace_bytes(fp8._lib.OP_GEMM, M, N, K, mode) == 0
-    a, w, aq, as_, wq, ws = _split_case(M, N, K, mode, 29)
-    junk = torch.full((1 << 20,), 0xA5, dtype=torch.uint8, device="cuda")
-    o1 = host_u16(fp8.block_gemm(aq, as_, wq, ws, mode))
-    o2 = host_u16(fp8.block_gemm(aq, as_, wq, ws, mode, workspace=junk))
-    assert np.array_equal(o1, o2)
-    check_out(o1, _oracle_mode(a, w, mode), f"{mode} {M}x{N}x{K}")
 
 
 def test_gemm_small_integers_exact():

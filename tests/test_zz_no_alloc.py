@@ -35,6 +35,7 @@ def operands(seed, M, N, K, mode):
     ("row", [(64, 512, 512), (17, 512, 512)]),
     ("block", [(4, 512, 1024), (1, 512, 1024)]),          # fused path: no scratch
     ("block", [(512, 1024, 4096), (300, 512, 2048)]),     # GEMM split in K: its slots in scratch
+    ("tensor", [(512, 1024, 4096), (300, 512, 2048)]),    # the same with one scale per tensor
 ])
 def test_noalloc_matches_linear(mode, shapes):
     for i, (M, N, K) in enumerate(shapes):
