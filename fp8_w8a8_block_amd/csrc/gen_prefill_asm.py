@@ -144,6 +144,7 @@ FOLD_LAG = 4
 # LDS (timed against folds after the MFMA: 114.9 -> 108.6 us on the MLP-down
 # shape, 61.7 -> 60.0 us at 4096^3, bit-identical output).
 FOLDS_BEFORE = 4
+COPY_LEAD = 4                     # the step's copies start this many slots before its end
 for _q, _seq in SLOT_SEQS.items():
     assert len(_seq) == _q
     _cyc = _seq + _seq[:FOLD_LAG]
@@ -388,9 +389,9 @@ def gen_loop(block, lay):
                 nbuf = (st // KB_GROUP + 1) % 2
                 at(base + Q - 2, lambda nbuf=nbuf: dma_scale_group(prog, lay, nbuf, f"blk{lay.tag}"))
         # copies of K block kb + S into this step's stage (released at the
-        # barrier), one per slot from slot Q - 4 on
+        # barrier), one per slot from slot Q - COPY_LEAD on
         for k, (op, t) in enumerate(copies(lay)):
-            at(base + Q - 4 + k, lambda st=st, op=op, t=t, p=p, k=k: dma_copy(
+            at(base + Q - COPY_LEAD + k, lambda st=st, op=op, t=t, p=p, k=k: dma_copy(
                 prog, lay, op, t, p, k, st + S))
 
     total = Q * nsteps
