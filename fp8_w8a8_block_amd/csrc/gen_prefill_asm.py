@@ -144,7 +144,12 @@ FOLD_LAG = 4
 # LDS (timed against folds after the MFMA: 114.9 -> 108.6 us on the MLP-down
 # shape, 61.7 -> 60.0 us at 4096^3, bit-identical output).
 FOLDS_BEFORE = 4
-COPY_LEAD = 4                     # the step's copies start this many slots before its end
+# the step's copies start this many slots before its end.  With block
+# scales right after its barrier (the barrier slot is Q - 6): timed against
+# 4, 112.0 -> 110.8 us on the MLP-down shape and 1659 -> 1598 us on the
+# large GEMM.  Scales constant along K keep 4 (95.2 against 98.8 us on the
+# MLP-down shape).  Medians of interleaved runs.
+COPY_LEAD = {True: 6, False: 4}   # by block scales or not
 for _q, _seq in SLOT_SEQS.items():
     assert len(_seq) == _q
     _cyc = _seq + _seq[:FOLD_LAG]
@@ -330,6 +335,8 @@ def gen_loop(block, lay):
     # the barrier follows the last fragment read of the step's stage; the
     # next step's first reads follow it, five slots before their first use
     bar_slot = Q - 6
+    lead = COPY_LEAD[block]
+    assert Q - lead >= bar_slot          # a step's copies follow its barrier
     for st in range(nsteps):
         p = st % S                   # LDS stage of this step
         q = (st + 1) % S             # LDS stage of the next step
@@ -389,9 +396,9 @@ def gen_loop(block, lay):
                 nbuf = (st // KB_GROUP + 1) % 2
                 at(base + Q - 2, lambda nbuf=nbuf: dma_scale_group(prog, lay, nbuf, f"blk{lay.tag}"))
         # copies of K block kb + S into this step's stage (released at the
-        # barrier), one per slot from slot Q - COPY_LEAD on
+        # barrier), one per slot from slot Q - lead on
         for k, (op, t) in enumerate(copies(lay)):
-            at(base + Q - COPY_LEAD + k, lambda st=st, op=op, t=t, p=p, k=k: dma_copy(
+            at(base + Q - lead + k, lambda st=st, op=op, t=t, p=p, k=k: dma_copy(
                 prog, lay, op, t, p, k, st + S))
 
     total = Q * nsteps

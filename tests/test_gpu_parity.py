@@ -259,13 +259,14 @@ def test_quant_tensor_edges():
 # ---------------------------------------------------------------------------
 # GEMM
 
-def run_gemm(a_bits, w_bits, mode="block"):
-    """GPU: quantize A and W, then GEMM.  Returns out bits (uint16 [M, N])."""
+def run_gemm(a_bits, w_bits, mode="block", split=True):
+    """GPU: quantize A and W, then GEMM (split in K where the shape allows it,
+    unless split is False).  Returns out bits (uint16 [M, N])."""
     x = dev_bf16(a_bits)
     wd = dev_bf16(w_bits)
     wq, ws = fp8.quant_weight_block(wd, mode)
     aq, as_ = fp8.quant_act(x, mode)
-    out = fp8.block_gemm(aq, as_, wq, ws, mode)
+    out = fp8.block_gemm(aq, as_, wq, ws, mode, split=split)
     torch.cuda.synchronize()
     return host_u16(out)
 
@@ -291,13 +292,16 @@ def check_out(out_bits, refd, what):
 @pytest.mark.parametrize("K", [32768, 33280])
 def test_gemm_longest_k(K):
     # K = 32768 fills the hand-scheduled kernel's weight-scale table (256 K
-    # blocks); one more 512 goes to the C++ prefill kernel
+    # blocks), split in K and unsplit; one more 512 goes to the C++ prefill
+    # kernel
     M, N = 300, 256
     rng = np.random.default_rng(K)
     a_bits = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
     w_bits = synth.f32_to_bf16_bits(rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02))
     log("gemm longest K", (M, N, K))
-    check_out(run_gemm(a_bits, w_bits), oracle_gemm(a_bits, w_bits), f"K={K}")
+    ref = oracle_gemm(a_bits, w_bits)
+    check_out(run_gemm(a_bits, w_bits), ref, f"K={K}")
+    check_out(run_gemm(a_bits, w_bits, split=False), ref, f"K={K} unsplit")
 
 
 def test_gemm_longest_k_256_tiles_sampled():

@@ -252,3 +252,48 @@ def test_scales_are_not_overwritten_before_their_last_fold():
             m = re.match(r"v_fmac_f32_e32 v\d+, v(\d+), ", l)
             if m:
                 assert int(m.group(1)) not in pending, (tag, l)
+
+
+def test_no_copy_overwrites_a_stage_before_every_wave_has_read_it():
+    # LDS write-after-read across waves: a copy into stage p (its m0 base
+    # names the stage) must come after a barrier that follows this wave's
+    # last fragment read of stage p (the read's offset names the stage)
+    g = _gen()
+    for tag, block in _all(g):
+        lay = g.layout(tag)
+        a_bytes, w_bytes = lay.a_units * lay.unit, lay.w_units * lay.unit
+        lines = [l for c in g.gen_loop(block, lay)[0] for l in c]
+        last_read = {}
+        last_bar = -1
+        pending_m0 = None
+        n_checked = 0
+        for i, l in enumerate(lines):
+            if l == "s_barrier":
+                last_bar = i
+                continue
+            m = re.fullmatch(r"ds_read_b128 v\[\d+:\d+\], (%\[rd[AW]\]|v\d+) offset:(\d+)", l)
+            if m:
+                reg, off = m.group(1), int(m.group(2))
+                if reg.startswith("%"):
+                    op = reg[2:5]
+                elif int(reg[1:]) in (g.RDA_HI, g.RDW_HI):
+                    op, off = ("rdA" if int(reg[1:]) == g.RDA_HI else "rdW"), off + 65536
+                else:
+                    continue
+                stage = ("A", off // a_bytes) if op == "rdA" else ("W", off // w_bytes)
+                last_read[stage] = i
+                continue
+            m = re.fullmatch(r"s_add_u32 m0, %\[wave1k\], (\d+)", l)
+            if m:
+                pending_m0 = int(m.group(1))
+                continue
+            if l.startswith("buffer_load_dwordx4") and l.endswith(" lds") and "%[dSa]" not in l:
+                base = pending_m0
+                if base >= lay.W[0]:
+                    stage = ("W", (base - lay.W[0]) // w_bytes)
+                else:
+                    stage = ("A", base // a_bytes)
+                if stage in last_read:
+                    assert last_bar > last_read[stage], (tag, block, i, l)
+                    n_checked += 1
+        assert n_checked > 0
