@@ -81,9 +81,11 @@ def dominant_kernel(workload, decode):
         return "gemm_grouped_decode_kernel"
     if workload == "moe_prefill":
         return "gemm_prefill_asm_kernel"
+    if workload == "tiny":
+        return "linear_decode_kernel"     # 16 x 256 x 512: one fused launch
     # the prefill-shaped workloads all have K % 512 == 0 and M > 64: the
     # hand-scheduled kernel
-    return "gemm_decode_kernel" if decode or workload == "tiny" else "gemm_prefill_asm_kernel"
+    return "gemm_decode_kernel" if decode else "gemm_prefill_asm_kernel"
 
 
 def measured_traffic(workload):

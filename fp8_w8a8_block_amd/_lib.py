@@ -276,9 +276,9 @@ def block_gemm(a_q, a_s, w_q, w_s, scale_mode="block", out=None, workspace=None,
 def linear(x, w_q, w_s, scale_mode="block", out=None, workspace=None):
     """One W8A8 linear call in one library call: out = GEMM(quant_act(x), W).
 
-    Bit-identical to quant_act followed by block_gemm.  Block scales with
-    M <= 4 run fused (no workspace); otherwise a workspace is used (allocated
-    here unless given).  Row mode: per-token activation scales, per-channel
+    Bit-identical to quant_act followed by block_gemm.  Block-scaled calls
+    with few rows run fused (no workspace: workspace_bytes(OP_LINEAR) is 0);
+    otherwise a workspace is used (allocated here unless given).  Row mode: per-token activation scales, per-channel
     weight scales w_s [N] (or one value).
     """
     mode = _mode(scale_mode)

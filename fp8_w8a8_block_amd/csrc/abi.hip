@@ -177,7 +177,7 @@ LinearLayout linear_layout(int64_t M, int64_t N, int64_t K, int scale_mode) {
 // Work-items of the largest grid fp8_linear launches: the fused decode
 // kernel, or the quantizer and then the GEMM.
 uint64_t linear_items(int64_t M, int64_t N, int64_t K, int scale_mode) {
-  if (scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, K))
+  if (scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, N, K))
     return fp8k::linear_decode_items(N);
   const uint64_t q = quant_items(M, K, scale_mode, false), g = fp8k::gemm_items(M, N, K);
   return q > g ? q : g;
@@ -216,7 +216,7 @@ size_t fp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int scale_mo
   if ((op == FP8_OP_QUANT_ACT || op == FP8_OP_QUANT_WEIGHT) && scale_mode == FP8_SCALE_TENSOR)
     return (size_t)fp8k::kTensorPartials * sizeof(uint32_t);
   if (op == FP8_OP_LINEAR) {
-    if (scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, K)) return 0;
+    if (scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, N, K)) return 0;
     if (M <= 0 || K <= 0) return 0;
     return linear_layout(M, N, K, scale_mode).total;
   }
@@ -353,7 +353,7 @@ fp8_status validate_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, 
               : scale_mode == FP8_SCALE_ROW ? row_scales(w_s, N, ld_ws)
                                             : range_of(w_s, 1, 1, 1, 4);
   if (overlap(ro, rx) || overlap(ro, rw) || overlap(ro, rws)) return FP8_ERR_ALIAS;
-  fused = scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, K);
+  fused = scale_mode == FP8_SCALE_BLOCK && fp8k::linear_decode_supported(M, N, K);
   lay = linear_layout(M, N, K, scale_mode);
   return FP8_OK;
 }

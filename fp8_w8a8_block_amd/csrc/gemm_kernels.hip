@@ -1299,14 +1299,24 @@ hipError_t launch_linear_decode(const uint16_t* x, int64_t ld_x, const uint8_t* 
   return hipGetLastError();
 }
 
-// Above this M the per-wave quantization costs more than the separate
-// quantizer launch it saves (measured on MI355X at N = 11008, K = 4096).
-#ifndef FP8_LINEAR_FUSED_MAX_M
-#define FP8_LINEAR_FUSED_MAX_M 4
-#endif
+// Every workgroup of the fused kernel quantizes all M rows over its K range,
+// so the fused launch pays M * K quantizations per wave group and N / 16
+// times that over the grid.  Up to 4 rows it beats the separate quantizer
+// launch at any width (measured on MI355X at N = 11008, K = 4096); up to 16
+// rows only while both counts stay small: per call, replayed from a graph,
+// 16 x 256 x 512 took 3.9 against 5.1 us and 16 x 512 x 1024 4.5 against
+// 5.3 us, while 16 x 1024 x 4096 took 9.5 against 7.0 us and 8 x 4096 x 4096
+// 7.3 against 7.1 us.
+constexpr int64_t kFusedMaxM = 4;
+constexpr int64_t kFusedWideMaxM = 16;           // rows of the fused kernel's A fragment
+constexpr int64_t kFusedWideMaxMK = 16384;       // M * K
+constexpr int64_t kFusedWideMaxGridMK = 1 << 21; // (N / 16) * M * K
 
-bool linear_decode_supported(int64_t M, int64_t K) {
-  return M >= 1 && M <= FP8_LINEAR_FUSED_MAX_M && K / 128 <= kDecodeMaxKB;
+bool linear_decode_supported(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || K / 128 > kDecodeMaxKB) return false;
+  if (M <= kFusedMaxM) return true;
+  return M <= kFusedWideMaxM && M * K <= kFusedWideMaxMK &&
+         (N / 16) * M * K <= kFusedWideMaxGridMK;
 }
 
 // Work-items of the grid a GEMM launches: the decode tile (16 columns per

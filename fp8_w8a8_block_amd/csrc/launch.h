@@ -64,9 +64,10 @@ size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K);
 uint32_t gemm_split_words(int64_t M, int64_t N, int64_t K);
 
 // Fused decode linear: dynamic 1x128 quantization of x inside the decode GEMM
-// (block scales).  Dispatched for 1 <= M <= 4 and K <= 16384; the result is
+// (block scales).  Dispatched for K <= 16384 and 1 <= M <= 4, or M <= 16
+// with M * K <= 16384 and (N / 16) * M * K <= 2^21; the result is
 // bit-identical to launch_quant_act_block followed by launch_gemm.
-bool linear_decode_supported(int64_t M, int64_t K);
+bool linear_decode_supported(int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear_decode(const uint16_t* x, int64_t ld_x, const uint8_t* w, int64_t ld_w,
                                 const float* sw, int64_t ld_sw, uint16_t* out, int64_t ld_out,
                                 int64_t M, int64_t N, int64_t K, hipStream_t st);

@@ -183,8 +183,10 @@ fp8_status fp8_block_gemm(const uint8_t* a_q, int64_t ld_a, const float* a_s, in
  *   by fp8_block_gemm.
  *   FP8_SCALE_ROW quantizes x per token (dynamic) and takes per-channel
  *   (or, with ld_ws = 0, per-tensor) weight scales w_s[n * ld_ws].
- *   FP8_SCALE_BLOCK with 1 <= M <= 4 and K <= 16384 runs as one fused
- *   launch (quantization inside the decode GEMM) and needs no workspace.
+ *   FP8_SCALE_BLOCK with K <= 16384 and either 1 <= M <= 4, or M <= 16
+ *   with M * K <= 16384 and (N / 16) * M * K <= 2^21, runs as one fused
+ *   launch (quantization inside the decode GEMM) and needs no workspace
+ *   (fp8_workspace_bytes(FP8_OP_LINEAR, ...) is 0 exactly for these).
  *   Any other call quantizes into the workspace and then multiplies; it
  *   needs fp8_workspace_bytes(FP8_OP_LINEAR, M, N, K, scale_mode) bytes of
  *   device memory (16-byte aligned, not initialized, not read afterwards),
@@ -199,8 +201,8 @@ fp8_status fp8_linear(const uint16_t* x, int64_t ld_x, const uint8_t* w_q, int64
 /* fp8_linear_noalloc -- fp8_linear for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments, arithmetic and result as fp8_linear,
- * bit for bit, without the workspace: the unfused path (anything but
- * FP8_SCALE_BLOCK with 1 <= M <= 4) keeps its activation codes, scales and
+ * bit for bit, without the workspace: the unfused path (every call but the
+ * fused ones above) keeps its activation codes, scales and
  * per-tensor partials in a scratch buffer of FP8_NOALLOC_SCRATCH_BYTES that
  * the library holds on every device it runs on, from the first call on that
  * device until the process ends (a static device array; its address is

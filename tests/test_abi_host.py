@@ -68,6 +68,13 @@ def test_workspace_bytes():
     assert max(lin, lin2) <= int(m.group(1)) << int(m.group(2))
     # fused decode linear needs none; other shapes hold codes + scales
     assert _lib.workspace_bytes(_lib.OP_LINEAR, 4, 11008, 4096, "block") == 0
+    # up to 16 rows fuse while M * K <= 16384 and (N / 16) * M * K <= 2^21
+    assert _lib.workspace_bytes(_lib.OP_LINEAR, 16, 256, 512, "block") == 0     # the tiny shape
+    assert _lib.workspace_bytes(_lib.OP_LINEAR, 16, 2048, 1024, "block") == 0   # 2^21 exactly
+    assert _lib.workspace_bytes(_lib.OP_LINEAR, 16, 2176, 1024, "block") > 0    # grid past 2^21
+    assert _lib.workspace_bytes(_lib.OP_LINEAR, 16, 256, 1152, "block") > 0     # M * K past 16384
+    assert _lib.workspace_bytes(_lib.OP_LINEAR, 17, 256, 512, "block") > 0
+    assert _lib.workspace_bytes(_lib.OP_LINEAR, 16, 256, 512, "tensor") > 0     # block scales only
     assert _lib.workspace_bytes(_lib.OP_LINEAR, 16, 11008, 4096, "block") >= 16 * 4096
     assert _lib.workspace_bytes(_lib.OP_LINEAR, 1, 256, 512, "block") == 0
     n = _lib.workspace_bytes(_lib.OP_LINEAR, 100, 256, 512, "block")

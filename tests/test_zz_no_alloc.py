@@ -34,6 +34,7 @@ def operands(seed, M, N, K, mode):
     ("tensor", [(257, 256, 1024), (3, 256, 1024)]),       # per-tensor partials in scratch
     ("row", [(64, 512, 512), (17, 512, 512)]),
     ("block", [(4, 512, 1024), (1, 512, 1024)]),          # fused path: no scratch
+    ("block", [(16, 256, 512), (9, 256, 512)]),           # fused up to 16 rows on small shapes
     ("block", [(512, 1024, 4096), (300, 512, 2048)]),     # GEMM split in K: its slots in scratch
     ("tensor", [(512, 1024, 4096), (300, 512, 2048)]),    # the same with one scale per tensor
 ])
