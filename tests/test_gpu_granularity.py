@@ -218,7 +218,7 @@ def test_gemm_rows_decode(M):
 @pytest.mark.parametrize("M,N,K", [(40, 384, 640), (300, 384, 512), (2000, 4224, 1024),
                                    (300, 384, 640), (129, 256, 2048)])
 def test_gemm_rows_paths(M, N, K):
-    # mid-size tile kernel, hand-scheduled prefill 256x128 and 256x256 tiles,
+    # mid-size tile kernel, hand-scheduled prefill 128x256 and 256x256 tiles,
     # C++ prefill (K % 512 != 0); ragged M and N
     rng = np.random.default_rng([M, N, K, 5])
     a = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
