@@ -1155,8 +1155,11 @@ int device_cus() {
 // Fused decode linear (M <= 16): the decode GEMM above with the dynamic 1x128
 // activation quantization done inside it, one launch per call.  Each wave
 // quantizes the groups of its own K blocks just in time: the bf16 loads of
-// block kb are issued before its weight copy, so the quantization (VALU)
-// runs while the weight is still streaming.  Quantization uses the same lane
+// block kb are issued with its weight copy.  (The compiler waits for every
+// load in flight before the bf16 values are used, since it does not order
+// ordinary loads against LDS copies, so the quantization follows the copy's
+// arrival; staging the bf16 rows by LDS copy to overlap the two was no
+// faster.)  Quantization uses the same lane
 // layout and device functions as quant_act_block_kernel (16 lanes x 8 values
 // per group, 16-lane DPP max), so the codes and scales are bit-identical to
 // fp8_quant_act's; the MFMA, fold and reduction order equal the decode
@@ -1240,6 +1243,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void linear_decode_kernel(
   if (kb_lo < kb_hi) issue(kb_lo);
   for (int kb = kb_lo; kb < kb_hi; ++kb) {            // wave-uniform; no barrier inside
     // the activation loads of block kb went out before its two weight copies
+    // (the compiler adds the wait for those too before the values are used)
     asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
