@@ -1,7 +1,7 @@
 """Writes prefill_asm.inc: the K loop of the prefill GEMM as gfx950 assembly.
 
-The loop is emitted as the text of one inline-asm statement per scale mode
-(block scales, per-tensor scales).  gemm_kernels.hip prepares the operands
+The loop is emitted as the text of one inline-asm statement per workgroup
+shape and scale mode (block scales, per-tensor scales).  gemm_kernels.hip prepares the operands
 (tile origin, buffer descriptors, per-lane offsets) in C++ and hands them to
 that statement; everything that touches the accumulators -- the copies into
 LDS, the fragment reads, the MFMAs, the per-K-block scale fold and the bf16
@@ -11,10 +11,11 @@ Why a generator: the instruction order is the performance.  The matrix unit
 should never wait for the fragment reads or the copies, and the compiler's
 scheduler, short of registers at 248 VGPRs, folds every partial product the
 moment it is produced and waits on the matrix unit with s_nop.  Here each
-K step is 32 MFMA slots (4 weight x 8 activation fragments of the wave's
-128 x 64 tile); memory operations are spread over the slots, each partial is
-folded four MFMAs after it was issued, and every LDS counter wait is computed
-from the issue order.
+K step is 4 fa MFMA slots (4 weight x fa activation fragments of the wave's
+16 fa x 64 tile: 32 slots for 128 x 64, 16 for 64 x 64); memory operations
+are spread over the slots, each partial is folded four MFMAs after it was
+issued (the four folds go out ahead of the next MFMA's fragment wait), and
+every LDS counter wait is computed from the issue order.
 
 M0 is written by the copies (the LDS destination of buffer_load ... lds) and is
 listed among the clobbers with the fixed registers, so the compiler keeps no
