@@ -101,3 +101,22 @@ def test_decode_line_fields():
     assert isinstance(cpu["cpu_model"], str) and cpu["cpu_model"]
     assert [r["workload"] for r in cpu["single_thread"]] == ["tiny", "decode", "prefill"]
     assert all(r["threads"] == 1 and r["GFLOP/s"] > 0 for r in cpu["single_thread"])
+
+
+def test_dominant_kernel_follows_the_dispatch():
+    # the roofline's kernel name is the one the library launches for the
+    # workload's step: one fused launch where fp8_linear needs no workspace
+    # (the tiny shape), the decode GEMM where it quantizes first (decode
+    # M = 16), the hand-scheduled prefill kernel for the prefill shapes
+    sys.path.insert(0, ROOT)
+    import bench
+    import fp8_w8a8_block_amd._lib as L
+    from workloads import synth
+    assert L.workspace_bytes(L.OP_LINEAR, 16, 256, 512, "block") == 0
+    assert bench.dominant_kernel("tiny", False) == "linear_decode_kernel"
+    assert L.workspace_bytes(L.OP_LINEAR, 16, 11008, 4096, "block") > 0
+    assert bench.gemm_kernel_name(16, 4096) == "gemm_decode_kernel"
+    for name in ("prefill", "mlp_down", "large"):
+        c = synth.CONFIGS[name]
+        assert bench.gemm_kernel_name(c["M"], c["K"]) == "gemm_prefill_asm_kernel"
+        assert bench.dominant_kernel(name, False) == "gemm_prefill_asm_kernel"
