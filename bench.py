@@ -329,6 +329,48 @@ def secondary_gemm(name, n_launches=None):
     return r
 
 
+def mfma_reference(n=5, grid=256, iters=2048):
+    """Timed matrix-unit reference for the prefill lines: the FP8
+    MFMA alone (hbm_probe.hip's mfma_chain_kernel: 8 waves per CU, 16
+    independent accumulators, operands in registers), n back-to-back launches
+    timed like the kernels, on random E4M3 codes (NaN codes replaced) and on
+    zero codes.  What it reaches is the rate the chip sustains for FP8 MFMAs
+    at the clock it holds under that load."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "fp8_w8a8_block_amd", "libhbmprobe.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m fp8_w8a8_block_amd.build`")
+    probe = ctypes.CDLL(path)
+    probe.mfma_chain_probe.restype = ctypes.c_int
+    probe.mfma_chain_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    rnd = torch.randint(0, 256, (1 << 20,), dtype=torch.uint8, device="cuda", generator=g)
+    rnd[(rnd & 0x7F) == 0x7F] -= 1                 # E4M3 NaN codes -> the largest finite
+    zero = torch.zeros_like(rnd)
+    sink = torch.empty(grid * 512, dtype=torch.int32, device="cuda")
+    flop = grid * 8 * iters * 16 * 2 * 16 * 16 * 128
+    res = {}
+    for name, codes in (("random_codes", rnd), ("zero_codes", zero)):
+        def run(i, codes=codes):
+            st = torch.cuda.current_stream().cuda_stream
+            rc = probe.mfma_chain_probe(codes.data_ptr(), iters, sink.data_ptr(), grid, st)
+            if rc != 0:
+                raise RuntimeError(f"mfma_chain_probe failed: {rc}")
+        run(0)
+        ms = time_launches(run, n)
+        tf = flop / (ms * 1e-3) / 1e12
+        res[name] = {"avg_launch_us": ms * 1e3, "TFLOP/s": tf, "frac_of_5000": tf / FP8_PEAK_TFLOPS}
+    res["flop_per_launch"] = flop
+    res["note"] = ("mfma_chain_kernel (fp8_w8a8_block_amd/csrc/hbm_probe.hip): "
+                   "v_mfma_f32_16x16x128_f8f6f4 only, 8 waves per CU, operands in registers")
+    del rnd, zero, sink
+    torch.cuda.empty_cache()
+    return res
+
+
 def hbm_reference(nbytes=1 << 30, n=10):
     """Timed HBM references beside the kernels, each n back-to-back
     launches timed like the kernels: torch's device copy of a 1 GiB buffer
@@ -908,6 +950,7 @@ def main():
         cpu = cpu_baseline(wl, args.cpu_baseline_seconds)
     secondary = None
     hbm_ref = hbm_reference()
+    mfma_ref = None if decode else mfma_reference()
     if decode and not args.no_secondary:
         del wl
         torch.cuda.empty_cache()
@@ -942,6 +985,8 @@ def main():
         "quantizer": quantizer,
         "hbm_reference": hbm_ref,
     }
+    if mfma_ref is not None:
+        line["mfma_reference"] = mfma_ref
     print(json.dumps(line), flush=True)
 
 
