@@ -19,7 +19,8 @@ shard small enough to split K in two sums its two halves at the end, a
 different order: the same value up to fp32 rounding, checked through the
 tolerance gate below.)  The first GPU's share is also checked against the
 oracle through the GEMM tolerance gate, through fp8_linear as a caller
-would run it.
+would run it.  Slices of the token rows (data parallelism) likewise give the
+full call's rows bit for bit.
 """
 
 import sys
@@ -98,6 +99,29 @@ def test_prefill_shards_equal_the_full_call(decode_weight):
         log(f"prefill shard M={M} columns {lo}..{hi}")
         got = host_u16(fp8.block_gemm(aq, as_, *shard(wq, ws, lo, hi), split=False))
         assert np.array_equal(got, full[:, lo:hi]), f"M={M} shard {lo}..{hi}"
+
+
+@pytest.mark.parametrize("M,parts", [(16, 4), (300, 3)])
+def test_row_slices_equal_the_full_call(M, parts, decode_weight):
+    # token rows (data parallel): rows are independent, scales are per row,
+    # so a slice of the batch gives the full call's rows bit for bit -- at
+    # M = 16 the slices of 4 rows take the fused kernel and the full call the
+    # two-launch path; at M = 300 both run the unsplit block GEMM
+    w, wq, ws = decode_weight
+    rng = np.random.default_rng([M, 79])
+    a = synth.f32_to_bf16_bits(rng.standard_normal((M, 4096)).astype(np.float32))
+    step = M // parts
+    if M <= 16:
+        full = host_u16(fp8.linear(dev_bf16(a), wq, ws))
+        part = lambda lo, hi: host_u16(fp8.linear(dev_bf16(a[lo:hi]), wq, ws))
+    else:
+        full = host_u16(fp8.block_gemm(*fp8.quant_act(dev_bf16(a)), wq, ws, split=False))
+        part = lambda lo, hi: host_u16(fp8.block_gemm(*fp8.quant_act(dev_bf16(a[lo:hi])), wq, ws,
+                                                      split=False))
+    for lo in range(0, M, step):
+        hi = min(lo + step, M)
+        log(f"row slice M={M} rows {lo}..{hi}")
+        assert np.array_equal(part(lo, hi), full[lo:hi]), f"M={M} rows {lo}..{hi}"
 
 
 @pytest.mark.parametrize("M", [4, 300])
