@@ -987,6 +987,9 @@ def main():
     }
     if mfma_ref is not None:
         line["mfma_reference"] = mfma_ref
+        # the dominant kernel against what the matrix units alone sustain on
+        # random codes, beside its fraction of the 5.0 PFLOP/s figure
+        roof["frac_of_mfma_reference"] = roof["achieved"] / mfma_ref["random_codes"]["TFLOP/s"]
     print(json.dumps(line), flush=True)
 
 
