@@ -37,6 +37,43 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def header_signatures():
+    """name -> (return type, [parameter types]) of every declaration in the
+    header, with parameter names and const dropped."""
+    text = re.sub(r"/\*.*?\*/|//[^\n]*", "", open(HEADER).read(), flags=re.S)
+    sigs = {}
+    for ret, name, params in re.findall(
+            r"^\s*((?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**)\s*(fp8_[a-z0-9_]+)\s*\(([^)]*)\)\s*;",
+            text, flags=re.M):
+        types = []
+        for prm in params.split(","):
+            prm = " ".join(prm.replace("const", " ").split())
+            m = re.fullmatch(r"([A-Za-z_][A-Za-z0-9_]*)\s*(\**)\s*[A-Za-z_][A-Za-z0-9_]*", prm)
+            assert m, (name, prm)
+            types.append(m.group(1) + m.group(2))
+        sigs[name] = (" ".join(ret.replace("const", " ").split()).replace(" *", "*"), types)
+    return sigs
+
+
+def test_binding_argument_types_match_the_header():
+    # every ctypes signature the binding sets is the header's, parameter for
+    # parameter: pointers as c_void_p, int64_t as c_int64, int and the status
+    # enum as c_int, size_t as c_size_t
+    c_of = {"int64_t": ctypes.c_int64, "int": ctypes.c_int, "size_t": ctypes.c_size_t,
+            "fp8_status": ctypes.c_int}
+    sigs = header_signatures()
+    assert sorted(sigs) == header_functions()
+    assert sorted(_lib._SIGS) == sorted(sigs)
+    for name, (ret, params) in sigs.items():
+        b_ret, b_args = _lib._SIGS[name]
+        want_ret = ctypes.c_char_p if ret == "char*" else c_of[ret]
+        assert b_ret is want_ret, (name, ret, b_ret)
+        assert len(b_args) == len(params), (name, params, b_args)
+        for i, (t, b) in enumerate(zip(params, b_args)):
+            want = ctypes.c_void_p if t.endswith("*") else c_of[t]
+            assert b is want, (name, i, t, b)
+
+
 def test_status_strings():
     for code in range(0, 12):
         s = _lib.status_str(code)
