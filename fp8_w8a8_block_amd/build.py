@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8w8a8.so")
 SOURCES = ["abi.hip", "quant_kernels.hip", "gemm_kernels.hip", "kv_kernels.hip"]
-PROBE_SOURCE = "hbm_probe.hip"                 # bench.py's HBM read reference
+PROBE_SOURCE = "hbm_probe.hip"                 # bench.py's HBM and matrix-unit references
 PROBE_LIB = os.path.join(PKG, "libhbmprobe.so")
 ARCH = "gfx950"
 
@@ -72,7 +72,7 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
-    # bench.py's HBM read reference, a library of its own
+    # bench.py's HBM read and matrix-unit references, a library of their own
     probe = _compile(PROBE_SOURCE, verbose)
     tmp = PROBE_LIB + ".tmp"
     r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, probe,
